@@ -1,0 +1,182 @@
+"""fp64 CPU oracle: plain, slow, materialising definition of causal scaled-dot-product attention.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path may import, call or execute this module;
+only the tests, the smoke check and the benchmark's CPU-baseline leg do. It shares no code with
+the HIP library and receives its inputs from the seeded generators in ``synth.py``.
+
+Every step follows the plain definition written on the pages; none of the tiling, online
+softmax or split-KV machinery of the GPU path appears here (exact attention has one result:
+"Transformer 架构完全深度解析" §十三 states the tiled method is mathematically identical).
+
+Sources (cited by page title and section):
+  [P1] "2.7 Transformer Decoder Block完整解析" (ningzhengsheng.cn)
+  [P2] "Transformer 架构快速入门" (liumengxuan04.github.io)
+  [P3] "Transformer 架构完全深度解析" (tufusi.com)
+  [P4] "Transformer 与 LLM：结构、实现与算量" (arganzheng.life slides)
+
+Where the pages are silent or disagree, the reading taken is stated next to the step it affects.
+
+Parity pins: every function here is pinned by tests/test_oracle.py against printed values,
+closed forms or invariants; no function is "parity unpinned". The page's own d=4, T=3 inputs
+are not in the text, so that example is pinned through a constructed case whose closed form
+rounds to the printed weights.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------------------------
+# RoPE  ([P1] §4 precompute/apply; [P2] §8.2 frequencies, §8.3 rotation; [P3] §七)
+# ---------------------------------------------------------------------------------------------
+def rope_inv_freq(head_dim: int, theta: float) -> np.ndarray:
+    """Pair frequencies theta_i = base^(-2i/D) for i = 0 .. D/2-1 ([P1] §4, [P2] §8.2).
+
+    The index is 0-based (theta_0 = 1), as in [P1]'s table code; [P4] slide 07's count of 14
+    unfinished low-frequency pairs at 8K (D=128, base 1e4) fixes this choice.
+    """
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    return np.float64(theta) ** (-2.0 * i / head_dim)
+
+
+def rope_angles(positions, head_dim: int, theta: float) -> np.ndarray:
+    """Angle m * theta_i for every position m and pair i ([P2] §8.2): shape positions.shape + (D/2,)."""
+    return _f64(positions)[..., None] * rope_inv_freq(head_dim, theta)
+
+
+def rope_rotate(x, positions, theta: float, interleaved: bool = False) -> np.ndarray:
+    """Rotate every head vector of x [B, S, N, D] by its position's angles, in fp64.
+
+    positions: [S] (shared by the batch) or [B, S].
+    Half-split pairing (default) rotates (x_i, x_{i+D/2}) as in [P1] §4's apply_rope:
+        (x_i cos a - x_{i+D/2} sin a,  x_i sin a + x_{i+D/2} cos a).
+    interleaved=True rotates adjacent pairs (x_{2i}, x_{2i+1}) with the same 2x2 rotation
+    ([P2] §8.3, [P3] §七). [P2] §8.1 notes that either pairing works when used consistently.
+    """
+    x = _f64(x)
+    B, S, N, D = x.shape
+    pos = np.broadcast_to(_f64(positions), (B, S))
+    ang = rope_angles(pos, D, theta)[:, :, None, :]  # [B, S, 1, D/2]
+    c, s = np.cos(ang), np.sin(ang)
+    out = np.empty_like(x)
+    if interleaved:
+        a, b = x[..., 0::2], x[..., 1::2]
+        out[..., 0::2] = a * c - b * s
+        out[..., 1::2] = a * s + b * c
+    else:
+        h = D // 2
+        a, b = x[..., :h], x[..., h:]
+        out[..., :h] = a * c - b * s
+        out[..., h:] = a * s + b * c
+    return out
+
+
+# ---------------------------------------------------------------------------------------------
+# Mask, softmax, one head  ([P1] §3, §4; [P2] §4.2-4.5; [P3] §五)
+# ---------------------------------------------------------------------------------------------
+def causal_mask(q_positions, n_keys: int) -> np.ndarray:
+    """Additive causal mask M[r, j] = -inf where key j lies after the query's position, else 0.
+
+    For q_positions = 0..S-1 this is the S x S matrix printed in [P1] §3.2 / §3.3.
+    """
+    j = np.arange(n_keys)
+    return np.where(j[None, :] > np.asarray(q_positions)[:, None], -np.inf, 0.0)
+
+
+def softmax_rows(s: np.ndarray) -> np.ndarray:
+    """Row softmax over the key axis ([P2] §4.4, [P3] §五 step 4): exp(s - max) / sum."""
+    m = np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def attention_weights(q, k, scale: float, mask=None) -> np.ndarray:
+    """A = softmax(scale * q k^T + M) for one head: q [R, D], k [T, D] -> [R, T] ([P2] §4.2-4.4)."""
+    s = np.float64(scale) * (_f64(q) @ _f64(k).T)
+    if mask is not None:
+        s = s + mask
+    return softmax_rows(s)
+
+
+def head_attention(q, k, v, scale: float, mask=None) -> np.ndarray:
+    """O = A v for one head ([P2] §4.5: o_m = sum_n A_mn v_n): returns [R, Dv]."""
+    return attention_weights(q, k, scale, mask) @ _f64(v)
+
+
+# ---------------------------------------------------------------------------------------------
+# Prefill: all positions of a sequence at once, GQA head sharing ([P2] §6.3)
+# ---------------------------------------------------------------------------------------------
+def kv_head_of(h: int, n_heads: int, n_kv_heads: int) -> int:
+    """Query head h reads KV head h // G with G = N_h / N_kv consecutive query heads per group
+    ([P2] §6.3: heads 1-4 -> KV 1, ..., 29-32 -> KV 8, written here 0-based)."""
+    return h // (n_heads // n_kv_heads)
+
+
+def prefill_rows(q, k, v, b: int, h: int, rows, *, causal: bool = True, scale: float | None = None,
+                 rope_theta: float = 0.0) -> np.ndarray:
+    """Output rows out[b, rows, h, :] of causal self-attention over one sequence, in fp64.
+
+    q [B, S, Nh, D], k/v [B, S, Nkv, D] (any float dtype; values are taken exactly).
+    Query and key positions are 0..S-1 ([P1] §4 uses arange(seq_len)). RoPE, when
+    rope_theta > 0, rotates q and k (not v: [P1] §2, [P2] §8.5) before the scores.
+    The full score row over all S keys is materialised and masked with -inf ([P1] §3.3).
+    """
+    B, S, Nh, D = q.shape
+    Nkv = k.shape[2]
+    g = kv_head_of(h, Nh, Nkv)
+    rows = np.asarray(rows, dtype=np.int64)
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)  # [P2] §4.3: divide by the per-head dimension
+    qh = _f64(q[b:b + 1, rows, h:h + 1, :])  # [1, R, 1, D]
+    kh = _f64(k[b:b + 1, :, g:g + 1, :])  # [1, S, 1, D]
+    if rope_theta > 0:
+        qh = rope_rotate(qh, rows, rope_theta)
+        kh = rope_rotate(kh, np.arange(S), rope_theta)
+    mask = causal_mask(rows, S) if causal else None
+    return head_attention(qh[0, :, 0, :], kh[0, :, 0, :], v[b, :, g, :], scale, mask)
+
+
+def prefill(q, k, v, *, causal: bool = True, scale: float | None = None, rope_theta: float = 0.0) -> np.ndarray:
+    """Full prefill output [B, S, Nh, Dv] in fp64 (every (b, h) independently)."""
+    B, S, Nh, _ = q.shape
+    out = np.empty((B, S, Nh, v.shape[3]), dtype=np.float64)
+    rows = np.arange(S)
+    for b in range(B):
+        for h in range(Nh):
+            out[b, :, h, :] = prefill_rows(q, k, v, b, h, rows, causal=causal, scale=scale, rope_theta=rope_theta)
+    return out
+
+
+# ---------------------------------------------------------------------------------------------
+# KV-cache decode ([P2] §13.2, [P3] §九) and the MLA-absorbed form ([P4] slide 06)
+# ---------------------------------------------------------------------------------------------
+def decode(q, kcache, vcache, ctx_lens, *, scale: float | None = None, rope_theta: float = 0.0) -> np.ndarray:
+    """One new query token per sequence attends to every cached key of its KV head.
+
+    q [B, Nh, Dqk]; kcache [B, T, Nkv, Dqk]; vcache [B, T, Nkv, Dv]; ctx_lens [B].
+    ctx_lens[b] counts the keys 0..ctx_b-1, the new token included: [P3] §九 appends the new
+    K/V before attending, so no mask is applied. The cache holds already-rotated keys ([P3] §七:
+    cached keys carry their position); with rope_theta > 0 the query is rotated at position
+    ctx_b - 1. For the MLA-absorbed form pass vcache = kcache[..., :Dv], i.e. V is the latent
+    part c^KV of the same cached row ([P4] slide 06).
+    Returns [B, Nh, Dv] in fp64.
+    """
+    B, Nh, Dqk = q.shape
+    Nkv = kcache.shape[2]
+    Dv = vcache.shape[3]
+    if scale is None:
+        scale = 1.0 / np.sqrt(Dqk)
+    out = np.empty((B, Nh, Dv), dtype=np.float64)
+    for b in range(B):
+        c = int(ctx_lens[b])
+        for h in range(Nh):
+            g = kv_head_of(h, Nh, Nkv)
+            qh = _f64(q[b, h, :])[None, None, None, :]
+            if rope_theta > 0:
+                qh = rope_rotate(qh, [c - 1], rope_theta)
+            out[b, h, :] = head_attention(qh[0, 0], kcache[b, :c, g, :], vcache[b, :c, g, :], scale)[0]
+    return out
