@@ -1,0 +1,230 @@
+"""Benchmark of the causal-attention hot path on one MI355X.
+
+One step = one pass of every kernel of the path over synthetic inputs:
+  1. Llama-3-8B-shaped GQA causal prefill with RoPE (B=4, S=8192, 32 query / 8 KV heads of 128,
+     theta 5e5): RoPE table + key rotation + the MFMA attention kernel;
+  2. Llama-3-8B-shaped GQA KV-cache decode (B=64, one query each, contexts drawn in [1024, 8192],
+     contiguous per-sequence caches of 8192 rows): split-KV kernel + split reduction;
+  3. MLA-absorbed decode (B=32, 128 heads, one shared 576-dim row per token, context 4096,
+     scale 1/sqrt(192)): MFMA kernel + split reduction.
+Prefill is priced in algorithmic TFLOP/s (4*Dh FLOPs per unmasked (query, key) pair) against the
+dense bf16 matrix peak; decode in algorithmic GB/s (each needed cache row once, plus q and out)
+against HBM peak. The headline value is the mean of the two fractions, in percent.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--only PART]
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import synth  # noqa: E402
+from causal_head_attention_gqa_amd import accounting as acc  # noqa: E402
+
+METRIC = "causal prefill TFLOP/s + KV-decode HBM GB/s, as % of MI355X peak"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
+    p.add_argument("--only", choices=["prefill", "decode", "mla"], default=None,
+                   help="time a single part (profiling runs); the JSON line then reports that part")
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------------------------- inputs ----
+def device_normal(torch, shape, seed):
+    """N(0,1) drawn on the device (seeded), rounded to bf16 (round-to-nearest-even)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+
+
+def make_inputs(torch, attn):
+    P, D, M = synth.LLAMA3_PREFILL, synth.LLAMA3_DECODE, synth.MLA_DECODE
+    x = {}
+    x["pq"] = device_normal(torch, (P.B, P.S, P.Nh, P.Dh), 1000 * P.wid + 0)
+    x["pk"] = device_normal(torch, (P.B, P.S, P.Nkv, P.Dh), 1000 * P.wid + 1)
+    x["pv"] = device_normal(torch, (P.B, P.S, P.Nkv, P.Dh), 1000 * P.wid + 2)
+    x["pout"] = torch.empty_like(x["pq"])
+    x["pws"] = torch.empty(max(1, attn.prefill_workspace_bytes(P.B, P.S, P.Nkv, P.Dh, P.rope_theta, attn.ATTN_BF16)),
+                           dtype=torch.uint8, device="cuda")
+    x["dq"] = device_normal(torch, (D.B, D.Nh, D.Dqk), 1000 * D.wid + 0)
+    x["dk"] = device_normal(torch, (D.B, D.max_ctx, D.Nkv, D.Dqk), 1000 * D.wid + 1)
+    x["dv"] = device_normal(torch, (D.B, D.max_ctx, D.Nkv, D.Dv), 1000 * D.wid + 2)
+    x["dctx_np"] = D.ctx_lens()
+    x["dctx"] = torch.as_tensor(x["dctx_np"], device="cuda")
+    x["dout"] = torch.empty((D.B, D.Nh, D.Dv), dtype=torch.bfloat16, device="cuda")
+    x["dws"] = torch.empty(attn.decode_workspace_bytes(D.B, D.Nh, D.Nkv, D.Dqk, D.Dv, D.max_ctx, attn.ATTN_BF16),
+                           dtype=torch.uint8, device="cuda")
+    x["mq"] = device_normal(torch, (M.B, M.Nh, M.Dqk), 1000 * M.wid + 0)
+    x["mkv"] = device_normal(torch, (M.B, M.max_ctx, 1, M.Dqk), 1000 * M.wid + 1)
+    x["mctx_np"] = M.ctx_lens()
+    x["mctx"] = torch.as_tensor(x["mctx_np"], device="cuda")
+    x["mout"] = torch.empty((M.B, M.Nh, M.Dv), dtype=torch.bfloat16, device="cuda")
+    x["mws"] = torch.empty(attn.decode_workspace_bytes(M.B, M.Nh, 1, M.Dqk, M.Dv, M.max_ctx, attn.ATTN_BF16),
+                           dtype=torch.uint8, device="cuda")
+    return x
+
+
+# ----------------------------------------------------------------------------- cpu baseline ----
+def cpu_baseline(prefill_flops_per_s_gpu=None):
+    """Time the fp64 oracle as it stands on a bounded sample of the same workloads."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    P, D, M = synth.LLAMA3_PREFILL, synth.LLAMA3_DECODE, synth.MLA_DECODE
+    # prefill: every 16th row of (b=0, h=0) of the Llama-3-8B prefill (512 rows, all of their keys)
+    q = synth.normal(P.wid, 0, (1, P.S, 1, P.Dh), "bf16")
+    k = synth.normal(P.wid, 1, (1, P.S, 1, P.Dh), "bf16")
+    v = synth.normal(P.wid, 2, (1, P.S, 1, P.Dh), "bf16")
+    rows = np.arange(0, P.S, 16)
+    qf, kf, vf = (synth.as_f32(a, "bf16") for a in (q, k, v))
+    t0 = time.perf_counter()
+    oracle.prefill_rows(qf, kf, vf, 0, 0, rows, rope_theta=P.rope_theta)
+    tp = time.perf_counter() - t0
+    p_flops = 4 * P.Dh * int(np.sum(rows + 1))
+    # decode: the first 8 sequences of the GQA decode, the first 2 of the MLA decode
+    ctx = D.ctx_lens()[:8]
+    T = int(ctx.max())
+    dq = synth.as_f32(synth.normal(D.wid, 0, (8, D.Nh, D.Dqk), "bf16"), "bf16")
+    dk = synth.as_f32(synth.normal(D.wid, 1, (8, T, D.Nkv, D.Dqk), "bf16"), "bf16")
+    dv = synth.as_f32(synth.normal(D.wid, 2, (8, T, D.Nkv, D.Dv), "bf16"), "bf16")
+    t0 = time.perf_counter()
+    oracle.decode(dq, dk, dv, ctx)
+    td = time.perf_counter() - t0
+    d_bytes = acc.decode_bytes(ctx, 8, D.Nh, D.Nkv, D.Dqk, D.Dv, 2)
+    mq = synth.as_f32(synth.normal(M.wid, 0, (2, M.Nh, M.Dqk), "bf16"), "bf16")
+    mk = synth.as_f32(synth.normal(M.wid, 1, (2, M.max_ctx, 1, M.Dqk), "bf16"), "bf16").astype(np.float64)
+    mctx = M.ctx_lens()[:2]
+    t0 = time.perf_counter()
+    oracle.decode(mq, mk, mk[..., :M.Dv], mctx, scale=M.scale)
+    tm = time.perf_counter() - t0
+    m_bytes = acc.decode_bytes(mctx, 2, M.Nh, 1, M.Dqk, M.Dv, 2, shared_row=True)
+    p_tflops = p_flops / tp / 1e12
+    d_gbs = (d_bytes + m_bytes) / (td + tm) / 1e9
+    frac = 0.5 * (p_tflops / acc.PEAK_BF16_TFLOPS + d_gbs / acc.PEAK_HBM_GBS)
+    return {
+        "value": 100.0 * frac, "unit": "% of peak", "cores": int(threads), "kind": "oracle",
+        "sample": (f"fp64 numpy oracle: prefill rows 0,16,..,8176 of (b=0,h=0) of the Llama-3-8B prefill "
+                   f"({tp:.2f} s, {p_tflops * 1e3:.3f} GFLOP/s algorithmic); GQA decode of 8 sequences "
+                   f"({td:.2f} s) and MLA decode of 2 sequences ({tm:.2f} s): {d_gbs:.3f} GB/s algorithmic; "
+                   f"host {platform.processor() or platform.machine()}, {os.cpu_count()} logical CPUs"),
+        "prefill_tflops": p_tflops, "decode_gbs": d_gbs,
+    }
+
+
+# ------------------------------------------------------------------------------------ main ----
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU: every workload is one GPU's share; "
+                                   "--gpus above 1 is not supported"}))
+        sys.exit(2)
+    import torch
+    import causal_head_attention_gqa_amd as attn
+    P, D, M = synth.LLAMA3_PREFILL, synth.LLAMA3_DECODE, synth.MLA_DECODE
+    x = make_inputs(torch, attn)
+
+    def run_prefill():
+        attn.prefill(x["pq"], x["pk"], x["pv"], rope_theta=P.rope_theta, out=x["pout"], workspace=x["pws"])
+
+    def run_decode():
+        attn.decode(x["dq"], x["dk"], x["dv"], x["dctx"], out=x["dout"], workspace=x["dws"])
+
+    def run_mla():
+        attn.decode(x["mq"], x["mkv"], x["mkv"][..., :M.Dv], x["mctx"], scale=M.scale, out=x["mout"],
+                    workspace=x["mws"])
+
+    parts = [("prefill", run_prefill), ("decode", run_decode), ("mla", run_mla)]
+    if args.only:
+        parts = [p for p in parts if p[0] == args.only]
+    stream = torch.cuda.current_stream()
+
+    def step(evs=None):
+        for i, (_, fn) in enumerate(parts):
+            if evs is not None:
+                evs[i][0].record(stream)
+            fn()
+            if evs is not None:
+                evs[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in parts] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {name: float(np.mean([events[s][i][0].elapsed_time(events[s][i][1]) for s in range(args.steps)]))
+          for i, (name, _) in enumerate(parts)}
+
+    p_flops = acc.prefill_flops(P.B, P.S, P.Nh, P.Dh, causal=True)
+    d_bytes = acc.decode_bytes(x["dctx_np"], D.B, D.Nh, D.Nkv, D.Dqk, D.Dv, 2)
+    m_bytes = acc.decode_bytes(x["mctx_np"], M.B, M.Nh, 1, M.Dqk, M.Dv, 2, shared_row=True)
+    comp = {}
+    if "prefill" in ms:
+        comp["prefill_tflops"] = p_flops / (ms["prefill"] * 1e-3) / 1e12
+        comp["prefill_ms"] = ms["prefill"]
+    if "decode" in ms:
+        comp["gqa_decode_gbs"] = d_bytes / (ms["decode"] * 1e-3) / 1e9
+        comp["gqa_decode_ms"] = ms["decode"]
+    if "mla" in ms:
+        comp["mla_decode_gbs"] = m_bytes / (ms["mla"] * 1e-3) / 1e9
+        comp["mla_decode_tflops"] = acc.decode_flops(x["mctx_np"], M.Nh, M.Dqk, M.Dv) / (ms["mla"] * 1e-3) / 1e12
+        comp["mla_decode_ms"] = ms["mla"]
+    dec_ms = ms.get("decode", 0.0) + ms.get("mla", 0.0)
+    dec_bytes = (d_bytes if "decode" in ms else 0) + (m_bytes if "mla" in ms else 0)
+    fracs = []
+    if "prefill" in ms:
+        fracs.append(comp["prefill_tflops"] / acc.PEAK_BF16_TFLOPS)
+    if dec_ms > 0:
+        comp["decode_gbs"] = dec_bytes / (dec_ms * 1e-3) / 1e9
+        fracs.append(comp["decode_gbs"] / acc.PEAK_HBM_GBS)
+    value = 100.0 * float(np.mean(fracs))
+
+    if "prefill" in ms:
+        roofline = {"kernel": "prefill_bf16_kernel (Llama-3-8B GQA prefill, one call incl. RoPE pre-pass)",
+                    "bound": "mfma", "achieved": comp["prefill_tflops"], "peak": acc.PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": comp["prefill_tflops"] / acc.PEAK_BF16_TFLOPS, "traffic": None}
+    else:
+        name = args.only
+        gbs = comp["gqa_decode_gbs"] if name == "decode" else comp["mla_decode_gbs"]
+        roofline = {"kernel": f"{name} decode", "bound": "hbm", "achieved": gbs, "peak": acc.PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": gbs / acc.PEAK_HBM_GBS, "traffic": None}
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "% of peak", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "Llama-3-8B GQA causal prefill B4 S8192 Nh32 Nkv8 Dh128 RoPE5e5 + Llama-3-8B GQA "
+                               "decode B64 ctx~U[1024,8192] + MLA-absorbed decode B32 ctx4096 128x576/512",
+                   "parts": [p[0] for p in parts]},
+        "components": comp,
+        "roofline": roofline,
+        "cpu_baseline": None if args.no_cpu_baseline or args.only else cpu_baseline(),
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,17 @@
+"""MI355X (gfx950) causal attention: prefill, KV-cache decode (GQA and MLA-absorbed) and RoPE.
+
+The computation lives in the HIP library libattn_gfx950.so (C ABI in include/attn.h);
+``lib`` is a thin ctypes binding with the same entry points.
+"""
+from .lib import (  # noqa: F401
+    ATTN_BF16,
+    ATTN_F32,
+    AttnError,
+    decode,
+    decode_workspace_bytes,
+    load,
+    prefill,
+    prefill_workspace_bytes,
+    rope_apply_,
+    status_str,
+)

@@ -1,0 +1,230 @@
+// C ABI of the library: argument validation on the host, workspace layout, kernel dispatch.
+// Nothing is launched unless every argument has been checked; no exception crosses the ABI.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/attn.h"
+#include "kernels.hpp"
+
+using namespace attn;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t esize(int dtype) { return dtype == ATTN_BF16 ? 2 : 4; }
+
+bool prefill_supported(int dtype, int Dh) {
+  if (dtype == ATTN_BF16) return Dh == 64 || Dh == 128;
+  if (dtype == ATTN_F32) return Dh == 16 || Dh == 32 || Dh == 64;
+  return false;
+}
+
+// Split-KV plan shared by the workspace query and the call.
+struct DecodePlan {
+  int chunk = 0, nsplit = 0;
+  bool mla = false;
+};
+
+bool is_mla_shape(int Nkv, int Dqk, int Dv) { return Dqk == 576 && Dv == 512 && Nkv == 1; }
+
+int heads_per_group(int G) { return G % 8 == 0 ? 8 : G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1; }
+
+DecodePlan decode_plan(int B, int Nh, int Nkv, int Dqk, int Dv, int max_ctx) {
+  DecodePlan p;
+  p.mla = is_mla_shape(Nkv, Dqk, Dv);
+  if (max_ctx <= 0 || B <= 0) return p;
+  if (p.mla) {
+    const int nw = Nh % 64 == 0 ? 4 : Nh % 32 == 0 ? 2 : 1;
+    const long long groups = (long long)B * (Nh / (16 * nw));
+    const int tiles = (max_ctx + 31) / 32;
+    long long want = (256 + groups - 1) / groups;  // about one work-group per CU
+    if (want > tiles) want = tiles;
+    if (want < 1) want = 1;
+    const int per = (int)((max_ctx + want - 1) / want);
+    p.chunk = (per + 31) / 32 * 32;
+  } else {
+    const long long groups = (long long)B * (Nh / heads_per_group(Nh / Nkv));
+    p.chunk = 512;
+    while (p.chunk > 64 && groups * ((max_ctx + p.chunk - 1) / p.chunk) < 1024) p.chunk /= 2;
+  }
+  p.nsplit = (max_ctx + p.chunk - 1) / p.chunk;
+  return p;
+}
+
+hipError_t g_last_hip = hipSuccess;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return ATTN_OK;
+  g_last_hip = e;
+  return ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_str(int status) {
+  switch (status) {
+    case ATTN_OK:
+      return "ATTN_OK";
+    case ATTN_ERR_INVALID:
+      return "ATTN_ERR_INVALID: invalid argument";
+    case ATTN_ERR_UNSUPPORTED:
+      return "ATTN_ERR_UNSUPPORTED: shape or dtype outside the built kernel set";
+    case ATTN_ERR_WORKSPACE:
+      return "ATTN_ERR_WORKSPACE: workspace missing or too small";
+    case ATTN_ERR_HIP:
+      return "ATTN_ERR_HIP: HIP runtime error";
+    default:
+      return "unknown attn status";
+  }
+}
+
+size_t attn_prefill_workspace_bytes(int B, int S, int Nkv, int Dh, float rope_theta, int dtype) {
+  if (!(rope_theta > 0.f) || B <= 0 || S <= 0 || Nkv <= 0 || Dh <= 0) return 0;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return 0;
+  const size_t table = align_up((size_t)S * (size_t)(Dh / 2) * sizeof(float2));
+  const size_t krot = align_up((size_t)B * (size_t)S * (size_t)Nkv * (size_t)Dh * esize(dtype));
+  return table + krot;
+}
+
+int attn_prefill(const void* q, const void* k, const void* v, void* out, int B, int S, int Nh, int Nkv, int Dh,
+                 float rope_theta, int causal, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  if (B < 0 || S < 0 || Nh <= 0 || Nkv <= 0 || Dh <= 0) return ATTN_ERR_INVALID;
+  if (Nh % Nkv != 0) return ATTN_ERR_INVALID;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVALID;
+  if (!std::isfinite(rope_theta) || !std::isfinite(scale)) return ATTN_ERR_INVALID;
+  if (!prefill_supported(dtype, Dh)) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)B * S * Nh > (1LL << 40)) return ATTN_ERR_INVALID;
+  if (B == 0 || S == 0) return ATTN_OK;
+  if (!q || !k || !v || !out) return ATTN_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_ERR_INVALID;
+  const bool rope = rope_theta > 0.f;
+  const size_t need = attn_prefill_workspace_bytes(B, S, Nkv, Dh, rope_theta, dtype);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
+    return ATTN_ERR_WORKSPACE;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const double sc = scale > 0.f ? (double)scale : 1.0 / std::sqrt((double)Dh);
+  PrefillArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.table = nullptr;
+  a.B = B;
+  a.S = S;
+  a.Nh = Nh;
+  a.Nkv = Nkv;
+  a.D = Dh;
+  a.scale_log2 = (float)(sc * 1.4426950408889634);
+  a.causal = causal ? 1 : 0;
+
+  if (rope) {
+    float2* table = static_cast<float2*>(workspace);
+    void* krot = static_cast<char*>(workspace) + align_up((size_t)S * (size_t)(Dh / 2) * sizeof(float2));
+    hipError_t e = launch_rope_table(table, S, Dh, (double)rope_theta, st);
+    if (e != hipSuccess) return hip_status(e);
+    const long long rows = (long long)B * S * Nkv;
+    if (dtype == ATTN_BF16)
+      e = launch_rope_rotate_table<bf16_t>(static_cast<const bf16_t*>(k), static_cast<bf16_t*>(krot), table, rows,
+                                           S, Nkv, Dh, st);
+    else
+      e = launch_rope_rotate_table<float>(static_cast<const float*>(k), static_cast<float*>(krot), table, rows, S,
+                                          Nkv, Dh, st);
+    if (e != hipSuccess) return hip_status(e);
+    a.table = table;
+    a.k = krot;
+  }
+  const hipError_t e = dtype == ATTN_BF16 ? launch_prefill_bf16(a, st) : launch_prefill_f32(a, st);
+  return hip_status(e);
+}
+
+size_t attn_decode_workspace_bytes(int B, int Nh, int Nkv, int Dqk, int Dv, int max_ctx, int dtype) {
+  if (B <= 0 || Nh <= 0 || Nkv <= 0 || Dv <= 0 || max_ctx <= 0 || dtype != ATTN_BF16) return 0;
+  if (Nh % Nkv != 0) return 0;
+  const DecodePlan p = decode_plan(B, Nh, Nkv, Dqk, Dv, max_ctx);
+  const size_t slots = (size_t)B * (size_t)Nh * (size_t)p.nsplit;
+  return align_up(slots * (size_t)Dv * sizeof(float)) + align_up(slots * 2 * sizeof(float));
+}
+
+int attn_decode(const void* q, const void* kcache, const void* vcache, const int32_t* ctx_lens, void* out, int B,
+                int Nh, int Nkv, int Dqk, int Dv, int max_ctx, long long ldk, long long ldv, float rope_theta,
+                float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || Nh <= 0 || Nkv <= 0 || Dqk <= 0 || Dv <= 0 || max_ctx <= 0) return ATTN_ERR_INVALID;
+  if (Nh % Nkv != 0 || ldk < Dqk || ldv < Dv) return ATTN_ERR_INVALID;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVALID;
+  if (!std::isfinite(rope_theta) || !std::isfinite(scale)) return ATTN_ERR_INVALID;
+  if (ldk % 8 != 0 || ldv % 8 != 0) return ATTN_ERR_INVALID;  // 16-byte aligned rows
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  const bool mla = is_mla_shape(Nkv, Dqk, Dv);
+  if (mla) {
+    if (vcache != kcache || ldv != ldk || Nh % 16 != 0) return ATTN_ERR_UNSUPPORTED;
+    if (rope_theta > 0.f) return ATTN_ERR_UNSUPPORTED;
+  } else {
+    if (Dqk != Dv || (Dqk != 64 && Dqk != 128)) return ATTN_ERR_UNSUPPORTED;
+  }
+  if (B == 0) return ATTN_OK;
+  if (!q || !kcache || !vcache || !ctx_lens || !out) return ATTN_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(ctx_lens) & 3u))
+    return ATTN_ERR_INVALID;
+  const size_t need = attn_decode_workspace_bytes(B, Nh, Nkv, Dqk, Dv, max_ctx, dtype);
+  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return ATTN_ERR_WORKSPACE;
+
+  const DecodePlan p = decode_plan(B, Nh, Nkv, Dqk, Dv, max_ctx);
+  const size_t slots = (size_t)B * (size_t)Nh * (size_t)p.nsplit;
+  DecodeArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.kc = static_cast<const uint16_t*>(kcache);
+  a.vc = static_cast<const uint16_t*>(vcache);
+  a.ctx_lens = ctx_lens;
+  a.out = static_cast<uint16_t*>(out);
+  a.part_o = static_cast<float*>(workspace);
+  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(slots * (size_t)Dv * sizeof(float)));
+  a.B = B;
+  a.Nh = Nh;
+  a.Nkv = Nkv;
+  a.Dqk = Dqk;
+  a.Dv = Dv;
+  a.max_ctx = max_ctx;
+  a.ldk = ldk;
+  a.ldv = ldv;
+  const double sc = scale > 0.f ? (double)scale : 1.0 / std::sqrt((double)Dqk);
+  a.scale_log2 = (float)(sc * 1.4426950408889634);
+  a.rope_theta = rope_theta > 0.f ? (double)rope_theta : 0.0;
+  a.chunk = p.chunk;
+  a.nsplit = p.nsplit;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = mla ? launch_decode_mla(a, st) : launch_decode_gqa(a, st);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(launch_decode_reduce(a, st));
+}
+
+int rope_apply(void* x, const int32_t* positions, int B, int S, int N, int Dh, float theta, int interleaved,
+               int dtype, void* stream) {
+  if (B < 0 || S < 0 || N <= 0 || Dh <= 0 || Dh % 2 != 0) return ATTN_ERR_INVALID;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVALID;
+  if (!std::isfinite(theta) || !(theta > 0.f)) return ATTN_ERR_INVALID;
+  if (Dh > 1024) return ATTN_ERR_UNSUPPORTED;
+  if (B == 0 || S == 0) return ATTN_OK;
+  if (!x) return ATTN_ERR_INVALID;
+  if ((reinterpret_cast<uintptr_t>(x) & (esize(dtype) - 1)) || (reinterpret_cast<uintptr_t>(positions) & 3u))
+    return ATTN_ERR_INVALID;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const long long rows = (long long)B * S * N;
+  const hipError_t e =
+      dtype == ATTN_BF16
+          ? launch_rope_apply<bf16_t>(static_cast<bf16_t*>(x), positions, rows, S, N, Dh, (double)theta,
+                                      interleaved ? 1 : 0, st)
+          : launch_rope_apply<float>(static_cast<float*>(x), positions, rows, S, N, Dh, (double)theta,
+                                     interleaved ? 1 : 0, st);
+  return hip_status(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// Launchers of the gfx950 kernels, called by the C ABI in api.hip after argument validation.
+// Every launcher only enqueues work on `st` and returns hipGetLastError().
+#pragma once
+
+#include "common.hpp"
+
+namespace attn {
+
+// bf16 storage element (bit pattern); arithmetic is always done in fp32.
+struct bf16_t {
+  uint16_t bits;
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return bf16_to_f32(x.bits); }
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return bf16_t{f32_to_bf16(x)}; }
+
+// ---- RoPE (rope.hip) ----
+hipError_t launch_rope_table(float2* table, int S, int D, double theta, hipStream_t st);
+template <typename T>
+hipError_t launch_rope_rotate_table(const T* src, T* dst, const float2* table, long long rows, int S, int N,
+                                    int D, hipStream_t st);
+template <typename T>
+hipError_t launch_rope_apply(T* x, const int* positions, long long rows, int S, int N, int D, double theta,
+                             int interleaved, hipStream_t st);
+
+// ---- Prefill (prefill_f32.hip, prefill_bf16.hip) ----
+struct PrefillArgs {
+  const void* q;
+  const void* k;  // rotated copy when table != nullptr
+  const void* v;
+  void* out;
+  const float2* table;  // [S][D/2] (cos, sin) or nullptr: q used as given
+  int B, S, Nh, Nkv, D;
+  float scale_log2;  // softmax scale * log2(e)
+  int causal;
+};
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t st);
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st);
+
+// ---- Decode (decode.hip, decode_mla.hip) ----
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint16_t* kc;
+  const uint16_t* vc;
+  const int* ctx_lens;
+  uint16_t* out;
+  float* part_o;   // [B][Nh][nsplit][Dv] fp32
+  float* part_ml;  // [B][Nh][nsplit][2]  fp32 (running max in log2 units, sum)
+  int B, Nh, Nkv, Dqk, Dv, max_ctx;
+  long long ldk, ldv;
+  float scale_log2;
+  double rope_theta;  // <= 0: none
+  int chunk, nsplit;
+};
+hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t st);
+
+}  // namespace attn

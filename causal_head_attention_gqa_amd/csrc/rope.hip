@@ -1,0 +1,118 @@
+// RoPE on gfx950: angle table, table-driven rotation (prefill pre-pass for K) and the standalone
+// in-place rotation with arbitrary positions.
+//
+// Frequencies theta_i = base^(-2i/D), i = 0 .. D/2-1 ("2.7 Transformer Decoder Block完整解析" §4,
+// "Transformer 架构快速入门" §8.2); angle = position * theta_i, evaluated in fp64 so that large
+// positions keep full fp32 accuracy after the single rounding of cos/sin. Half-split pairs
+// (i, i + D/2) follow the first page's apply_rope; adjacent pairs (2i, 2i+1) follow
+// "Transformer 架构快速入门" §8.3. Only Q and K are rotated (same page, §8.5).
+#include "kernels.hpp"
+
+namespace attn {
+
+// table[pos * half + i] = (cos(pos * theta_i), sin(pos * theta_i)), fp64 angle, fp32 result.
+__global__ void rope_table_kernel(float2* __restrict__ table, int S, int half, double neg2_log2theta_over_d) {
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long long)S * half) return;
+  const int pos = (int)(idx / half);
+  const int i = (int)(idx % half);
+  const double inv_freq = exp2(neg2_log2theta_over_d * (double)i);
+  double s, c;
+  sincos((double)pos * inv_freq, &s, &c);
+  table[idx] = make_float2((float)c, (float)s);
+}
+
+// Rotates half-split pairs of src [rows, D] (row r has position (r / N) % S) into dst with the
+// table. Each thread owns 8 consecutive pair indices of one row: two 8-element vectors.
+template <typename T>
+__global__ void rope_rotate_table_kernel(const T* __restrict__ src, T* __restrict__ dst,
+                                         const float2* __restrict__ table, long long rows, int S, int N,
+                                         int D) {
+  const int groups = D / 16;  // 8 pairs per thread
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= rows * groups) return;
+  const long long row = idx / groups;
+  const int i0 = (int)(idx % groups) * 8;
+  const int pos = (int)((row / N) % S);
+  const T* x = src + row * D;
+  T* y = dst + row * D;
+  const float2* tb = table + (long long)pos * (D / 2) + i0;
+  float a[8], b[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = to_f32(x[i0 + e]);
+    b[e] = to_f32(x[i0 + D / 2 + e]);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float2 cs = tb[e];
+    const float ra = a[e] * cs.x - b[e] * cs.y;
+    const float rb = a[e] * cs.y + b[e] * cs.x;
+    y[i0 + e] = from_f32<T>(ra);
+    y[i0 + D / 2 + e] = from_f32<T>(rb);
+  }
+}
+
+// In-place rotation with explicit positions; fp64 angle and fp64 rotation, one rounding at the
+// store. One thread per pair.
+template <typename T>
+__global__ void rope_apply_kernel(T* __restrict__ x, const int* __restrict__ positions, long long rows,
+                                  int S, int N, int D, double neg2_log2theta_over_d, int interleaved) {
+  const int half = D / 2;
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= rows * half) return;
+  const long long row = idx / half;
+  const int i = (int)(idx % half);
+  const long long tok = row / N;  // b * S + s
+  const int pos = positions ? positions[tok] : (int)(tok % S);
+  const double inv_freq = exp2(neg2_log2theta_over_d * (double)i);
+  double s, c;
+  sincos((double)pos * inv_freq, &s, &c);
+  T* p = x + row * D;
+  const int ia = interleaved ? 2 * i : i;
+  const int ib = interleaved ? 2 * i + 1 : i + half;
+  const double a = (double)to_f32(p[ia]);
+  const double b = (double)to_f32(p[ib]);
+  p[ia] = from_f32<T>((float)(a * c - b * s));
+  p[ib] = from_f32<T>((float)(a * s + b * c));
+}
+
+hipError_t launch_rope_table(float2* table, int S, int D, double theta, hipStream_t st) {
+  const long long n = (long long)S * (D / 2);
+  if (n == 0) return hipSuccess;
+  const double k = -2.0 * log2(theta) / (double)D;
+  rope_table_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(table, S, D / 2, k);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_rope_rotate_table(const T* src, T* dst, const float2* table, long long rows, int S, int N,
+                                    int D, hipStream_t st) {
+  const long long n = rows * (D / 16);
+  if (n == 0) return hipSuccess;
+  rope_rotate_table_kernel<T><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(src, dst, table, rows,
+                                                                                       S, N, D);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_rope_apply(T* x, const int* positions, long long rows, int S, int N, int D, double theta,
+                             int interleaved, hipStream_t st) {
+  const long long n = rows * (D / 2);
+  if (n == 0) return hipSuccess;
+  const double k = -2.0 * log2(theta) / (double)D;
+  rope_apply_kernel<T><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(x, positions, rows, S, N, D, k,
+                                                                                interleaved);
+  return hipGetLastError();
+}
+
+template hipError_t launch_rope_rotate_table<float>(const float*, float*, const float2*, long long, int, int, int,
+                                                    hipStream_t);
+template hipError_t launch_rope_rotate_table<bf16_t>(const bf16_t*, bf16_t*, const float2*, long long, int, int,
+                                                     int, hipStream_t);
+template hipError_t launch_rope_apply<float>(float*, const int*, long long, int, int, int, double, int,
+                                             hipStream_t);
+template hipError_t launch_rope_apply<bf16_t>(bf16_t*, const int*, long long, int, int, int, double, int,
+                                              hipStream_t);
+
+}  // namespace attn

@@ -1,0 +1,186 @@
+"""ctypes binding of libattn_gfx950.so: argument marshalling only.
+
+Every step of the computation runs in the HIP library; this module turns torch tensors into
+device pointers, sizes the outputs and workspaces (torch allocates them), and passes torch's
+current HIP stream. There is no fallback: if the shared library is missing or a call fails,
+an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libattn_gfx950.so")
+
+ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(5)
+ATTN_F32, ATTN_BF16 = 0, 1
+
+EXPORTS = (
+    "attn_status_str",
+    "attn_prefill_workspace_bytes",
+    "attn_prefill",
+    "attn_decode_workspace_bytes",
+    "attn_decode",
+    "rope_apply",
+)
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what} failed: {status_str(status)}")
+
+
+def load() -> ctypes.CDLL:
+    """Load the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m causal_head_attention_gqa_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    c_int, c_float, c_size, c_vp, c_ll = ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_longlong
+    lib.attn_status_str.restype = ctypes.c_char_p
+    lib.attn_status_str.argtypes = [c_int]
+    lib.attn_prefill_workspace_bytes.restype = c_size
+    lib.attn_prefill_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_float, c_int]
+    lib.attn_prefill.restype = c_int
+    lib.attn_prefill.argtypes = [c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_float, c_int, c_float,
+                                 c_int, c_vp, c_size, c_vp]
+    lib.attn_decode_workspace_bytes.restype = c_size
+    lib.attn_decode_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int, c_int]
+    lib.attn_decode.restype = c_int
+    lib.attn_decode.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_int, c_ll, c_ll,
+                                c_float, c_float, c_int, c_vp, c_size, c_vp]
+    lib.rope_apply.restype = c_int
+    lib.rope_apply.argtypes = [c_vp, c_vp, c_int, c_int, c_int, c_int, c_float, c_int, c_int, c_vp]
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load().attn_status_str(int(status)).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != ATTN_OK:
+        raise AttnError(status, what)
+
+
+# ------------------------------------------------------------------------------ torch side ----
+def _torch():
+    import torch  # noqa: WPS433 (torch is plumbing: device memory and streams)
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream_ptr(dev) -> int:
+    return _torch().cuda.current_stream(dev).cuda_stream
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def prefill_workspace_bytes(B: int, S: int, Nkv: int, Dh: int, rope_theta: float, dtype: int) -> int:
+    return int(load().attn_prefill_workspace_bytes(B, S, Nkv, Dh, float(rope_theta), dtype))
+
+
+def decode_workspace_bytes(B: int, Nh: int, Nkv: int, Dqk: int, Dv: int, max_ctx: int, dtype: int) -> int:
+    return int(load().attn_decode_workspace_bytes(B, Nh, Nkv, Dqk, Dv, max_ctx, dtype))
+
+
+def prefill(q, k, v, *, rope_theta: float = 0.0, causal: bool = True, scale: float | None = None, out=None,
+            workspace=None):
+    """Causal (or full) attention over [B, S, N, Dh] BSHD tensors; returns out [B, S, Nh, Dh]."""
+    torch = _torch()
+    _need_cuda(q, k, v)
+    B, S, Nh, Dh = q.shape
+    Nkv = k.shape[2]
+    if k.shape != (B, S, Nkv, Dh) or v.shape != (B, S, Nkv, Dh):
+        raise ValueError("q/k/v shapes disagree")
+    dt = _dtype_code(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    _need_cuda(out)
+    need = prefill_workspace_bytes(B, S, Nkv, Dh, rope_theta, dt)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load().attn_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, S, Nh, Nkv, Dh,
+                             float(rope_theta), 1 if causal else 0, float(scale or 0.0), dt, ws_ptr, ws_len,
+                             _stream_ptr(q.device))
+    _check(st, "attn_prefill")
+    return out
+
+
+def decode(q, kcache, vcache, ctx_lens, *, scale: float | None = None, rope_theta: float = 0.0, out=None,
+           workspace=None):
+    """One query token per sequence against a KV cache.
+
+    q [B, Nh, Dqk]; kcache [B, max_ctx, Nkv, Dqk]-shaped (last dim may be a view of a wider row:
+    its row pitch is taken from the stride); vcache [B, max_ctx, Nkv, Dv] likewise, possibly a
+    view into kcache's rows (MLA: vcache = kcache[..., :512]); ctx_lens int32 [B] on the GPU.
+    Returns out [B, Nh, Dv] (bf16).
+    """
+    torch = _torch()
+    _need_cuda(q, ctx_lens)
+    for t in (kcache, vcache):
+        if not t.is_cuda:
+            raise ValueError("caches must live on the GPU")
+        B_, T_, N_, D_ = t.shape
+        if t.stride(3) != 1 or t.stride(1) != N_ * t.stride(2) or t.stride(0) != T_ * t.stride(1):
+            raise ValueError("cache must be [B, max_ctx, Nkv, row] with a dense row pitch")
+    B, Nh, Dqk = q.shape
+    _, max_ctx, Nkv, Dk = kcache.shape
+    Dv = vcache.shape[3]
+    if Dk != Dqk or vcache.shape[:3] != kcache.shape[:3]:
+        raise ValueError("cache shapes disagree with q")
+    if ctx_lens.dtype != torch.int32 or ctx_lens.shape != (B,):
+        raise ValueError("ctx_lens must be int32 [B]")
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty((B, Nh, Dv), dtype=q.dtype, device=q.device)
+    need = decode_workspace_bytes(B, Nh, Nkv, Dqk, Dv, max_ctx, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = load().attn_decode(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), ctx_lens.data_ptr(), out.data_ptr(),
+                            B, Nh, Nkv, Dqk, Dv, max_ctx, kcache.stride(2), vcache.stride(2), float(rope_theta),
+                            float(scale or 0.0), dt, workspace.data_ptr(),
+                            workspace.numel() * workspace.element_size(), _stream_ptr(q.device))
+    _check(st, "attn_decode")
+    return out
+
+
+def rope_apply_(x, *, theta: float, positions=None, interleaved: bool = False):
+    """Rotate x [B, S, N, Dh] in place; positions: int32 [B, S] on the GPU or None (= s)."""
+    _need_cuda(x)
+    B, S, N, Dh = x.shape
+    pos_ptr = None
+    if positions is not None:
+        _need_cuda(positions)
+        if positions.numel() != B * S:
+            raise ValueError("positions must hold B*S entries")
+        pos_ptr = positions.data_ptr()
+    st = load().rope_apply(x.data_ptr(), pos_ptr, B, S, N, Dh, float(theta), 1 if interleaved else 0,
+                           _dtype_code(x), _stream_ptr(x.device))
+    _check(st, "rope_apply")
+    return x

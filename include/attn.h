@@ -1,0 +1,123 @@
+/*
+ * attn.h - C ABI of the MI355X (gfx950) causal-attention library (libattn_gfx950.so).
+ *
+ * What the library computes (sources cited by page title and section):
+ *   out = softmax(scale * Q K^T + M) V            per (batch, query head)
+ *   "Transformer 架构快速入门" §4.2-4.5 (scores, 1/sqrt(D_h) scale, causal mask, weighted sum of V)
+ *   "2.7 Transformer Decoder Block完整解析" §3 (additive -inf causal mask, skipped by index in tiles)
+ *   "Transformer 架构快速入门" §6 (MHA / GQA / MQA: query head h reads KV head h / (N_h / N_kv))
+ *   "2.7 ..." §4 and "Transformer 架构快速入门" §8 (RoPE on Q and K only)
+ *   "Transformer 架构完全深度解析" §九 and "Transformer 架构快速入门" §13.2 (KV-cache decode)
+ *   "Transformer 与 LLM：结构、实现与算量" slide 06 (MLA absorbed decode: MQA with one 576-dim row)
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller. The library allocates nothing
+ *     and keeps no state between calls; concurrent calls on different streams are safe as long
+ *     as they use different workspaces.
+ *   - Layouts are row-major. Prefill tensors are BSHD: element (b, s, h, d) of a [B, S, N, D]
+ *     tensor sits at ((b * S + s) * N + h) * D + d.
+ *   - dtype: ATTN_BF16 means bf16 storage for every floating tensor argument with fp32
+ *     accumulation inside; ATTN_F32 means fp32 storage and fp32 arithmetic.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL selects the null stream).
+ *     Arguments are validated on the host BEFORE any launch; on an error nothing is launched
+ *     and no output is touched. Launch failures are reported as ATTN_ERR_HIP. Faults inside a
+ *     kernel surface at the caller's next synchronisation, as for any HIP kernel.
+ *   - Tensor pointers must be 16-byte aligned (ATTN_ERR_INVALID otherwise); rope_apply only
+ *     needs element alignment.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef ATTN_GFX950_H
+#define ATTN_GFX950_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID = 1,      /* bad pointer, size, alignment or argument combination */
+  ATTN_ERR_UNSUPPORTED = 2,  /* valid request outside the built kernel set (head dim, dtype, ...) */
+  ATTN_ERR_WORKSPACE = 3,    /* workspace missing or smaller than the *_workspace_bytes figure */
+  ATTN_ERR_HIP = 4           /* the HIP runtime rejected a launch */
+} attn_status;
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+/* Human-readable name of a status code (static storage). */
+const char* attn_status_str(int status);
+
+/* ------------------------------------------------------------------------------------------
+ * Prefill: causal (or full) self-attention over whole sequences, with optional RoPE.
+ *   "Transformer 架构快速入门" §4 (one head), §6.3 (GQA sharing); "2.7 ..." §3.3 (tile skipping).
+ *
+ * q   [B, S, Nh,  Dh]  read only
+ * k   [B, S, Nkv, Dh]  read only (never modified: rotated keys go to the workspace)
+ * v   [B, S, Nkv, Dh]  read only
+ * out [B, S, Nh,  Dh]  written
+ * Nh % Nkv == 0; query head h uses KV head h / (Nh / Nkv).
+ * rope_theta > 0 rotates q and k (half-split pairs (i, i + Dh/2), frequency
+ *   rope_theta^(-2i/Dh), i = 0-based, angle = position * frequency evaluated in fp64,
+ *   positions 0 .. S-1 of each sequence); rope_theta <= 0 uses q and k as given.
+ * causal != 0 masks key j for query i when j > i; causal == 0 is full attention.
+ * scale <= 0 selects 1 / sqrt(Dh).
+ * Supported: ATTN_BF16 with Dh in {64, 128}; ATTN_F32 with Dh in {16, 32, 64}.
+ * B == 0 or S == 0 is a valid empty call (nothing launched).
+ * workspace: device buffer of at least attn_prefill_workspace_bytes(...) bytes (may be NULL
+ *   when that figure is 0). Its contents are scratch; it must not be used by another call
+ *   until this one has completed on `stream`.
+ * ------------------------------------------------------------------------------------------ */
+size_t attn_prefill_workspace_bytes(int B, int S, int Nkv, int Dh, float rope_theta, int dtype);
+
+int attn_prefill(const void* q, const void* k, const void* v, void* out,
+                 int B, int S, int Nh, int Nkv, int Dh,
+                 float rope_theta, int causal, float scale, int dtype,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * KV-cache decode: one new query token per sequence attends to every cached key of its head.
+ *   "Transformer 架构完全深度解析" §九 (append new K/V, then attend the new query to the cache),
+ *   "Transformer 与 LLM：结构、实现与算量" slide 06 (absorbed MLA = MQA over one shared row).
+ *
+ * q        [B, Nh, Dqk]                      read only
+ * kcache   element (b, t, g, d) at ((b * max_ctx + t) * Nkv + g) * ldk + d,  d < Dqk
+ * vcache   element (b, t, g, d) at ((b * max_ctx + t) * Nkv + g) * ldv + d,  d < Dv
+ *          vcache MAY equal kcache (MLA: V is the first Dv elements of the cached K row).
+ * ctx_lens device int32 [B]: keys 0 .. ctx_lens[b]-1 are attended, the new token's own key
+ *          included (it is appended before the call). Values must lie in [1, max_ctx]; a value
+ *          outside is clamped to [0, max_ctx] for memory safety and 0 keys give an all-zero
+ *          output row (the result is then not meaningful).
+ * out      [B, Nh, Dv]                      written
+ * rope_theta > 0 rotates q at position ctx_lens[b]-1 (the cache holds already-rotated keys);
+ *          only for Dqk == Dv. scale <= 0 selects 1 / sqrt(Dqk).
+ * Supported (ATTN_BF16 only): Dqk == Dv in {64, 128} with any Nh % Nkv == 0 whose group size
+ *   Nh / Nkv is a multiple of 1, 2, 4 or 8 (heads are processed in groups of up to 8);
+ *   and the MLA form Dqk = 576, Dv = 512, Nkv = 1, vcache == kcache, ldv == ldk, Nh % 16 == 0.
+ * workspace: at least attn_decode_workspace_bytes(...) bytes (split-KV partial results).
+ * ------------------------------------------------------------------------------------------ */
+size_t attn_decode_workspace_bytes(int B, int Nh, int Nkv, int Dqk, int Dv, int max_ctx, int dtype);
+
+int attn_decode(const void* q, const void* kcache, const void* vcache, const int32_t* ctx_lens,
+                void* out, int B, int Nh, int Nkv, int Dqk, int Dv, int max_ctx,
+                long long ldk, long long ldv, float rope_theta, float scale, int dtype,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * RoPE, in place: rotate every head vector of x [B, S, N, Dh] by its position.
+ *   "2.7 ..." §4 (half-split pairs), "Transformer 架构快速入门" §8.2-8.3 (frequencies, adjacent
+ *   pairs), "Transformer 架构完全深度解析" §七.
+ * positions: device int32 [B * S] (position of token (b, s) at b * S + s), or NULL for s.
+ * interleaved == 0: pairs (i, i + Dh/2); interleaved != 0: pairs (2i, 2i + 1).
+ * Frequency theta^(-2i/Dh), i = 0 .. Dh/2 - 1; angle = position * frequency in fp64.
+ * Supported: ATTN_F32 and ATTN_BF16, Dh even and <= 1024, theta > 0.
+ * ------------------------------------------------------------------------------------------ */
+int rope_apply(void* x, const int32_t* positions, int B, int S, int N, int Dh,
+               float theta, int interleaved, int dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_GFX950_H */

@@ -1,0 +1,104 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every function the
+header declares, and rejects bad arguments before anything is launched."""
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+def _lib():
+    from causal_head_attention_gqa_amd import lib
+    if not os.path.exists(lib.LIB_PATH):
+        pytest.fail("libattn_gfx950.so is not built (run __graft_entry__.build())")
+    return lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", text,
+                                 flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    fns = declared_functions()
+    for name in ("attn_prefill", "attn_decode", "rope_apply", "attn_prefill_workspace_bytes",
+                 "attn_decode_workspace_bytes", "attn_status_str"):
+        assert name in fns
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    from causal_head_attention_gqa_amd import lib
+    _lib()
+    assert lib.status_str(0) == "ATTN_OK"
+    assert "UNSUPPORTED" in lib.status_str(2)
+    assert "unknown" in lib.status_str(99)
+
+
+P = 0x10000  # a 16-byte-aligned stand-in address; these calls never reach a launch
+
+
+def test_prefill_argument_errors():
+    L = _lib()
+    call = lambda **kw: L.attn_prefill(  # noqa: E731
+        kw.get("q", P), kw.get("k", P), kw.get("v", P), kw.get("o", P), kw.get("B", 1), kw.get("S", 8),
+        kw.get("Nh", 4), kw.get("Nkv", 2), kw.get("Dh", 64), kw.get("rope", 0.0), 1, 0.0, kw.get("dt", 1),
+        kw.get("ws", None), kw.get("wsb", 0), None)
+    assert call(Nh=3, Nkv=2) == 1               # heads not a multiple of KV heads
+    assert call(Dh=96) == 2                     # unsupported head dim
+    assert call(Dh=16) == 2                     # bf16 needs 64 or 128
+    assert call(dt=7) == 1                      # unknown dtype
+    assert call(B=-1) == 1
+    assert call(q=None) == 1                    # null pointer
+    assert call(q=P + 2) == 1                   # misaligned
+    assert call(rope=1e4) == 3                  # RoPE needs a workspace
+    assert call(rope=1e4, ws=P, wsb=16) == 3    # too small
+    assert call(rope=float("nan")) == 1
+    assert call(B=0) == 0 and call(S=0) == 0    # empty: nothing to do
+
+
+def test_decode_argument_errors():
+    L = _lib()
+    def call(**kw):
+        return L.attn_decode(kw.get("q", P), kw.get("kc", P), kw.get("vc", P), kw.get("ctx", P), kw.get("o", P),
+                             kw.get("B", 2), kw.get("Nh", 8), kw.get("Nkv", 2), kw.get("Dqk", 128), kw.get("Dv", 128),
+                             kw.get("T", 100), kw.get("ldk", 128), kw.get("ldv", 128), kw.get("rope", 0.0), 0.0,
+                             kw.get("dt", 1), kw.get("ws", None), kw.get("wsb", 0), None)
+    assert call(Nh=6, Nkv=4) == 1
+    assert call(ldk=64) == 1                    # row pitch shorter than the row
+    assert call(Dqk=96, Dv=96, ldk=96, ldv=96) == 2
+    assert call(dt=0) == 2                      # fp32 decode is not built
+    assert call(Dqk=576, Dv=512, Nkv=1, Nh=128, ldk=576, ldv=576, vc=P + 4096) == 2  # MLA needs V aliasing K
+    assert call(Dqk=576, Dv=512, Nkv=1, Nh=128, ldk=576, ldv=576, rope=1e4) == 2
+    assert call() == 3                          # no workspace
+    assert call(ws=P, wsb=8) == 3
+    assert call(ctx=None) == 1
+    assert call(B=0) == 0
+
+
+def test_rope_argument_errors():
+    L = _lib()
+    assert L.rope_apply(P, None, 1, 4, 2, 63, 1e4, 0, 1, None) == 1   # odd head dim
+    assert L.rope_apply(P, None, 1, 4, 2, 64, 0.0, 0, 1, None) == 1   # theta must be > 0
+    assert L.rope_apply(P, None, 1, 4, 2, 2048, 1e4, 0, 1, None) == 2
+    assert L.rope_apply(P + 1, None, 1, 4, 2, 64, 1e4, 0, 1, None) == 1
+    assert L.rope_apply(P, None, 0, 4, 2, 64, 1e4, 0, 1, None) == 0
+
+
+def test_workspace_queries():
+    from causal_head_attention_gqa_amd import lib
+    _lib()
+    assert lib.prefill_workspace_bytes(4, 8192, 8, 128, 0.0, 1) == 0
+    # RoPE: fp32 (cos, sin) table [S, Dh/2] plus rotated keys
+    assert lib.prefill_workspace_bytes(4, 8192, 8, 128, 5e5, 1) == 8192 * 64 * 8 + 4 * 8192 * 8 * 128 * 2
+    ws = lib.decode_workspace_bytes(64, 32, 8, 128, 128, 8192, 1)
+    assert ws > 0 and ws % 256 == 0

@@ -1,0 +1,130 @@
+"""Parity of the HIP KV-cache decode paths (GQA split-KV and MLA-absorbed) against the oracle.
+
+Small cases cover MHA/GQA/MQA groups, context lengths that end inside a chunk, a context of
+one key, and RoPE applied to the query in-kernel. The full Llama-3-8B-shaped decode (B=64,
+contexts drawn in [1024, 8192]) and the full MLA-absorbed decode (B=32, 128 heads, 576-dim
+shared row, context 4096) are compared over every output. Cache rows beyond a sequence's
+context are filled with NaN in one test to show they are never read.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import BF16_TOL, max_abs, to_dev, values
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_decode(q, kc, vc, ctx, scale=None, rope=0.0, mla=False):
+    """Per-sequence oracle calls on fp64 slices (keeps host memory and time bounded)."""
+    B, Nh, _ = q.shape
+    Dv = 512 if mla else vc.shape[3]
+    out = np.empty((B, Nh, Dv))
+    for b in range(B):
+        c = int(ctx[b])
+        kb = values(kc[b:b + 1, :c], "bf16").astype(np.float64)
+        vb = kb[..., :Dv] if mla else values(vc[b:b + 1, :c], "bf16").astype(np.float64)
+        out[b] = oracle.decode(values(q[b:b + 1], "bf16"), kb, vb, np.array([c]), scale=scale, rope_theta=rope)[0]
+    return out
+
+
+def _gpu_decode(q, kc, vc, ctx, scale=None, rope=0.0, mla=False):
+    import causal_head_attention_gqa_amd as attn
+    torch = __import__("torch")
+    kd = to_dev(kc, "bf16")
+    vd = kd[..., :512] if mla else to_dev(vc, "bf16")
+    ctx_d = torch.as_tensor(np.asarray(ctx, np.int32), device="cuda")
+    out = attn.decode(to_dev(q, "bf16"), kd, vd, ctx_d, scale=scale, rope_theta=rope)
+    return out.float().cpu().numpy()
+
+
+GQA_CASES = [
+    # B, Nh, Nkv, D, max_ctx, ctx list (None: random in [1, max_ctx]), rope
+    (3, 32, 8, 128, 1500, [1, 777, 1500], 0.0),
+    (4, 8, 8, 128, 600, None, 0.0),       # MHA
+    (2, 16, 2, 64, 2049, [2049, 513], 0.0),  # group of 8
+    (5, 12, 1, 128, 300, None, 0.0),      # MQA with 12 heads -> groups of 4
+    (2, 32, 8, 128, 900, [900, 17], 5e5),  # q rotated at ctx-1
+    (3, 6, 2, 64, 100, [1, 2, 64], 1e4),
+]
+
+
+@pytest.mark.parametrize("case", GQA_CASES, ids=lambda c: "B%dH%dK%dD%dT%d" % c[:5])
+def test_decode_gqa_small(case):
+    B, Nh, Nkv, D, T, ctx, rope = case
+    wid = 400 + T
+    rng = np.random.default_rng(wid)
+    ctx = np.asarray(ctx if ctx is not None else rng.integers(1, T, B, endpoint=True), np.int32)
+    q = synth.normal(wid, 0, (B, Nh, D), "bf16")
+    kc = synth.normal(wid, 1, (B, T, Nkv, D), "bf16")
+    vc = synth.normal(wid, 2, (B, T, Nkv, D), "bf16")
+    got = _gpu_decode(q, kc, vc, ctx, rope=rope)
+    want = _oracle_decode(q, kc, vc, ctx, rope=rope)
+    assert max_abs(got, want) <= BF16_TOL
+
+
+def test_decode_never_reads_beyond_context():
+    B, Nh, Nkv, D, T = 3, 8, 2, 128, 700
+    ctx = np.array([5, 333, 700], np.int32)
+    q = synth.normal(450, 0, (B, Nh, D), "bf16")
+    kc = synth.normal(450, 1, (B, T, Nkv, D), "bf16")
+    vc = synth.normal(450, 2, (B, T, Nkv, D), "bf16")
+    clean = _gpu_decode(q, kc, vc, ctx)
+    kn, vn = kc.copy(), vc.copy()
+    for b, c in enumerate(ctx):
+        kn[b, c:] = 0x7FC0  # bf16 NaN
+        vn[b, c:] = 0x7FC0
+    dirty = _gpu_decode(q, kn, vn, ctx)
+    assert np.all(np.isfinite(dirty))
+    assert np.array_equal(clean, dirty)
+
+
+def test_mla_decode_small():
+    B, Nh, T = 2, 32, 300
+    ctx = np.array([300, 45], np.int32)
+    q = synth.normal(460, 0, (B, Nh, 576), "bf16")
+    kc = synth.normal(460, 1, (B, T, 1, 576), "bf16")
+    scale = 1.0 / math.sqrt(192)
+    got = _gpu_decode(q, kc, None, ctx, scale=scale, mla=True)
+    want = _oracle_decode(q, kc, None, ctx, scale=scale, mla=True)
+    assert max_abs(got, want) <= BF16_TOL
+
+
+def test_llama3_decode_full():
+    w = synth.LLAMA3_DECODE
+    q, kc, vc, ctx = w.inputs()
+    got = _gpu_decode(q, kc, vc, ctx)
+    want = _oracle_decode(q, kc, vc, ctx)
+    assert got.shape == (64, 32, 128)
+    assert max_abs(got, want) <= BF16_TOL
+
+
+def test_mla_decode_full():
+    w = synth.MLA_DECODE
+    q, kc, _, ctx = w.inputs()
+    got = _gpu_decode(q, kc, None, ctx, scale=w.scale, mla=True)
+    want = _oracle_decode(q, kc, None, ctx, scale=w.scale, mla=True)
+    assert got.shape == (32, 128, 512)
+    assert max_abs(got, want) <= BF16_TOL
+
+
+def test_prefill_equals_token_by_token_decode():
+    """With and without the KV cache the outputs agree ("Transformer 与 LLM" slide 02): prefill
+    with RoPE versus decoding every position against a cache of rotated keys."""
+    import causal_head_attention_gqa_amd as attn
+    torch = __import__("torch")
+    B, S, Nh, Nkv, D, th = 2, 96, 8, 2, 128, 5e5
+    q = to_dev(synth.normal(470, 0, (B, S, Nh, D), "bf16"), "bf16")
+    k = to_dev(synth.normal(470, 1, (B, S, Nkv, D), "bf16"), "bf16")
+    v = to_dev(synth.normal(470, 2, (B, S, Nkv, D), "bf16"), "bf16")
+    full = attn.prefill(q, k, v, rope_theta=th).float()
+    kcache = attn.rope_apply_(k.clone(), theta=th)
+    worst = 0.0
+    for t in range(S):
+        ctx = torch.full((B,), t + 1, dtype=torch.int32, device="cuda")
+        dec = attn.decode(q[:, t].contiguous(), kcache, v, ctx, rope_theta=th).float()
+        worst = max(worst, float((dec - full[:, t]).abs().max()))
+    assert worst <= BF16_TOL

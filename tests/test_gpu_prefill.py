@@ -1,0 +1,142 @@
+"""Parity of the HIP prefill path against the fp64 oracle (GPU only).
+
+Small cases span several 64-key tiles, every head-packing variant (MHA, GQA groups of 2/3/4,
+MQA), ragged tails and the non-causal form, and are compared element by element over the whole
+output. The two full-size workloads are checked in full (GPT-2-small shape) or on sampled rows
+the oracle computes one by one (Llama-3-8B shape), in the same launch configuration the
+benchmark times.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import BF16_TOL, F32_TOL, max_abs, to_dev, to_host_f64, values
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(B, S, Nh, Nkv, D, dtype, rope, causal, wid, scale=None):
+    import causal_head_attention_gqa_amd as attn
+    q = synth.normal(wid, 0, (B, S, Nh, D), dtype)
+    k = synth.normal(wid, 1, (B, S, Nkv, D), dtype)
+    v = synth.normal(wid, 2, (B, S, Nkv, D), dtype)
+    out = attn.prefill(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), rope_theta=rope, causal=causal,
+                       scale=scale)
+    got = to_host_f64(out)
+    want = oracle.prefill(values(q, dtype), values(k, dtype), values(v, dtype), causal=causal, rope_theta=rope,
+                          scale=scale)
+    return got, want, (q, k, v)
+
+
+SMALL_BF16 = [
+    # B, S, Nh, Nkv, D, rope, causal
+    (2, 200, 8, 2, 128, 5e5, True),    # GQA group 4, ragged tail
+    (1, 333, 6, 6, 64, 0.0, True),     # MHA, 128-position work-groups
+    (2, 130, 4, 2, 128, 1e4, True),    # GQA group 2
+    (1, 97, 8, 1, 64, 1e4, True),      # MQA, two head groups per KV head
+    (1, 150, 4, 1, 128, 0.0, False),   # full attention
+    (3, 1, 4, 4, 64, 1e4, True),       # single token
+    (1, 129, 12, 4, 64, 1e4, True),    # group of 3 -> one head per work-group
+    (1, 64, 4, 2, 128, 0.0, True),     # exactly one tile
+]
+
+
+@pytest.mark.parametrize("case", SMALL_BF16, ids=lambda c: "B%dS%dH%dK%dD%d_r%g_c%d" % c)
+def test_prefill_bf16_small(case):
+    B, S, Nh, Nkv, D, rope, causal = case
+    got, want, _ = _run(B, S, Nh, Nkv, D, "bf16", rope, causal, wid=100 + S)
+    assert max_abs(got, want) <= BF16_TOL
+
+
+SMALL_F32 = [
+    (1, 128, 4, 4, 16, 1e4, True),
+    (2, 150, 4, 2, 32, 1e4, True),
+    (1, 70, 8, 2, 64, 5e5, True),
+    (1, 33, 2, 1, 16, 0.0, False),
+]
+
+
+@pytest.mark.parametrize("case", SMALL_F32, ids=lambda c: "B%dS%dH%dK%dD%d_r%g_c%d" % c)
+def test_prefill_f32_small(case):
+    B, S, Nh, Nkv, D, rope, causal = case
+    got, want, _ = _run(B, S, Nh, Nkv, D, "f32", rope, causal, wid=200 + S)
+    assert max_abs(got, want) <= F32_TOL
+
+
+def test_tiny_f32_workload_full():
+    """B=1, S=128, 4 heads of 16, fp32, RoPE 1e4: every output within 1e-5 of the oracle."""
+    w = synth.TINY_F32
+    got, want, _ = _run(w.B, w.S, w.Nh, w.Nkv, w.Dh, w.dtype, w.rope_theta, True, wid=w.wid)
+    assert got.shape == (1, 128, 4, 16)
+    assert max_abs(got, want) <= F32_TOL
+
+
+def test_row0_is_v0_exactly():
+    """Position 0 sees only itself: out[:, 0, h] equals v[:, 0, h // G] bit for bit."""
+    import causal_head_attention_gqa_amd as attn
+    torch = __import__("torch")
+    q = synth.normal(300, 0, (2, 70, 8, 128), "bf16")
+    k = synth.normal(300, 1, (2, 70, 2, 128), "bf16")
+    v = synth.normal(300, 2, (2, 70, 2, 128), "bf16")
+    vd = to_dev(v, "bf16")
+    out = attn.prefill(to_dev(q, "bf16"), to_dev(k, "bf16"), vd, rope_theta=5e5)
+    for h in range(8):
+        assert torch.equal(out[:, 0, h], vd[:, 0, h // 4])
+
+
+def test_scale_argument():
+    got, want, _ = _run(1, 90, 4, 2, 64, "bf16", 0.0, True, wid=301, scale=0.3)
+    assert max_abs(got, want) <= BF16_TOL
+
+
+def test_causality_on_gpu():
+    """Changing keys/values after position t leaves outputs up to t unchanged."""
+    import causal_head_attention_gqa_amd as attn
+    torch = __import__("torch")
+    q = to_dev(synth.normal(302, 0, (1, 160, 4, 128), "bf16"), "bf16")
+    k = to_dev(synth.normal(302, 1, (1, 160, 1, 128), "bf16"), "bf16")
+    v = to_dev(synth.normal(302, 2, (1, 160, 1, 128), "bf16"), "bf16")
+    a = attn.prefill(q, k, v, rope_theta=1e4)
+    k2, v2 = k.clone(), v.clone()
+    k2[:, 100:] = 3.0
+    v2[:, 100:] = -7.0
+    b = attn.prefill(q, k2, v2, rope_theta=1e4)
+    assert torch.equal(a[:, :100], b[:, :100])
+    assert not torch.equal(a[:, 100:], b[:, 100:])
+
+
+def test_empty_batch_is_a_no_op():
+    import causal_head_attention_gqa_amd as attn
+    torch = __import__("torch")
+    q = torch.zeros((0, 16, 4, 64), dtype=torch.bfloat16, device="cuda")
+    kv = q[:, :, :2].contiguous()
+    out = attn.prefill(q, kv, kv)
+    assert out.shape == q.shape
+
+
+def test_gpt2_small_prefill_full():
+    """B=8, S=1024, 12 heads of 64, bf16, no RoPE: all 6.3M outputs against the oracle."""
+    w = synth.GPT2_PREFILL
+    got, want, _ = _run(w.B, w.S, w.Nh, w.Nkv, w.Dh, w.dtype, w.rope_theta, True, wid=w.wid)
+    assert max_abs(got, want) <= BF16_TOL
+
+
+def test_llama3_prefill_sampled_rows():
+    """B=4, S=8192, 32 query / 8 KV heads of 128, RoPE 5e5: the full launch on the GPU, then
+    sampled (batch, head) pairs and rows (first/last rows, tile edges, random) from the oracle."""
+    import causal_head_attention_gqa_amd as attn
+    w = synth.LLAMA3_PREFILL
+    q, k, v = w.inputs()
+    out = attn.prefill(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), rope_theta=w.rope_theta)
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, 63, 64, 4095, 8190, 8191], rng.integers(0, w.S, 23)]))
+    rows_t = __import__("torch").as_tensor(rows, device=out.device)
+    worst = 0.0
+    for b, h in [(0, 0), (1, 5), (2, 17), (3, 31), (3, 12)]:
+        got = out[b, rows_t, h].float().cpu().numpy()
+        g = h // (w.Nh // w.Nkv)
+        want = oracle.prefill_rows(values(q[b:b + 1, :, h:h + 1], "bf16"), values(k[b:b + 1, :, g:g + 1], "bf16"),
+                                   values(v[b:b + 1, :, g:g + 1], "bf16"), 0, 0, rows, rope_theta=w.rope_theta)
+        worst = max(worst, max_abs(got, want))
+    assert worst <= BF16_TOL
