@@ -43,7 +43,24 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     p.add_argument("--only", choices=["prefill", "decode", "mla"], default=None,
                    help="time a single part (profiling runs); the JSON line then reports that part")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="run only a plain 1 GiB device-to-device copy (calibrates the HBM byte counters)")
     return p.parse_args()
+
+
+def copy_probe(torch, reps=5):
+    """A copy kernel of known size: reads and writes exactly 1 GiB per launch."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "ms_per_copy": dt * 1e3,
+                      "copy_gbs_read_plus_write": 2 * n / dt / 1e9}))
 
 
 # ---------------------------------------------------------------------------------- inputs ----
@@ -82,8 +99,8 @@ def make_inputs(torch, attn):
 
 
 # ----------------------------------------------------------------------------- cpu baseline ----
-def cpu_baseline(prefill_flops_per_s_gpu=None):
-    """Time the fp64 oracle as it stands on a bounded sample of the same workloads."""
+def cpu_baseline():
+    """Time the fp64 oracle as it stands on a bounded sample of the same workloads (~10 s)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -91,44 +108,67 @@ def cpu_baseline(prefill_flops_per_s_gpu=None):
     except Exception:  # noqa: BLE001
         threads = 1
     P, D, M = synth.LLAMA3_PREFILL, synth.LLAMA3_DECODE, synth.MLA_DECODE
-    # prefill: every 16th row of (b=0, h=0) of the Llama-3-8B prefill (512 rows, all of their keys)
-    q = synth.normal(P.wid, 0, (1, P.S, 1, P.Dh), "bf16")
-    k = synth.normal(P.wid, 1, (1, P.S, 1, P.Dh), "bf16")
-    v = synth.normal(P.wid, 2, (1, P.S, 1, P.Dh), "bf16")
-    rows = np.arange(0, P.S, 16)
-    qf, kf, vf = (synth.as_f32(a, "bf16") for a in (q, k, v))
-    t0 = time.perf_counter()
-    oracle.prefill_rows(qf, kf, vf, 0, 0, rows, rope_theta=P.rope_theta)
-    tp = time.perf_counter() - t0
-    p_flops = 4 * P.Dh * int(np.sum(rows + 1))
-    # decode: the first 8 sequences of the GQA decode, the first 2 of the MLA decode
-    ctx = D.ctx_lens()[:8]
-    T = int(ctx.max())
-    dq = synth.as_f32(synth.normal(D.wid, 0, (8, D.Nh, D.Dqk), "bf16"), "bf16")
-    dk = synth.as_f32(synth.normal(D.wid, 1, (8, T, D.Nkv, D.Dqk), "bf16"), "bf16")
-    dv = synth.as_f32(synth.normal(D.wid, 2, (8, T, D.Nkv, D.Dv), "bf16"), "bf16")
-    t0 = time.perf_counter()
-    oracle.decode(dq, dk, dv, ctx)
-    td = time.perf_counter() - t0
-    d_bytes = acc.decode_bytes(ctx, 8, D.Nh, D.Nkv, D.Dqk, D.Dv, 2)
-    mq = synth.as_f32(synth.normal(M.wid, 0, (2, M.Nh, M.Dqk), "bf16"), "bf16")
-    mk = synth.as_f32(synth.normal(M.wid, 1, (2, M.max_ctx, 1, M.Dqk), "bf16"), "bf16").astype(np.float64)
-    mctx = M.ctx_lens()[:2]
-    t0 = time.perf_counter()
-    oracle.decode(mq, mk, mk[..., :M.Dv], mctx, scale=M.scale)
-    tm = time.perf_counter() - t0
-    m_bytes = acc.decode_bytes(mctx, 2, M.Nh, 1, M.Dqk, M.Dv, 2, shared_row=True)
+    # prefill: all 8192 rows of query heads 0-3 of sequence 0 (they share KV head 0)
+    hq = 4
+    q = synth.as_f32(synth.normal(P.wid, 10, (1, P.S, hq, P.Dh), "bf16"), "bf16")
+    k = synth.as_f32(synth.normal(P.wid, 11, (1, P.S, 1, P.Dh), "bf16"), "bf16")
+    v = synth.as_f32(synth.normal(P.wid, 12, (1, P.S, 1, P.Dh), "bf16"), "bf16")
+    rows = np.arange(P.S)
+    tp = 0.0
+    for h in range(hq):
+        t0 = time.perf_counter()
+        oracle.prefill_rows(q[:, :, h:h + 1], k, v, 0, 0, rows, rope_theta=P.rope_theta)
+        tp += time.perf_counter() - t0
+    p_flops = hq * acc.prefill_flops(1, P.S, 1, P.Dh, causal=True)
+    # decode: every sequence of the GQA decode and of the MLA decode, one at a time
+    td, tm = 0.0, 0.0
+    ctx = D.ctx_lens()
+    for b in range(D.B):
+        c = int(ctx[b])
+        dq = synth.as_f32(synth.normal(D.wid, 100 + 3 * b, (1, D.Nh, D.Dqk), "bf16"), "bf16")
+        dk = synth.as_f32(synth.normal(D.wid, 101 + 3 * b, (1, c, D.Nkv, D.Dqk), "bf16"), "bf16")
+        dv = synth.as_f32(synth.normal(D.wid, 102 + 3 * b, (1, c, D.Nkv, D.Dv), "bf16"), "bf16")
+        t0 = time.perf_counter()
+        oracle.decode(dq, dk, dv, np.array([c]))
+        td += time.perf_counter() - t0
+    d_bytes = acc.decode_bytes(ctx, D.B, D.Nh, D.Nkv, D.Dqk, D.Dv, 2)
+    mctx = M.ctx_lens()
+    for b in range(M.B):
+        c = int(mctx[b])
+        mq = synth.as_f32(synth.normal(M.wid, 100 + 2 * b, (1, M.Nh, M.Dqk), "bf16"), "bf16")
+        mk = synth.as_f32(synth.normal(M.wid, 101 + 2 * b, (1, c, 1, M.Dqk), "bf16"), "bf16").astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.decode(mq, mk, mk[..., :M.Dv], np.array([c]), scale=M.scale)
+        tm += time.perf_counter() - t0
+    m_bytes = acc.decode_bytes(mctx, M.B, M.Nh, 1, M.Dqk, M.Dv, 2, shared_row=True)
     p_tflops = p_flops / tp / 1e12
     d_gbs = (d_bytes + m_bytes) / (td + tm) / 1e9
     frac = 0.5 * (p_tflops / acc.PEAK_BF16_TFLOPS + d_gbs / acc.PEAK_HBM_GBS)
     return {
         "value": 100.0 * frac, "unit": "% of peak", "cores": int(threads), "kind": "oracle",
-        "sample": (f"fp64 numpy oracle: prefill rows 0,16,..,8176 of (b=0,h=0) of the Llama-3-8B prefill "
-                   f"({tp:.2f} s, {p_tflops * 1e3:.3f} GFLOP/s algorithmic); GQA decode of 8 sequences "
-                   f"({td:.2f} s) and MLA decode of 2 sequences ({tm:.2f} s): {d_gbs:.3f} GB/s algorithmic; "
-                   f"host {platform.processor() or platform.machine()}, {os.cpu_count()} logical CPUs"),
+        "sample": (f"fp64 numpy oracle on the host: every row of query heads 0-3 of sequence 0 of the Llama-3-8B "
+                   f"prefill ({tp:.1f} s, {p_tflops * 1e3:.2f} GFLOP/s algorithmic); all 64 sequences of the "
+                   f"GQA decode ({td:.1f} s) and all 32 of the MLA decode ({tm:.1f} s): {d_gbs:.3f} GB/s "
+                   f"algorithmic; {threads} BLAS threads; host {platform.machine()}, {os.cpu_count()} logical CPUs"),
         "prefill_tflops": p_tflops, "decode_gbs": d_gbs,
     }
+
+
+def prefill_traffic():
+    """HBM bytes per launch of the prefill kernel from the committed rocprofv3 counter record, or
+    None when the kernel sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "prefill_bf16_llama3_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in rec["source_files"]:
+        h.update((hashlib.sha256(open(os.path.join(ROOT, f), "rb").read()).hexdigest() + "  " + f + "\n").encode())
+    if h.hexdigest() != rec["source_sha256"]:
+        return None
+    return int((rec["fetch_size_kib_per_dispatch"] * rec["fetch_scale"]
+                + rec["write_size_kib_per_dispatch"] * rec["write_scale"]) * 1024)
 
 
 # ------------------------------------------------------------------------------------ main ----
@@ -139,6 +179,9 @@ def main():
                                    "--gpus above 1 is not supported"}))
         sys.exit(2)
     import torch
+    if args.copy_probe:
+        copy_probe(torch)
+        return
     import causal_head_attention_gqa_amd as attn
     P, D, M = synth.LLAMA3_PREFILL, synth.LLAMA3_DECODE, synth.MLA_DECODE
     x = make_inputs(torch, attn)
@@ -205,7 +248,8 @@ def main():
     if "prefill" in ms:
         roofline = {"kernel": "prefill_bf16_kernel (Llama-3-8B GQA prefill, one call incl. RoPE pre-pass)",
                     "bound": "mfma", "achieved": comp["prefill_tflops"], "peak": acc.PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": comp["prefill_tflops"] / acc.PEAK_BF16_TFLOPS, "traffic": None}
+                    "unit": "TFLOP/s", "frac": comp["prefill_tflops"] / acc.PEAK_BF16_TFLOPS,
+                    "traffic": prefill_traffic()}
     else:
         name = args.only
         gbs = comp["gqa_decode_gbs"] if name == "decode" else comp["mla_decode_gbs"]
