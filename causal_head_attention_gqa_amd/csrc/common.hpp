@@ -54,4 +54,26 @@ __device__ __forceinline__ float pair_sum32(float x) {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+
+// 16 bytes per lane straight from global memory into LDS (global_load_lds_dwordx4): lane i's
+// bytes land at lds_base + 16 * i, so one wave instruction fills 1 KiB of LDS. lds_base must be
+// the same for the whole wave.
+__device__ __forceinline__ void load_lds16(const void* gptr, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gptr, (lds_void_t*)lds_base, 16, 0, 0);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16). Within each group of 16 lanes, lanes 4j..4j+3 each
+// address 4 consecutive 16-bit elements of "row" j (16 elements per row); afterwards lane i holds
+// element i of rows 0..3. With a row-major [key][dim] tile this yields 4 consecutive keys of one
+// dim per lane: the k-slots of an MFMA operand whose reduction runs over keys.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
+  return __builtin_bit_cast(uint2, r);
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 }  // namespace attn

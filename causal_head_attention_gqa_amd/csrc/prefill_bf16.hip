@@ -10,14 +10,18 @@
 //   - each wave owns 32 query rows of one head and computes the transposed score block
 //     S^T = K Q^T, so that one lane holds one query's scores: the row max needs a single
 //     lane-pair exchange and the row sum none until the end;
-//   - K/V tiles of 64 keys are loaded with 128-bit coalesced loads into registers one tile
-//     ahead, then stored to a double-buffered LDS tile (V transposed on the way, so that the
-//     P.V contraction reads 4 consecutive keys per 8-byte LDS read);
+//   - K/V tiles of 64 keys go from HBM straight into a double-buffered LDS tile
+//     (global_load_lds_dwordx4, no staging registers); rows are stored as they are in memory
+//     with their 16-byte chunks XOR-swizzled by the row index, so that the K operand reads
+//     (16 B per lane, 32 different rows) and the transposing V reads (ds_read_b64_tr_b16, which
+//     hands each lane 4 consecutive keys of one dim) spread over the LDS banks;
 //   - tiles past the work-group's last query are never visited and 32-key blocks above a wave's
 //     diagonal are skipped ("2.7 Transformer Decoder Block完整解析" §3.3); the element mask is
 //     applied only on blocks that cross the diagonal or the sequence end;
-//   - online softmax over tiles ("Transformer 架构完全深度解析" §十三: running max and sum; the
-//     output accumulator is rescaled by the same factor, and only when some row's max moved).
+//   - online softmax per 32-key block ("Transformer 架构完全深度解析" §十三: running max and sum;
+//     the output accumulator is rescaled by the same factor, and only when some row's max
+//     moved). Both blocks' Q.K products are issued before the first block's exponentials so the
+//     matrix core works while the vector ALUs do the softmax.
 // Grid order puts the work-groups with the most tiles first.
 #include "kernels.hpp"
 
@@ -27,26 +31,20 @@ namespace {
 constexpr int kBC = 64;
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ uint32_t sel_lo(uint32_t x, uint32_t y) { return __byte_perm(x, y, 0x5410); }
-__device__ __forceinline__ uint32_t sel_hi(uint32_t x, uint32_t y) { return __byte_perm(x, y, 0x7632); }
-__device__ __forceinline__ uint32_t dw(const U4& v, int e) { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; }
-
 template <int D, int HPW>
 __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ out, const float2* __restrict__ table, int B, int S, int Nh, int Nkv, float c,
     int causal, int n_ptiles) {
-  constexpr int BP = 32 * (4 / HPW);        // query positions per work-group
-  constexpr int KP = D + 8;                 // K tile row pitch (elements)
-  constexpr int VP = kBC + 4;               // transposed V row pitch (elements)
-  constexpr int OCT = D / 8;                // 16-byte chunks per row
-  constexpr int NKC = kBC * OCT / kThreads; // K chunks per thread
-  constexpr int NVU = (kBC / 4) * OCT;      // V units of 4 keys x 8 dims
-  constexpr int NQ = D / 16;                // MFMA k-steps over the head dim
-  constexpr int NDB = D / 32;               // 32-row blocks of the output's head dim
+  constexpr int BP = 32 * (4 / HPW);  // query positions per work-group
+  constexpr int CH = D / 8;           // 16-byte chunks per row
+  constexpr int RPL = 64 / CH;        // rows per 1 KiB load instruction
+  constexpr int LPW = kBC * CH / 64 / 4;  // load instructions per wave per tile (K and V each)
+  constexpr int NQ = D / 16;          // MFMA k-steps over the head dim
+  constexpr int NDB = D / 32;         // 32-row blocks of the output's head dim
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBC * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VP];
+  __shared__ __attribute__((aligned(1024))) uint16_t Ks[2][kBC * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vs[2][kBC * D];
 
   const int tid = threadIdx.x;
   const int HGn = Nh / HPW;
@@ -77,17 +75,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
         for (int kk = 0; kk < NQ / 2; ++kk) {
           U4& ra = raw[kk];
           U4& rb = raw[kk + NQ / 2];
-          uint32_t na[4], nb[4];
+          uint32_t* pa = &ra.x;
+          uint32_t* pb = &rb.x;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float2 c0 = tb[kk * 16 + 2 * e], c1 = tb[kk * 16 + 2 * e + 1];
-            const float a0 = bf16lo(dw(ra, e)), a1 = bf16hi(dw(ra, e));
-            const float b0 = bf16lo(dw(rb, e)), b1 = bf16hi(dw(rb, e));
-            na[e] = pack_bf16x2(a0 * c0.x - b0 * c0.y, a1 * c1.x - b1 * c1.y);
-            nb[e] = pack_bf16x2(a0 * c0.y + b0 * c0.x, a1 * c1.y + b1 * c1.x);
+            const float a0 = bf16lo(pa[e]), a1 = bf16hi(pa[e]);
+            const float b0 = bf16lo(pb[e]), b1 = bf16hi(pb[e]);
+            pa[e] = pack_bf16x2(a0 * c0.x - b0 * c0.y, a1 * c1.x - b1 * c1.y);
+            pb[e] = pack_bf16x2(a0 * c0.y + b0 * c0.x, a1 * c1.y + b1 * c1.x);
           }
-          ra = U4{na[0], na[1], na[2], na[3]};
-          rb = U4{nb[0], nb[1], nb[2], nb[3]};
         }
       }
     } else {
@@ -108,141 +105,117 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   const uint16_t* kbase = k + ((long long)b * S * Nkv + g) * D;
   const uint16_t* vbase = v + ((long long)b * S * Nkv + g) * D;
 
-  U4 kreg[NKC];
-  U4 vreg[4];
-  auto load_tile = [&](int j) {
+  // Tile j -> LDS buffer: wave w fills 1 KiB slots w*LPW .. w*LPW+LPW-1 of K and of V. Lane i of a
+  // slot writes physical chunk i % CH of row slot*RPL + i / CH, which holds logical chunk
+  // (i % CH) ^ (row % CH). Rows past the sequence end re-read row S-1 (finite data, masked).
+  auto issue_tile = [&](int j, int buf) {
 #pragma unroll
-    for (int r = 0; r < NKC; ++r) {
-      const int ch = tid + kThreads * r;
-      const int key = j * kBC + ch / OCT;
-      kreg[r] = key < S ? ldg16(kbase + key * kv_stride + (ch % OCT) * 8) : U4{0, 0, 0, 0};
-    }
-    if (tid < NVU) {
-      const int kq = tid / OCT, oc = tid % OCT;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = j * kBC + kq * 4 + r;
-        vreg[r] = key < S ? ldg16(vbase + key * kv_stride + oc * 8) : U4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int r = 0; r < NKC; ++r) {
-      const int ch = tid + kThreads * r;
-      *reinterpret_cast<U4*>(&Ks[buf][(ch / OCT) * KP + (ch % OCT) * 8]) = kreg[r];
-    }
-    if (tid < NVU) {
-      const int kq = tid / OCT, oc = tid % OCT;
-      const int unit = kq ^ (oc & 15);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t x0 = dw(vreg[0], e), x1 = dw(vreg[1], e), x2 = dw(vreg[2], e), x3 = dw(vreg[3], e);
-        uint2 lo = make_uint2(sel_lo(x0, x1), sel_lo(x2, x3));
-        uint2 hi = make_uint2(sel_hi(x0, x1), sel_hi(x2, x3));
-        *reinterpret_cast<uint2*>(&Vt[buf][(oc * 8 + 2 * e) * VP + unit * 4]) = lo;
-        *reinterpret_cast<uint2*>(&Vt[buf][(oc * 8 + 2 * e + 1) * VP + unit * 4]) = hi;
-      }
+    for (int r = 0; r < LPW; ++r) {
+      const int slot = w * LPW + r;
+      const int row = slot * RPL + lane / CH;
+      const int chunk = (lane % CH) ^ (row & (CH - 1));
+      const int key = min(j * kBC + row, S - 1);
+      load_lds16(kbase + key * kv_stride + chunk * 8, &Ks[buf][slot * 512]);
+      load_lds16(vbase + key * kv_stride + chunk * 8, &Vs[buf][slot * 512]);
     }
   };
 
   const int last = causal ? min(S, p0 + BP) : S;
   const int n_tiles = (last + kBC - 1) / kBC;
 
-  load_tile(0);
-  store_tile(0);
+  // Per-lane constants of the transposing V read: 16-lane group q covers dims dq*16 .. +15 of a
+  // 32-dim block and keys hh*4 + j (j = row within the group's 4-row read).
+  const int tr_j = (lane & 15) >> 2;
+  const int tr_c = lane & 3;
+  const int tr_dq = (lane >> 4) & 1;
+
+  issue_tile(0, 0);
+  wait_vmem();
   __syncthreads();
 
-  for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < n_tiles) load_tile(j + 1);
+  for (int jt = 0; jt < n_tiles; ++jt) {
+    const int buf = jt & 1;
+    if (jt + 1 < n_tiles) issue_tile(jt + 1, buf ^ 1);
+    const uint16_t* Kt = Ks[buf];
+    const uint16_t* Vt = Vs[buf];
 
-    // ---- S^T = K Q^T for the two 32-key blocks of this tile ----
+    // ---- S^T = K Q^T for both 32-key blocks ----
     f32x16 sacc[2];
     bool active[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int kb0 = j * kBC + kb * 32;
+      const int kb0 = jt * kBC + kb * 32;
       active[kb] = kb0 < S && (!causal || kb0 <= wp0 + 31);
       sacc[kb] = f32x16{};
       if (active[kb]) {
-        const uint16_t* kr = &Ks[buf][(kb * 32 + col) * KP + hh * 8];
+        const int row = kb * 32 + col;
+        const uint16_t* kr = Kt + row * D;
 #pragma unroll
         for (int kk = 0; kk < NQ; ++kk) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kr + kk * 16);
+          const int chunk = (2 * kk + hh) ^ (row & (CH - 1));
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kr + chunk * 8);
           sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], sacc[kb], 0, 0, 0);
         }
       }
     }
 
-    // ---- mask, running max, probabilities ----
-    float mt = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int kb0 = j * kBC + kb * 32;
-      if (active[kb]) {
-        const bool need_mask = (causal && kb0 + 31 > wp0) || (kb0 + 32 > S);
-        if (need_mask) {
+      if (!active[kb]) continue;
+      const int kb0 = jt * kBC + kb * 32;
+      // ---- mask, running max, probabilities for this block ----
+      const bool need_mask = (causal && kb0 + 31 > wp0) || (kb0 + 32 > S);
+      if (need_mask) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kb0 + (i >> 2) * 8 + hh * 4 + (i & 3);
-            if (key >= S || (causal && key > p)) sacc[kb][i] = -INFINITY;
-          }
+        for (int i = 0; i < 16; ++i) {
+          const int key = kb0 + (i >> 2) * 8 + hh * 4 + (i & 3);
+          if (key >= S || (causal && key > p)) sacc[kb][i] = -INFINITY;
         }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[kb][i]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[kb][i] = -INFINITY;
       }
-    }
-    mt = pair_max32(mt);
-    const float m_new = fmaxf(m, mt * c);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m - m_use);
-    m = m_new;
-
-    uint32_t pk[2][2][4];  // [key block][k-step][dword] bf16 probabilities
-    float psum = 0.f;
+      float mt = sacc[kb][0];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int i = 1; i < 16; ++i) mt = fmaxf(mt, sacc[kb][i]);
+      mt = pair_max32(mt);
+      const float m_new = fmaxf(m, mt * c);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fast_exp2(m - m_use);
+      m = m_new;
+      uint32_t pk[2][4];
+      float psum = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
         const float e0 = fast_exp2(fmaf(sacc[kb][i], c, -m_use));
         const float e1 = fast_exp2(fmaf(sacc[kb][i + 1], c, -m_use));
         psum += e0 + e1;
-        pk[kb][i >> 3][(i & 7) >> 1] = pack_bf16x2(e0, e1);
+        pk[i >> 3][(i & 7) >> 1] = pack_bf16x2(e0, e1);
       }
-    }
-    lsum = lsum * alpha + psum;
-    if (__ballot(alpha != 1.f)) {
+      lsum = fmaf(lsum, alpha, psum);
+      if (__ballot(alpha != 1.f)) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-    }
+          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+      }
 
-    // ---- O^T += V^T P^T ----
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (!active[kb]) continue;
+      // ---- O^T += V^T P^T over this block's 32 keys ----
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const bf16x8 bop = __builtin_bit_cast(bf16x8, U4{pk[kb][s][0], pk[kb][s][1], pk[kb][s][2], pk[kb][s][3]});
+        const bf16x8 bop = __builtin_bit_cast(bf16x8, U4{pk[s][0], pk[s][1], pk[s][2], pk[s][3]});
+        const int row0 = kb * 32 + 16 * s + hh * 4 + tr_j;  // keys for k-slots 0..3
+        const int row1 = row0 + 8;                           // keys for k-slots 4..7
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const int dim = db * 32 + col;
-          const int sw = (dim >> 3) & 15;
-          const uint16_t* row = &Vt[buf][dim * VP];
-          const uint2 lo = *reinterpret_cast<const uint2*>(row + ((kb * 8 + 4 * s + hh) ^ sw) * 4);
-          const uint2 hi = *reinterpret_cast<const uint2*>(row + ((kb * 8 + 4 * s + 2 + hh) ^ sw) * 4);
+          const int dchunk = db * 4 + tr_dq * 2 + (tr_c >> 1);
+          const int half = (tr_c & 1) * 4;
+          const uint2 lo = lds_read_tr16(Vt + row0 * D + ((dchunk ^ (row0 & (CH - 1))) * 8) + half);
+          const uint2 hi = lds_read_tr16(Vt + row1 * D + ((dchunk ^ (row1 & (CH - 1))) * 8) + half);
           const bf16x8 aop = __builtin_bit_cast(bf16x8, U4{lo.x, lo.y, hi.x, hi.y});
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop, o[db], 0, 0, 0);
         }
       }
     }
 
-    if (j + 1 < n_tiles) store_tile(buf ^ 1);
+    wait_vmem();
     __syncthreads();
   }
 
