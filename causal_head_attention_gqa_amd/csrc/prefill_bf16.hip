@@ -10,11 +10,11 @@
 //   - each wave owns 32 query rows of one head and computes the transposed score block
 //     S^T = K Q^T, so that one lane holds one query's scores: the row max needs a single
 //     lane-pair exchange and the row sum none until the end;
-//   - K/V tiles of 64 keys go from HBM straight into a double-buffered LDS tile
-//     (global_load_lds_dwordx4, no staging registers); rows are stored as they are in memory
-//     with their 16-byte chunks XOR-swizzled by the row index, so that the K operand reads
-//     (16 B per lane, 32 different rows) and the transposing V reads (ds_read_b64_tr_b16, which
-//     hands each lane 4 consecutive keys of one dim) spread over the LDS banks;
+//   - K/V tiles of 64 keys go from HBM straight into LDS (global_load_lds_dwordx4, no staging
+//     registers), double-buffered in two distinct LDS arrays so the next tile's loads overlap the
+//     current tile's math; rows are stored as in memory with their 16-byte chunks XOR-swizzled by
+//     the row index, so the K operand reads (16 B per lane, 32 rows) and the transposing V reads
+//     (ds_read_b64_tr_b16: 4 consecutive keys of one dim per lane) spread over the LDS banks;
 //   - tiles past the work-group's last query are never visited and 32-key blocks above a wave's
 //     diagonal are skipped ("2.7 Transformer Decoder Block完整解析" §3.3); the element mask is
 //     applied only on blocks that cross the diagonal or the sequence end;
@@ -22,7 +22,8 @@
 //     the output accumulator is rescaled by the same factor, and only when some row's max
 //     moved). Both blocks' Q.K products are issued before the first block's exponentials so the
 //     matrix core works while the vector ALUs do the softmax.
-// Grid order puts the work-groups with the most tiles first.
+// All per-wave control values are scalar (wave-uniform branches); per-lane LDS and global
+// offsets are computed once. Grid order puts the work-groups with the most tiles first.
 #include "kernels.hpp"
 
 namespace attn {
@@ -36,17 +37,21 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ out, const float2* __restrict__ table, int B, int S, int Nh, int Nkv, float c,
     int causal, int n_ptiles) {
-  constexpr int BP = 32 * (4 / HPW);  // query positions per work-group
-  constexpr int CH = D / 8;           // 16-byte chunks per row
-  constexpr int RPL = 64 / CH;        // rows per 1 KiB load instruction
+  constexpr int BP = 32 * (4 / HPW);      // query positions per work-group
+  constexpr int CH = D / 8;               // 16-byte chunks per row
+  constexpr int RPL = 64 / CH;            // rows per 1 KiB load instruction
   constexpr int LPW = kBC * CH / 64 / 4;  // load instructions per wave per tile (K and V each)
-  constexpr int NQ = D / 16;          // MFMA k-steps over the head dim
-  constexpr int NDB = D / 32;         // 32-row blocks of the output's head dim
+  constexpr int NQ = D / 16;              // MFMA k-steps over the head dim
+  constexpr int NDB = D / 32;             // 32-row blocks of the output's head dim
 
-  __shared__ __attribute__((aligned(1024))) uint16_t Ks[2][kBC * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t Vs[2][kBC * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Ks0[kBC * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vs0[kBC * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Ks1[kBC * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vs1[kBC * D];
 
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int HGn = Nh / HPW;
   const int id = blockIdx.x;
   const int bh = id % (B * HGn);
@@ -55,11 +60,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   const int h0 = (bh % HGn) * HPW;
   const int g = h0 / (Nh / Nkv);
   const int p0 = pt * BP;
-  const int w = tid >> 6, lane = tid & 63;
   const int h = h0 + (w % HPW);
-  const int wp0 = p0 + (w / HPW) * 32;
+  const int wp0 = p0 + (w / HPW) * 32;  // wave's first query position (scalar)
   const int col = lane & 31, hh = lane >> 5;
-  const int p = wp0 + col;  // this lane's query position
+  const int p = wp0 + col;               // this lane's query position
 
   // ---- Q^T operand in registers (RoPE applied here when a table is given) ----
   bf16x8 qreg[NQ];
@@ -73,10 +77,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
         const float2* tb = table + (long long)p * (D / 2) + hh * 8;
 #pragma unroll
         for (int kk = 0; kk < NQ / 2; ++kk) {
-          U4& ra = raw[kk];
-          U4& rb = raw[kk + NQ / 2];
-          uint32_t* pa = &ra.x;
-          uint32_t* pb = &rb.x;
+          uint32_t* pa = &raw[kk].x;
+          uint32_t* pb = &raw[kk + NQ / 2].x;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float2 c0 = tb[kk * 16 + 2 * e], c1 = tb[kk * 16 + 2 * e + 1];
@@ -101,80 +103,100 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   float m = -INFINITY;  // running max of scale*log2(e)*score for this lane's query
   float lsum = 0.f;     // running sum over the keys this lane holds
 
+  // ---- per-lane global source offsets of the tile loads (row r of a tile, swizzled chunk) ----
   const long long kv_stride = (long long)Nkv * D;
   const uint16_t* kbase = k + ((long long)b * S * Nkv + g) * D;
   const uint16_t* vbase = v + ((long long)b * S * Nkv + g) * D;
-
-  // Tile j -> LDS buffer: wave w fills 1 KiB slots w*LPW .. w*LPW+LPW-1 of K and of V. Lane i of a
-  // slot writes physical chunk i % CH of row slot*RPL + i / CH, which holds logical chunk
-  // (i % CH) ^ (row % CH). Rows past the sequence end re-read row S-1 (finite data, masked).
-  auto issue_tile = [&](int j, int buf) {
+  int lrow[LPW];
+  long long loff[LPW];
 #pragma unroll
-    for (int r = 0; r < LPW; ++r) {
-      const int slot = w * LPW + r;
-      const int row = slot * RPL + lane / CH;
-      const int chunk = (lane % CH) ^ (row & (CH - 1));
-      const int key = min(j * kBC + row, S - 1);
-      load_lds16(kbase + key * kv_stride + chunk * 8, &Ks[buf][slot * 512]);
-      load_lds16(vbase + key * kv_stride + chunk * 8, &Vs[buf][slot * 512]);
+  for (int r = 0; r < LPW; ++r) {
+    lrow[r] = (w * LPW + r) * RPL + lane / CH;
+    loff[r] = (long long)lrow[r] * kv_stride + ((lane % CH) ^ (lrow[r] & (CH - 1))) * 8;
+  }
+  const long long tile_step = kBC * kv_stride;
+
+  // ---- per-lane LDS read offsets (elements), identical for every tile ----
+  // K operand: row kb*32 + col, logical chunk 2*kk + hh; (row & (CH-1)) == (col & (CH-1)) for kb*32.
+  int koff[NQ];
+#pragma unroll
+  for (int kk = 0; kk < NQ; ++kk) koff[kk] = col * D + (((2 * kk + hh) ^ (col & (CH - 1))) * 8);
+  // V operand (transposing read): rows kb*32 + 16s + 8t + hh*4 + j, dims db*32 + dq*16 + 4c.
+  const int tr_j = (lane & 15) >> 2, tr_c = lane & 3, tr_dq = (lane >> 4) & 1;
+  int voff[2][NDB];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int row = 8 * t + hh * 4 + tr_j;  // low 4 bits of the key row
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int chunk = db * 4 + tr_dq * 2 + (tr_c >> 1);
+      voff[t][db] = row * D + ((chunk ^ (row & (CH - 1))) * 8) + (tr_c & 1) * 4;
     }
-  };
+  }
 
   const int last = causal ? min(S, p0 + BP) : S;
   const int n_tiles = (last + kBC - 1) / kBC;
 
-  // Per-lane constants of the transposing V read: 16-lane group q covers dims dq*16 .. +15 of a
-  // 32-dim block and keys hh*4 + j (j = row within the group's 4-row read).
-  const int tr_j = (lane & 15) >> 2;
-  const int tr_c = lane & 3;
-  const int tr_dq = (lane >> 4) & 1;
-
-  issue_tile(0, 0);
-  wait_vmem();
-  __syncthreads();
-
-  for (int jt = 0; jt < n_tiles; ++jt) {
-    const int buf = jt & 1;
-    if (jt + 1 < n_tiles) issue_tile(jt + 1, buf ^ 1);
-    const uint16_t* Kt = Ks[buf];
-    const uint16_t* Vt = Vs[buf];
-
-    // ---- S^T = K Q^T for both 32-key blocks ----
-    f32x16 sacc[2];
-    bool active[2];
+  auto issue_tile = [&](int jt, uint16_t* kdst, uint16_t* vdst) {
+    const long long tbase = (long long)jt * tile_step;
+    if (jt * kBC + kBC <= S) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int kb0 = jt * kBC + kb * 32;
-      active[kb] = kb0 < S && (!causal || kb0 <= wp0 + 31);
-      sacc[kb] = f32x16{};
-      if (active[kb]) {
-        const int row = kb * 32 + col;
-        const uint16_t* kr = Kt + row * D;
-#pragma unroll
-        for (int kk = 0; kk < NQ; ++kk) {
-          const int chunk = (2 * kk + hh) ^ (row & (CH - 1));
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kr + chunk * 8);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kk], sacc[kb], 0, 0, 0);
-        }
+      for (int r = 0; r < LPW; ++r) {
+        const int slot = w * LPW + r;
+        load_lds16(kbase + tbase + loff[r], kdst + slot * 512);
+        load_lds16(vbase + tbase + loff[r], vdst + slot * 512);
       }
+    } else {  // last, partial tile: rows past the end re-read row S-1 (finite data, masked)
+#pragma unroll
+      for (int r = 0; r < LPW; ++r) {
+        const int slot = w * LPW + r;
+        const int key = min(jt * kBC + lrow[r], S - 1);
+        const long long off = (long long)key * kv_stride + ((lane % CH) ^ (lrow[r] & (CH - 1))) * 8;
+        load_lds16(kbase + off, kdst + slot * 512);
+        load_lds16(vbase + off, vdst + slot * 512);
+      }
+    }
+  };
+
+  auto compute_tile = [&](int jt, const uint16_t* Kt, const uint16_t* Vt) {
+    const int key0 = jt * kBC;
+    // blocks of 32 keys: active unless past the sequence or entirely above this wave's diagonal
+    const bool act0 = !causal || key0 <= wp0 + 31;
+    const bool act1 = key0 + 32 < S && (!causal || key0 + 32 <= wp0 + 31);
+    f32x16 sacc[2];
+    if (act0) {
+      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(Kt + koff[0]), qreg[0],
+                                                         f32x16{}, 0, 0, 0);
+#pragma unroll
+      for (int kk = 1; kk < NQ; ++kk)
+        sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(Kt + koff[kk]),
+                                                           qreg[kk], sacc[0], 0, 0, 0);
+    }
+    if (act1) {
+      const uint16_t* K1 = Kt + 32 * D;
+      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(K1 + koff[0]), qreg[0],
+                                                         f32x16{}, 0, 0, 0);
+#pragma unroll
+      for (int kk = 1; kk < NQ; ++kk)
+        sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(K1 + koff[kk]),
+                                                           qreg[kk], sacc[1], 0, 0, 0);
     }
 
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      if (!active[kb]) continue;
-      const int kb0 = jt * kBC + kb * 32;
-      // ---- mask, running max, probabilities for this block ----
-      const bool need_mask = (causal && kb0 + 31 > wp0) || (kb0 + 32 > S);
-      if (need_mask) {
+      if (!(kb == 0 ? act0 : act1)) continue;
+      const int kb0 = key0 + kb * 32;
+      f32x16 sv = sacc[kb];
+      // ---- mask (only on blocks crossing the diagonal or the sequence end) ----
+      if ((causal && kb0 + 31 > wp0) || kb0 + 32 > S) {
+        const int lim = (causal ? min(p, S - 1) : S - 1) - kb0 - hh * 4;  // keys with offset > lim are out
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kb0 + (i >> 2) * 8 + hh * 4 + (i & 3);
-          if (key >= S || (causal && key > p)) sacc[kb][i] = -INFINITY;
-        }
+        for (int i = 0; i < 16; ++i)
+          if ((i >> 2) * 8 + (i & 3) > lim) sv[i] = -INFINITY;
       }
-      float mt = sacc[kb][0];
+      float mt = sv[0];
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mt = fmaxf(mt, sacc[kb][i]);
+      for (int i = 1; i < 16; ++i) mt = fmaxf(mt, sv[i]);
       mt = pair_max32(mt);
       const float m_new = fmaxf(m, mt * c);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
@@ -184,8 +206,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
       float psum = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
-        const float e0 = fast_exp2(fmaf(sacc[kb][i], c, -m_use));
-        const float e1 = fast_exp2(fmaf(sacc[kb][i + 1], c, -m_use));
+        const float e0 = fast_exp2(fmaf(sv[i], c, -m_use));
+        const float e1 = fast_exp2(fmaf(sv[i + 1], c, -m_use));
         psum += e0 + e1;
         pk[i >> 3][(i & 7) >> 1] = pack_bf16x2(e0, e1);
       }
@@ -201,20 +223,29 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const bf16x8 bop = __builtin_bit_cast(bf16x8, U4{pk[s][0], pk[s][1], pk[s][2], pk[s][3]});
-        const int row0 = kb * 32 + 16 * s + hh * 4 + tr_j;  // keys for k-slots 0..3
-        const int row1 = row0 + 8;                           // keys for k-slots 4..7
+        const uint16_t* Vb = Vt + (kb * 32 + 16 * s) * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const int dchunk = db * 4 + tr_dq * 2 + (tr_c >> 1);
-          const int half = (tr_c & 1) * 4;
-          const uint2 lo = lds_read_tr16(Vt + row0 * D + ((dchunk ^ (row0 & (CH - 1))) * 8) + half);
-          const uint2 hi = lds_read_tr16(Vt + row1 * D + ((dchunk ^ (row1 & (CH - 1))) * 8) + half);
+          const uint2 lo = lds_read_tr16(Vb + voff[0][db]);
+          const uint2 hi = lds_read_tr16(Vb + voff[1][db]);
           const bf16x8 aop = __builtin_bit_cast(bf16x8, U4{lo.x, lo.y, hi.x, hi.y});
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop, o[db], 0, 0, 0);
         }
       }
     }
+  };
 
+  issue_tile(0, Ks0, Vs0);
+  wait_vmem();
+  __syncthreads();
+  for (int jt = 0; jt < n_tiles; jt += 2) {
+    if (jt + 1 < n_tiles) issue_tile(jt + 1, Ks1, Vs1);
+    compute_tile(jt, Ks0, Vs0);
+    wait_vmem();
+    __syncthreads();
+    if (jt + 1 >= n_tiles) break;
+    if (jt + 2 < n_tiles) issue_tile(jt + 2, Ks0, Vs0);
+    compute_tile(jt + 1, Ks1, Vs1);
     wait_vmem();
     __syncthreads();
   }
