@@ -13,8 +13,9 @@
 //   - K/V tiles of 64 keys go from HBM straight into LDS (global_load_lds_dwordx4, no staging
 //     registers), double-buffered in two distinct LDS arrays so the next tile's loads overlap the
 //     current tile's math; rows are stored as in memory with their 16-byte chunks XOR-swizzled by
-//     the row index, so the K operand reads (16 B per lane, 32 rows) and the transposing V reads
-//     (ds_read_b64_tr_b16: 4 consecutive keys of one dim per lane) spread over the LDS banks;
+//     a permutation of the row index, so the K operand reads (16 B per lane, 32 rows) and the
+//     transposing V reads (ds_read_b64_tr_b16: 4 consecutive keys of one dim per lane) spread
+//     over the LDS banks;
 //   - tiles past the work-group's last query are never visited and 32-key blocks above a wave's
 //     diagonal are skipped ("2.7 Transformer Decoder Block完整解析" §3.3); the element mask is
 //     applied only on blocks that cross the diagonal or the sequence end;
@@ -31,6 +32,16 @@ namespace attn {
 namespace {
 constexpr int kBC = 64;
 constexpr int kThreads = 256;
+
+// Physical 16-byte chunk of logical chunk c in tile row `row` (CH chunks per row). The XOR key
+// permutes the row's low bits (b3 b2 b1 b0 -> b3 b1 b0 b2), a bijection on 8 and on 16
+// consecutive rows (K operand reads: 16 B from each of 8-16 consecutive rows) that also sends the
+// 4 consecutive rows of one transposing V read to 4 different 32-byte bank groups.
+template <int CH>
+__device__ __forceinline__ int swz(int c, int row) {
+  const int key = ((row & 3) << 1) | ((row >> 2) & 1) | (CH == 16 ? (row & 8) : 0);
+  return c ^ key;
+}
 
 template <int D, int HPW>
 __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
@@ -112,15 +123,15 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
 #pragma unroll
   for (int r = 0; r < LPW; ++r) {
     lrow[r] = (w * LPW + r) * RPL + lane / CH;
-    loff[r] = (long long)lrow[r] * kv_stride + ((lane % CH) ^ (lrow[r] & (CH - 1))) * 8;
+    loff[r] = (long long)lrow[r] * kv_stride + swz<CH>(lane % CH, lrow[r]) * 8;
   }
   const long long tile_step = kBC * kv_stride;
 
   // ---- per-lane LDS read offsets (elements), identical for every tile ----
-  // K operand: row kb*32 + col, logical chunk 2*kk + hh; (row & (CH-1)) == (col & (CH-1)) for kb*32.
+  // K operand: row kb*32 + col, logical chunk 2*kk + hh; the swizzle only sees the row's low 4 bits.
   int koff[NQ];
 #pragma unroll
-  for (int kk = 0; kk < NQ; ++kk) koff[kk] = col * D + (((2 * kk + hh) ^ (col & (CH - 1))) * 8);
+  for (int kk = 0; kk < NQ; ++kk) koff[kk] = col * D + swz<CH>(2 * kk + hh, col) * 8;
   // V operand (transposing read): rows kb*32 + 16s + 8t + hh*4 + j, dims db*32 + dq*16 + 4c.
   const int tr_j = (lane & 15) >> 2, tr_c = lane & 3, tr_dq = (lane >> 4) & 1;
   int voff[2][NDB];
@@ -130,7 +141,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const int chunk = db * 4 + tr_dq * 2 + (tr_c >> 1);
-      voff[t][db] = row * D + ((chunk ^ (row & (CH - 1))) * 8) + (tr_c & 1) * 4;
+      voff[t][db] = row * D + swz<CH>(chunk, row) * 8 + (tr_c & 1) * 4;
     }
   }
 
@@ -151,7 +162,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
       for (int r = 0; r < LPW; ++r) {
         const int slot = w * LPW + r;
         const int key = min(jt * kBC + lrow[r], S - 1);
-        const long long off = (long long)key * kv_stride + ((lane % CH) ^ (lrow[r] & (CH - 1))) * 8;
+        const long long off = (long long)key * kv_stride + swz<CH>(lane % CH, lrow[r]) * 8;
         load_lds16(kbase + off, kdst + slot * 512);
         load_lds16(vbase + off, vdst + slot * 512);
       }
