@@ -4,7 +4,7 @@
 #include <cstdint>
 #include <cstring>
 
-#include "../../include/attn.h"
+#include "attn.h"
 #include "kernels.hpp"
 
 using namespace attn;

@@ -118,12 +118,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   const long long kv_stride = (long long)Nkv * D;
   const uint16_t* kbase = k + ((long long)b * S * Nkv + g) * D;
   const uint16_t* vbase = v + ((long long)b * S * Nkv + g) * D;
-  int lrow[LPW];
-  long long loff[LPW];
+  // (offsets within one 64-row tile stay far below 2^31 elements)
+  int loff[LPW];
 #pragma unroll
   for (int r = 0; r < LPW; ++r) {
-    lrow[r] = (w * LPW + r) * RPL + lane / CH;
-    loff[r] = (long long)lrow[r] * kv_stride + swz<CH>(lane % CH, lrow[r]) * 8;
+    const int row = (w * LPW + r) * RPL + lane / CH;
+    loff[r] = row * (int)kv_stride + swz<CH>(lane % CH, row) * 8;
   }
   const long long tile_step = kBC * kv_stride;
 
@@ -133,17 +133,23 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
 #pragma unroll
   for (int kk = 0; kk < NQ; ++kk) koff[kk] = col * D + swz<CH>(2 * kk + hh, col) * 8;
   // V operand (transposing read): rows kb*32 + 16s + 8t + hh*4 + j, dims db*32 + dq*16 + 4c.
+  // With row = hh*4 + j (< 8) the swizzle key has bit 3 clear, so the physical chunk of
+  // db*4 + x is ((db ^ key>>2) * 4) + (x ^ (key & 3)): only db's parity interacts with the lane,
+  // and adding 8 rows (t = 1) flips chunk bit 3, a +-8-chunk shift fixed by db >> 1. Two
+  // registers (even / odd db) plus compile-time immediates give every read's address.
   const int tr_j = (lane & 15) >> 2, tr_c = lane & 3, tr_dq = (lane >> 4) & 1;
-  int voff[2][NDB];
+  int voff_par[2];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int row = 8 * t + hh * 4 + tr_j;  // low 4 bits of the key row
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int chunk = db * 4 + tr_dq * 2 + (tr_c >> 1);
-      voff[t][db] = row * D + swz<CH>(chunk, row) * 8 + (tr_c & 1) * 4;
-    }
+  for (int par = 0; par < 2; ++par) {
+    const int row = hh * 4 + tr_j;
+    voff_par[par] = row * D + swz<CH>(par * 4 + tr_dq * 2 + (tr_c >> 1), row) * 8 + (tr_c & 1) * 4;
   }
+  // element offset of the read for (t, db): voff_par[db & 1] + vimm(t, db)
+  auto vimm = [](int t, int db) {
+    const int dbase = (db & ~1) * 32;  // chunk (db & ~1)*4 -> element offset, unchanged by keys < 8
+    const int tshift = CH == 16 ? (((db >> 1) & 1) ? -64 : 64) : 0;  // chunk bit 3 flip for rows + 8
+    return dbase + t * (8 * D + tshift);
+  };
 
   const int last = causal ? min(S, p0 + BP) : S;
   const int n_tiles = (last + kBC - 1) / kBC;
@@ -161,8 +167,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < LPW; ++r) {
         const int slot = w * LPW + r;
-        const int key = min(jt * kBC + lrow[r], S - 1);
-        const long long off = (long long)key * kv_stride + swz<CH>(lane % CH, lrow[r]) * 8;
+        const int row = slot * RPL + lane / CH;
+        const int key = min(jt * kBC + row, S - 1);
+        const long long off = (long long)key * kv_stride + swz<CH>(lane % CH, row) * 8;
         load_lds16(kbase + off, kdst + slot * 512);
         load_lds16(vbase + off, vdst + slot * 512);
       }
@@ -237,8 +244,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
         const uint16_t* Vb = Vt + (kb * 32 + 16 * s) * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const uint2 lo = lds_read_tr16(Vb + voff[0][db]);
-          const uint2 hi = lds_read_tr16(Vb + voff[1][db]);
+          const uint2 lo = lds_read_tr16(Vb + voff_par[db & 1] + vimm(0, db));
+          const uint2 hi = lds_read_tr16(Vb + voff_par[db & 1] + vimm(1, db));
           const bf16x8 aop = __builtin_bit_cast(bf16x8, U4{lo.x, lo.y, hi.x, hi.y});
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop, o[db], 0, 0, 0);
         }
