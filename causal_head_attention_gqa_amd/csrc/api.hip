@@ -30,15 +30,14 @@ struct DecodePlan {
 
 bool is_mla_shape(int Nkv, int Dqk, int Dv) { return Dqk == 576 && Dv == 512 && Nkv == 1; }
 
-int heads_per_group(int G) { return G % 8 == 0 ? 8 : G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1; }
-
 DecodePlan decode_plan(int B, int Nh, int Nkv, int Dqk, int Dv, int max_ctx) {
   DecodePlan p;
   p.mla = is_mla_shape(Nkv, Dqk, Dv);
   if (max_ctx <= 0 || B <= 0) return p;
   if (p.mla) {
-    const int nw = Nh % 64 == 0 ? 4 : Nh % 32 == 0 ? 2 : 1;
-    const long long groups = (long long)B * (Nh / (16 * nw));
+    // one 8/4/2/1-wave work-group per (sequence, 16*waves heads, chunk); its 108 KiB LDS ring
+    // allows one per CU, so aim for about 256 work-groups
+    const long long groups = (long long)B * (Nh / (16 * mla_waves_per_group(Nh)));
     const int tiles = (max_ctx + 31) / 32;
     long long want = (256 + groups - 1) / groups;  // about one work-group per CU
     if (want > tiles) want = tiles;
@@ -46,7 +45,10 @@ DecodePlan decode_plan(int B, int Nh, int Nkv, int Dqk, int Dv, int max_ctx) {
     const int per = (int)((max_ctx + want - 1) / want);
     p.chunk = (per + 31) / 32 * 32;
   } else {
-    const long long groups = (long long)B * (Nh / heads_per_group(Nh / Nkv));
+    // work-groups of (sequence, KV head, up to 16 query heads, chunk); 512-token chunks unless
+    // that leaves fewer than ~1024 work-groups
+    const int G = Nh / Nkv;
+    const long long groups = (long long)B * Nkv * (G < 16 ? 1 : G / 16);
     p.chunk = 512;
     while (p.chunk > 64 && groups * ((max_ctx + p.chunk - 1) / p.chunk) < 1024) p.chunk /= 2;
   }
@@ -167,6 +169,7 @@ int attn_decode(const void* q, const void* kcache, const void* vcache, const int
     if (rope_theta > 0.f) return ATTN_ERR_UNSUPPORTED;
   } else {
     if (Dqk != Dv || (Dqk != 64 && Dqk != 128)) return ATTN_ERR_UNSUPPORTED;
+    if (Nh / Nkv > 16 && (Nh / Nkv) % 16 != 0) return ATTN_ERR_UNSUPPORTED;  // heads go in groups of 16
   }
   if (B == 0) return ATTN_OK;
   if (!q || !kcache || !vcache || !ctx_lens || !out) return ATTN_ERR_INVALID;
@@ -203,6 +206,7 @@ int attn_decode(const void* q, const void* kcache, const void* vcache, const int
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = mla ? launch_decode_mla(a, st) : launch_decode_gqa(a, st);
   if (e != hipSuccess) return hip_status(e);
+  if (mla && p.nsplit == 1) return ATTN_OK;  // a single chunk already wrote the output
   return hip_status(launch_decode_reduce(a, st));
 }
 

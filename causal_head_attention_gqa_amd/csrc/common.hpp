@@ -76,4 +76,29 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// The same 16-byte direct-to-LDS load issued as inline assembly. The compiler then neither knows
+// that LDS is written nor waits for it: the caller owns every vmcnt wait for these loads (with
+// vmcnt(N) it can keep the newest N loads in flight, e.g. a ring of LDS stages). The LDS base of
+// the wave (byte address) goes through M0.
+__device__ __forceinline__ void load_lds16_async(const void* gptr, const void* lds_base) {
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(lds_addr) : "memory");
+}
+
+// Work-group barrier without the memory fences of __syncthreads(): for tiles filled by
+// load_lds16_async after an explicit vmcnt wait, where the fence's wait for every outstanding
+// load (including later stages still in flight) is not wanted.
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
+// vmcnt(0) as a real s_waitcnt the compiler's wait tracking sees (gfx9 encoding: expcnt and
+// lgkmcnt fields at their maximum): use it to retire ordinary loads before async LDS loads start,
+// so no lazily placed wait for them lands inside a loop and drains the async loads too.
+__device__ __forceinline__ void retire_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 }  // namespace attn

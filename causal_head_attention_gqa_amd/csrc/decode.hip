@@ -5,13 +5,14 @@
 // cached keys 0 .. ctx_b-1 of KV head h / (Nh/Nkv) with no mask ("Transformer 架构完全深度解析"
 // §九: the new K/V are appended first; "Transformer 架构快速入门" §13.2).
 //
-// Decode streams the cache once and does ~4 FLOP per byte, so it is bound by HBM bandwidth:
-//   - a work-group owns (b, a group of up to 8 query heads sharing one KV head, one context
-//     chunk); every cached row is read by exactly one work-group, with 128-bit loads by 16
-//     lanes per 256-byte row, several rows in flight per lane;
-//   - pass 1 streams K and forms q.k with bf16 dot2 instructions (exact bf16 products) and a
-//     16-lane DPP reduction; pass 2 takes the chunk's max and exp2 once per score (no running
-//     rescale inside a chunk); pass 3 streams V and accumulates p.v;
+// Decode streams the cache once at ~4 FLOP per byte, so it is bound by HBM bandwidth. The design
+// keeps many bytes in flight and the vector ALUs nearly idle:
+//   - a work-group owns (b, one KV head, up to 16 of its query heads, one context chunk): every
+//     cached row is fetched once, shared by the query heads of its group in registers;
+//   - each of the 4 waves streams its own 16-token stages through a private LDS ring with
+//     direct-to-LDS loads (several stages in flight per wave, no barrier while streaming);
+//   - the tiny contractions run on the matrix cores with the heads padded to 16 (q.k as
+//     16x16x32, p.v as 16x16x16 whose p operand is the score block's own register layout);
 //   - each chunk writes (max, sum, unnormalised output) in fp32; the reduction kernel merges
 //     the chunks with the online-softmax algebra ("Transformer 架构完全深度解析" §十三: the
 //     running max / sum recurrences, applied to whole chunks).
@@ -21,221 +22,225 @@ namespace attn {
 
 namespace {
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 
-// Sum over the 16 lanes of a DPP row; every lane of the row receives the total.
-__device__ __forceinline__ float row16_sum(float x) {
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));   // quad xor 1
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));   // quad xor 2
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));  // half-row mirror
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false));  // row mirror
-  return x;
+// XOR key of the 16-byte chunk index in stage row `row` (CH chunks per row): a permutation of the
+// row's low bits, distinct over 16 consecutive rows (K operand reads) and sending the 4 rows of
+// one transposing V read to 4 different 32-byte bank groups.
+template <int CH>
+__device__ __forceinline__ int dkey(int row) {
+  return ((row & 3) << 1) | ((row >> 2) & 1) | (CH == 16 ? (row & 8) : 0);
 }
 
-// Pairwise sums over rows (0,1),(2,3) then lanes (l, l^32): the whole-wave sum of the four rows.
-__device__ __forceinline__ float rows_sum(float x) {
+// Max / sum over the four 16-lane rows that hold one head's tokens.
+__device__ __forceinline__ float rows_max4(float x) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  return pair_sum32(x);
+  return pair_max32(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-
-template <int DPL>
-struct Vec;  // DPL bf16 elements = DPL/2 dwords
-template <>
-struct Vec<8> {
-  uint32_t d[4];
-  __device__ __forceinline__ void load(const uint16_t* p) {
-    const U4 v = ldg16(p);
-    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
-  }
-};
-template <>
-struct Vec<4> {
-  uint32_t d[2];
-  __device__ __forceinline__ void load(const uint16_t* p) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
-    d[0] = v.x; d[1] = v.y;
-  }
-};
-
-template <int D, int HG>
+// One work-group = 4 waves for (sequence b, KV head g, up to 16 of its query heads, one chunk).
+// Each wave streams its own 16-token stages (stage k of the chunk goes to wave k % 4) through a
+// private NB-deep LDS ring filled by direct-to-LDS loads, so no barrier is needed while streaming:
+//   S^T[16 tokens x 16 heads] = K Q^T   (v_mfma_f32_16x16x32_bf16, query heads padded to 16)
+//   online softmax per head (running max and sum, output rescaled only when some max moved)
+//   O^T[D x 16 heads] += V^T P^T        (v_mfma_f32_16x16x16bf16_1k; P^T is the score block's
+//                                        own register layout, V^T comes from the transposing read)
+// The four waves' (max, sum, output) are merged in LDS and written as the chunk's partial.
+template <int D, int NB>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
-  constexpr int DPL = D / 16;  // dims per lane: one row per 16 lanes
-  constexpr int NDW = DPL / 2;
-  extern __shared__ float smem[];
-  float* sc = smem;  // [chunk][HG] scores, then probabilities
-  __shared__ float red[4][HG][D];
-  __shared__ float mls[HG][2];
+  constexpr int CH = D / 8;          // 16-byte chunks per row
+  constexpr int ROWS = 16;           // tokens per stage
+  constexpr int SE = ROWS * D;       // elements per stage and operand
+  constexpr int LPS = SE * 2 / 1024; // 1 KiB load instructions per stage and operand
+  constexpr int NKK = D / 32;        // Q.K k-steps
+  constexpr int NDB = D / 16;        // output dim blocks
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[4][NB][2][SE];
+  static_assert(NB * 2 * SE * 2 >= (16 * (D + 4) + 32) * 4, "merge area must fit in a wave's ring");
 
   const int tid = threadIdx.x;
-  const int n_hg = a.Nh / HG;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = a.Nh / a.Nkv;
+  const int HG = G < 16 ? G : 16;
+  const int n_hg = G / HG;  // head groups per KV head
   const int s = blockIdx.x % a.nsplit;
-  const int hgrp = (blockIdx.x / a.nsplit) % n_hg;
-  const int b = blockIdx.x / (a.nsplit * n_hg);
+  const int rest = blockIdx.x / a.nsplit;
+  const int hgi = rest % (a.Nkv * n_hg);
+  const int b = rest / (a.Nkv * n_hg);
+  const int g = hgi / n_hg;
+  const int h0 = g * G + (hgi % n_hg) * HG;
   const int ctx = min(max(a.ctx_lens[b], 0), a.max_ctx);
   const int t0 = s * a.chunk;
   if (t0 >= ctx) return;  // empty split: the reduction ignores it
   const int t1 = min(ctx, t0 + a.chunk);
-  const int n = t1 - t0;
-  const int h0 = hgrp * HG;
-  const int g = h0 / (a.Nh / a.Nkv);
-  const int lg = tid >> 4, li = tid & 15;
-  const int w = tid >> 6, lane = tid & 63;
+  const int hc = lane & 15, rg = lane >> 4;
+  const bool real = hc < HG;
 
-  // ---- query (optionally rotated at position ctx-1), kept as bf16 pairs for dot2 ----
-  uint32_t qv[HG][NDW];
+  // ---- Q^T operand (head column hc, dims kk*32 + rg*8 .. +7), rotated at ctx-1 if asked ----
+  bf16x8 qreg[NKK];
+  {
+    U4 raw[NKK];
+    const uint16_t* qp = a.q + ((long long)b * a.Nh + h0 + (real ? hc : 0)) * D + rg * 8;
 #pragma unroll
-  for (int hl = 0; hl < HG; ++hl) {
-    const uint16_t* qp = a.q + ((long long)b * a.Nh + h0 + hl) * D;
-    Vec<DPL> mine;
-    mine.load(qp + li * DPL);
-    if (a.rope_theta > 0) {
-      const bool first = li * DPL < D / 2;
-      Vec<DPL> other;
-      other.load(qp + (first ? li * DPL + D / 2 : li * DPL - D / 2));
+    for (int kk = 0; kk < NKK; ++kk) raw[kk] = real ? ldg16(qp + kk * 32) : U4{0, 0, 0, 0};
+    if (a.rope_theta > 0 && real) {
       const double k2 = -2.0 * log2(a.rope_theta) / (double)D;
 #pragma unroll
-      for (int e = 0; e < NDW; ++e) {
-        float r[2];
+      for (int kk = 0; kk < NKK / 2; ++kk) {
+        uint32_t* pa = &raw[kk].x;
+        uint32_t* pb = &raw[kk + NKK / 2].x;
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int dim = li * DPL + 2 * e + hf;
-          const int i = first ? dim : dim - D / 2;
-          double sn, cs;
-          sincos((double)(ctx - 1) * exp2(k2 * (double)i), &sn, &cs);
-          const double x = hf ? bf16hi(mine.d[e]) : bf16lo(mine.d[e]);
-          const double y = hf ? bf16hi(other.d[e]) : bf16lo(other.d[e]);
-          r[hf] = first ? (float)(x * cs - y * sn) : (float)(y * sn + x * cs);
-        }
-        qv[hl][e] = pack_bf16x2(r[0], r[1]);
-      }
-    } else {
+        for (int e = 0; e < 4; ++e) {
+          float ra[2], rb[2];
 #pragma unroll
-      for (int e = 0; e < NDW; ++e) qv[hl][e] = mine.d[e];
-    }
-  }
-
-  const long long row_k = (long long)a.Nkv * a.ldk;
-  const long long row_v = (long long)a.Nkv * a.ldv;
-  const uint16_t* kb = a.kc + ((long long)b * a.max_ctx * a.Nkv + g) * a.ldk + li * DPL;
-  const uint16_t* vb = a.vc + ((long long)b * a.max_ctx * a.Nkv + g) * a.ldv + li * DPL;
-
-  // ---- pass 1: scores x = scale*log2(e) * q.k ----
-  for (int base = t0 + lg; base < t1; base += 16 * kUnroll) {
-    Vec<DPL> kr[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int t = base + 16 * u;
-      if (t < t1) kr[u].load(kb + t * row_k);
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int t = base + 16 * u;
-      if (t < t1) {
-#pragma unroll
-        for (int hl = 0; hl < HG; ++hl) {
-          float acc = 0.f;
-#pragma unroll
-          for (int e = 0; e < NDW; ++e)
-            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qv[hl][e]),
-                                                  __builtin_bit_cast(bf16x2, kr[u].d[e]), acc, false);
-          acc = row16_sum(acc);
-          if (li == 0) sc[(t - t0) * HG + hl] = acc * a.scale_log2;
+          for (int hf = 0; hf < 2; ++hf) {
+            const int i = kk * 32 + rg * 8 + 2 * e + hf;  // pair (i, i + D/2)
+            double sn, cs;
+            sincos((double)(ctx - 1) * exp2(k2 * (double)i), &sn, &cs);
+            const double x = hf ? bf16hi(pa[e]) : bf16lo(pa[e]);
+            const double y = hf ? bf16hi(pb[e]) : bf16lo(pb[e]);
+            ra[hf] = (float)(x * cs - y * sn);
+            rb[hf] = (float)(x * sn + y * cs);
+          }
+          pa[e] = pack_bf16x2(ra[0], ra[1]);
+          pb[e] = pack_bf16x2(rb[0], rb[1]);
         }
       }
     }
-  }
-  __syncthreads();
-
-  // ---- pass 2: chunk max and sum per head; scores become probabilities ----
-  for (int hl = w; hl < HG; hl += 4) {
-    float mx = -INFINITY;
-    for (int i = lane; i < n; i += 64) mx = fmaxf(mx, sc[i * HG + hl]);
-    mx = wave_max(mx);
-    float sum = 0.f;
-    for (int i = lane; i < n; i += 64) {
-      const float pr = fast_exp2(sc[i * HG + hl] - mx);
-      sc[i * HG + hl] = pr;
-      sum += pr;
-    }
-    sum = wave_sum(sum);
-    if (lane == 0) {
-      mls[hl][0] = mx;
-      mls[hl][1] = sum;
-    }
-  }
-  __syncthreads();
-
-  // ---- pass 3: o = sum_t p_t v_t ----
-  float o[HG][DPL];
 #pragma unroll
-  for (int hl = 0; hl < HG; ++hl)
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) o[hl][e] = 0.f;
-  for (int base = t0 + lg; base < t1; base += 16 * kUnroll) {
-    Vec<DPL> vr[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int t = base + 16 * u;
-      if (t < t1) vr[u].load(vb + t * row_v);
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int t = base + 16 * u;
-      if (t < t1) {
-        float vf[DPL];
-#pragma unroll
-        for (int e = 0; e < NDW; ++e) {
-          vf[2 * e] = bf16lo(vr[u].d[e]);
-          vf[2 * e + 1] = bf16hi(vr[u].d[e]);
-        }
-#pragma unroll
-        for (int hl = 0; hl < HG; ++hl) {
-          const float pr = sc[(t - t0) * HG + hl];
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) o[hl][e] = fmaf(pr, vf[e], o[hl][e]);
-        }
-      }
-    }
+    for (int kk = 0; kk < NKK; ++kk) qreg[kk] = as_bf16x8(raw[kk]);
+    retire_vmem();
   }
 
-  // ---- reduce the 16 row groups of the work-group, write the partial ----
+  // ---- per-lane LDS offsets within a stage (elements) ----
+  int koff[NKK];  // K operand: row hc, logical chunk 4*kk + rg
 #pragma unroll
-  for (int hl = 0; hl < HG; ++hl)
+  for (int kk = 0; kk < NKK; ++kk) koff[kk] = hc * D + ((4 * kk + rg) ^ dkey<CH>(hc)) * 8;
+  const int tj = (lane & 15) >> 2, tc = lane & 3;
+  const int vrow = rg * 4 + tj;  // V operand: rows rg*4 + j, dims db*16 + 4c
+  const int vkey = dkey<CH>(vrow);
+
+  // ---- stage loads (this wave only): lane i of instruction r covers stage bytes r*1024 + 16*i ----
+  const long long rk = (long long)a.Nkv * a.ldk, rv = (long long)a.Nkv * a.ldv;
+  const uint16_t* kb = a.kc + ((long long)b * a.max_ctx * a.Nkv + g) * a.ldk;
+  const uint16_t* vb = a.vc + ((long long)b * a.max_ctx * a.Nkv + g) * a.ldv;
+  auto issue_stage = [&](int k, int slot) {
+    const int tb = t0 + k * ROWS;
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) o[hl][e] = rows_sum(o[hl][e]);
-  if (lane < 16) {
+    for (int r = 0; r < LPS; ++r) {
+      const int ob = r * 1024 + 16 * lane;
+      const int row = ob / (D * 2);
+      const int pc = (ob % (D * 2)) / 16;
+      const int t = min(tb + row, t1 - 1);  // rows past the chunk re-read a valid row (masked)
+      const int lc = pc ^ dkey<CH>(row);
+      load_lds16_async(kb + t * rk + lc * 8, &ring[w][slot][0][r * 512]);
+      load_lds16_async(vb + t * rv + lc * 8, &ring[w][slot][1][r * 512]);
+    }
+  };
+
+  f32x4 o[NDB];
 #pragma unroll
-    for (int hl = 0; hl < HG; ++hl)
+  for (int i = 0; i < NDB; ++i) o[i] = f32x4{};
+  float m = -INFINITY, lsum = 0.f;
+
+  const int n_stages = (t1 - t0 + ROWS - 1) / ROWS;
+  const int my_n = n_stages > w ? (n_stages - w + 3) / 4 : 0;  // stages w, w+4, ...
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) red[w][hl][li * DPL + e] = o[hl][e];
+  for (int i = 0; i < NB - 1; ++i)
+    if (i < my_n) issue_stage(w + 4 * i, i);
+  for (int i = 0; i < my_n; ++i) {
+    const int k = w + 4 * i;
+    const int later = min(my_n - 1 - i, NB - 2);  // stages already issued after this one
+    if (later >= 2)
+      wait_vmem_n<4 * LPS>();
+    else if (later == 1)
+      wait_vmem_n<2 * LPS>();
+    else
+      wait_vmem();
+    if (i + NB - 1 < my_n) issue_stage(k + 4 * (NB - 1), (i + NB - 1) % NB);
+    const uint16_t* Ks = ring[w][i % NB][0];
+    const uint16_t* Vs = ring[w][i % NB][1];
+
+    f32x4 sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(Ks + koff[0]), qreg[0],
+                                                          f32x4{}, 0, 0, 0);
+#pragma unroll
+    for (int kk = 1; kk < NKK; ++kk)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(Ks + koff[kk]), qreg[kk],
+                                                     sacc, 0, 0, 0);
+    const int tb = t0 + k * ROWS + rg * 4;  // tokens of this lane's 4 scores
+    if (t0 + k * ROWS + ROWS > t1) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (tb + e >= t1) sacc[e] = -INFINITY;
+    }
+    float mt = fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3]));
+    mt = rows_max4(mt);
+    const float m_new = fmaxf(m, mt * a.scale_log2);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m - m_use);
+    m = m_new;
+    float pe[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pe[e] = fast_exp2(fmaf(sacc[e], a.scale_log2, -m_use));
+    lsum = fmaf(lsum, alpha, (pe[0] + pe[1]) + (pe[2] + pe[3]));
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[db][e] *= alpha;
+    }
+    const i16x4 pb = __builtin_bit_cast(i16x4, make_uint2(pack_bf16x2(pe[0], pe[1]), pack_bf16x2(pe[2], pe[3])));
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int lc = 2 * db + (tc >> 1);
+      const uint2 v = lds_read_tr16(Vs + vrow * D + (lc ^ vkey) * 8 + (tc & 1) * 4);
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, v), pb, o[db], 0, 0, 0);
+    }
+  }
+
+  // ---- merge the four waves (per head: max, sum and output), write the chunk partial ----
+  const float lt = [&] {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
+    return pair_sum32(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+  }();
+  // the merge reuses each wave's own ring area (its loads have all landed): [16][D+4] outputs, then
+  // [16][2] (max, sum)
+  auto mo = [&](int v) { return reinterpret_cast<float*>(&ring[v][0][0][0]); };
+  auto mm = [&](int v) { return reinterpret_cast<float*>(&ring[v][0][0][0]) + 16 * (D + 4); };
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) mo(w)[hc * (D + 4) + db * 16 + rg * 4 + e] = o[db][e];
+  if (rg == 0) {
+    mm(w)[hc * 2 + 0] = my_n > 0 ? m : -INFINITY;
+    mm(w)[hc * 2 + 1] = my_n > 0 ? lt : 0.f;
   }
   __syncthreads();
   for (int i = tid; i < HG * D; i += kThreads) {
     const int hl = i / D, d = i % D;
-    const float tot = red[0][hl][d] + red[1][hl][d] + red[2][hl][d] + red[3][hl][d];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) mx = fmaxf(mx, mm(v)[hl * 2]);
+    float acc = 0.f, l = 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float mv = mm(v)[hl * 2];
+      const float wgt = mv == -INFINITY ? 0.f : fast_exp2(mv - mx);
+      acc = fmaf(wgt, mo(v)[hl * (D + 4) + d], acc);
+      l = fmaf(wgt, mm(v)[hl * 2 + 1], l);
+    }
     const long long slot = ((long long)b * a.Nh + h0 + hl) * a.nsplit + s;
-    a.part_o[slot * D + d] = tot;
+    a.part_o[slot * D + d] = acc;
     if (d == 0) {
-      a.part_ml[slot * 2 + 0] = mls[hl][0];
-      a.part_ml[slot * 2 + 1] = mls[hl][1];
+      a.part_ml[slot * 2 + 0] = mx;
+      a.part_ml[slot * 2 + 1] = l;
     }
   }
 }
 
 // Merge the chunks of each (b, h): m* = max m_s, l* = sum 2^(m_s - m*) l_s,
-// out = sum 2^(m_s - m*) o_s / l*. One wave per (b, h).
+// out = sum 2^(m_s - m*) o_s / l*. One wave per (b, h); each lane owns float4 columns and keeps
+// the loads of several chunks in flight.
 __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(DecodeArgs a) {
   const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -245,39 +250,58 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(DecodeArgs a) {
   const int ns = (ctx + a.chunk - 1) / a.chunk;
   const long long slot0 = (long long)wid * a.nsplit;
   const int Dv = a.Dv;
+  const int nvec = Dv / 4;
   uint16_t* op = a.out + (long long)wid * Dv;
   if (ns == 0) {
-    for (int d = lane; d < Dv; d += 64) op[d] = 0;
+    for (int c = lane; c < nvec; c += 64) *reinterpret_cast<uint2*>(op + 4 * c) = make_uint2(0u, 0u);
     return;
   }
+  const float* ml = a.part_ml + slot0 * 2;
   float mx = -INFINITY;
-  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, a.part_ml[(slot0 + s) * 2]);
+  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, ml[2 * s]);
   float l = 0.f;
-  for (int s = 0; s < ns; ++s) l += fast_exp2(a.part_ml[(slot0 + s) * 2] - mx) * a.part_ml[(slot0 + s) * 2 + 1];
+  for (int s = 0; s < ns; ++s) l += fast_exp2(ml[2 * s] - mx) * ml[2 * s + 1];
   const float inv = 1.f / l;
-  for (int d = lane; d < Dv; d += 64) {
-    float acc = 0.f;
-    for (int s = 0; s < ns; ++s) acc += fast_exp2(a.part_ml[(slot0 + s) * 2] - mx) * a.part_o[(slot0 + s) * Dv + d];
-    op[d] = f32_to_bf16(acc * inv);
+  const float4* po = reinterpret_cast<const float4*>(a.part_o + slot0 * Dv);
+  for (int c = lane; c < nvec; c += 64) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    int s = 0;
+    for (; s + 4 <= ns; s += 4) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = po[(long long)(s + u) * nvec + c];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float wgt = fast_exp2(ml[2 * (s + u)] - mx);
+        acc.x = fmaf(wgt, v[u].x, acc.x);
+        acc.y = fmaf(wgt, v[u].y, acc.y);
+        acc.z = fmaf(wgt, v[u].z, acc.z);
+        acc.w = fmaf(wgt, v[u].w, acc.w);
+      }
+    }
+    for (; s < ns; ++s) {
+      const float4 v = po[(long long)s * nvec + c];
+      const float wgt = fast_exp2(ml[2 * s] - mx);
+      acc.x = fmaf(wgt, v.x, acc.x);
+      acc.y = fmaf(wgt, v.y, acc.y);
+      acc.z = fmaf(wgt, v.z, acc.z);
+      acc.w = fmaf(wgt, v.w, acc.w);
+    }
+    *reinterpret_cast<uint2*>(op + 4 * c) =
+        make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
   }
 }
 
-template <int D, int HG>
-hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
-  const long long n_wg = (long long)a.B * (a.Nh / HG) * a.nsplit;
-  if (n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  const size_t lds = (size_t)a.chunk * HG * sizeof(float);
-  decode_split_kernel<D, HG><<<dim3((unsigned)n_wg), dim3(kThreads), lds, st>>>(a);
-  return hipGetLastError();
-}
+constexpr int kDecodeNB = 2;  // LDS ring stages per wave (2: two work-groups fit a CU)
 
 template <int D>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t st) {
   const int G = a.Nh / a.Nkv;
-  if (G % 8 == 0) return launch_t<D, 8>(a, st);
-  if (G % 4 == 0) return launch_t<D, 4>(a, st);
-  if (G % 2 == 0) return launch_t<D, 2>(a, st);
-  return launch_t<D, 1>(a, st);
+  const int HG = G < 16 ? G : 16;
+  const long long n_wg = (long long)a.B * a.Nkv * (G / HG) * a.nsplit;
+  if (n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  decode_split_kernel<D, kDecodeNB><<<dim3((unsigned)n_wg), dim3(kThreads), 0, st>>>(a);
+  return hipGetLastError();
 }
 }  // namespace
 

@@ -7,13 +7,21 @@
 // DeepSeek-V3's 128 + 64 per-head query dims).
 //
 // With 128 heads per row the work is ~242 FLOP per cached byte, so the matrix cores are used:
-//   - a work-group = 4 waves x 16 heads owns (b, 64 heads, one context chunk); each cached row
-//     is loaded once per work-group with 128-bit coalesced loads (4 rows per thread unit, one
-//     tile of 32 tokens ahead in registers) into a double-buffered LDS tile: row-major for the
-//     scores and transposed (dims x tokens) for the value contraction;
-//   - per wave and tile: S^T[32 tokens x 16 heads] = K Q^T (18 k-steps over 576 dims), online
-//     softmax per head, then O^T[512 x 16] += V^T P^T (32 MFMAs);
-//   - each chunk writes (max, sum, unnormalised output) in fp32 for the shared split reduction.
+//   - a work-group = NW waves x 16 heads owns (sequence, 16*NW heads, one context chunk); with
+//     NW = 8 all 128 heads share the work-group, so every cached row crosses HBM once per chunk;
+//   - 32-token tiles (36 KiB) go from HBM straight into an LDS ring of NB stages
+//     (global_load_lds_dwordx4): the loads of tiles j+1 .. j+NB-1 are in flight while tile j is
+//     computed;
+//     16-byte chunks are XOR-swizzled within aligned groups of 8 by a permutation of the row
+//     index so operand reads from consecutive rows spread over the banks;
+//   - per wave and tile: S^T[32 tokens x 16 heads] = K Q^T (18 k-steps over 576 dims, K operand
+//     read row-major), online softmax per head, then O^T[512 x 16] += V^T P^T (32 MFMAs) with the
+//     V operand read from the SAME row-major tile by the transposing LDS read (4 consecutive
+//     tokens of one dim per lane) - the row serves as K and as V without a second copy;
+//   - each chunk writes (max, sum, unnormalised output) in fp32 for the split reduction; a single
+//     chunk writes the normalised bf16 output directly.
+// Work-group ids are mapped so that the head groups of one (sequence, chunk) run on one XCD and
+// share its L2 when the heads do not fit one work-group.
 #include "kernels.hpp"
 
 namespace attn {
@@ -21,17 +29,20 @@ namespace attn {
 namespace {
 constexpr int DQ = 576;
 constexpr int DV = 512;
-constexpr int TT = 32;          // tokens per tile
-constexpr int KP = DQ + 8;      // row-major tile pitch (elements)
-constexpr int VP = TT + 4;      // transposed tile pitch (elements)
-constexpr int OCT = DQ / 8;     // 72 16-byte chunks per row
-constexpr int NUNIT = (TT / 4) * OCT;  // 576 load units of 4 tokens x 8 dims
-constexpr int NKK = DQ / 32;    // 18 k-steps
-constexpr int NDB = DV / 16;    // 32 output blocks of 16 dims
+constexpr int TT = 32;            // tokens per tile
+constexpr int TILE = TT * DQ;     // elements per tile (36 KiB)
+constexpr int NSLOT = TILE * 2 / 1024;  // 36 load instructions of 1 KiB per tile
+constexpr int NKK = DQ / 32;      // 18 k-steps
+constexpr int NDB = DV / 16;      // 32 output blocks of 16 dims
+constexpr int NB = 2;             // LDS ring stages (tiles in flight: NB - 1)
 
-__device__ __forceinline__ uint32_t sel_lo(uint32_t x, uint32_t y) { return __byte_perm(x, y, 0x5410); }
-__device__ __forceinline__ uint32_t sel_hi(uint32_t x, uint32_t y) { return __byte_perm(x, y, 0x7632); }
-__device__ __forceinline__ uint32_t dw(const U4& v, int e) { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; }
+// XOR key applied to the 16-byte chunk index in tile row `row`: a permutation of the row's low 4
+// bits (b3 b2 b1 b0 -> b3 b1 b0 b2) for chunks 0..63 (it stays inside the chunk's aligned group of
+// 16), and of the low 3 bits for chunks 64..71 (aligned group of 8; 72 chunks per row). Rows
+// 0..15 get distinct keys, so the K operand reads (16 consecutive rows, one chunk) hit distinct
+// bank groups, and the 4 rows of one transposing V read land in 4 different 32-byte groups.
+__device__ __forceinline__ int rkey3(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+__device__ __forceinline__ int rkey(int row, int chunk) { return rkey3(row) | (chunk < 64 ? (row & 8) : 0); }
 
 // Max / sum over the four 16-lane rows that hold one head's tokens.
 __device__ __forceinline__ float rows_max(float x) {
@@ -44,22 +55,28 @@ __device__ __forceinline__ float rows_sum(float x) {
 }
 
 template <int NW>
-__global__ __launch_bounds__(NW * 64, 1) void decode_mla_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(NW * 64, (NW >= 8 ? 2 : 1)) void decode_mla_kernel(DecodeArgs a) {
   constexpr int NT = NW * 64;
-  constexpr int UPT = (NUNIT + NT - 1) / NT;  // load units per thread
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][TT * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][DV * VP];
+  constexpr int SPW = (NSLOT + NW - 1) / NW;  // load slots per wave (some waves one fewer)
+  constexpr int WAITN = NSLOT / NW;           // loads of the next tile every wave has issued
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[NB][TILE];
 
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // id -> (pair = (b, split), head group): the head groups of a pair sit 8 ids apart (one XCD)
   const int n_hg = a.Nh / (16 * NW);
-  const int s = blockIdx.x % a.nsplit;
-  const int hgrp = (blockIdx.x / a.nsplit) % n_hg;
-  const int b = blockIdx.x / (a.nsplit * n_hg);
+  const int n_pairs = a.B * a.nsplit;
+  const int id = blockIdx.x;
+  const int pair = (id / 8 / n_hg) * 8 + id % 8;
+  const int hgrp = (id / 8) % n_hg;
+  if (pair >= n_pairs) return;
+  const int b = pair / a.nsplit;
+  const int s = pair % a.nsplit;
   const int ctx = min(max(a.ctx_lens[b], 0), a.max_ctx);
   const int t0 = s * a.chunk;
   if (t0 >= ctx) return;
   const int t1 = min(ctx, t0 + a.chunk);
-  const int w = tid >> 6, lane = tid & 63;
   const int hc = lane & 15, rg = lane >> 4;  // head column, row group
   const int h = hgrp * 16 * NW + w * 16 + hc;
 
@@ -69,6 +86,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mla_kernel(DecodeArgs a) {
     const uint16_t* qp = a.q + ((long long)b * a.Nh + h) * DQ + rg * 8;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) qreg[kk] = as_bf16x8(ldg16(qp + kk * 32));
+    retire_vmem();
   }
 
   f32x4 o[NDB];
@@ -76,75 +94,64 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mla_kernel(DecodeArgs a) {
   for (int i = 0; i < NDB; ++i) o[i] = f32x4{};
   float m = -INFINITY, lsum = 0.f;
 
-  const long long row = a.ldk;  // Nkv == 1
-  const uint16_t* base = a.kc + (long long)b * a.max_ctx * row;
+  // ---- per-lane LDS offsets (elements) ----
+  // K operand (row hc of a 16-token group, logical chunk 4*kk + rg). For kk < 16 the physical
+  // chunk is 4*(kk ^ (key>>2)) + ((rg ^ key) & 3) with a 4-bit key: one base per kk mod 4 plus
+  // 32*(kk & ~3); chunks 64..71 (kk = 16, 17) use the 3-bit key.
+  const int kkey = rkey(hc, 0);
+  int koff[4], koffr[2];
+#pragma unroll
+  for (int m4 = 0; m4 < 4; ++m4) koff[m4] = hc * DQ + ((4 * m4 + rg) ^ kkey) * 8;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) koffr[i] = hc * DQ + ((4 * (16 + i) + rg) ^ rkey(hc, 64)) * 8;
+  // V operand (transposing read): 16-lane group rg addresses token rows rg*4 + j (and +16), dims
+  // db*16 + 4c, logical chunk 2*db + (c>>1): physical 2*(db ^ (key>>1)) + (((c>>1) ^ key) & 1).
+  const int tj = (lane & 15) >> 2, tc = lane & 3;
+  const int vrow = rg * 4 + tj;
+  const int vkey = rkey(vrow, 0);
+  const int vbase = vrow * DQ + ((((tc >> 1) ^ vkey) & 1) * 8) + (tc & 1) * 4;
+  const int vx = vkey >> 1;
 
-  U4 lr[UPT][4];
-  auto load_tile = [&](int j) {
+  // ---- tile loads: wave w fills slots w, w+NW, ...; lane i of slot sl covers tile bytes
+  // sl*1024 + 16*i = row*1152 + 16*pc and fetches logical chunk pc ^ rkey(row, pc) of that row ----
+  const long long row_pitch = a.ldk;  // Nkv == 1
+  const uint16_t* seq = a.kc + (long long)b * a.max_ctx * row_pitch;
+  auto issue_tile = [&](int j, uint16_t* dst) {
 #pragma unroll
-    for (int r = 0; r < UPT; ++r) {
-      const int u = tid + NT * r;
-      if (u < NUNIT) {
-        const int tq = u / OCT, oc = u % OCT;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = t0 + j * TT + tq * 4 + e;
-          lr[r][e] = t < t1 ? ldg16(base + t * row + oc * 8) : U4{0, 0, 0, 0};
-        }
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int r = 0; r < UPT; ++r) {
-      const int u = tid + NT * r;
-      if (u < NUNIT) {
-        const int tq = u / OCT, oc = u % OCT;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) *reinterpret_cast<U4*>(&Ks[buf][(tq * 4 + e) * KP + oc * 8]) = lr[r][e];
-        if (oc < DV / 8) {
-          const int unit = tq ^ (oc & 7);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t x0 = dw(lr[r][0], e), x1 = dw(lr[r][1], e), x2 = dw(lr[r][2], e), x3 = dw(lr[r][3], e);
-            *reinterpret_cast<uint2*>(&Vt[buf][(oc * 8 + 2 * e) * VP + unit * 4]) =
-                make_uint2(sel_lo(x0, x1), sel_lo(x2, x3));
-            *reinterpret_cast<uint2*>(&Vt[buf][(oc * 8 + 2 * e + 1) * VP + unit * 4]) =
-                make_uint2(sel_hi(x0, x1), sel_hi(x2, x3));
-          }
-        }
+    for (int r = 0; r < SPW; ++r) {
+      const int sl = w + NW * r;
+      if (sl < NSLOT) {
+        const int ob = sl * 1024 + 16 * lane;
+        const int row = ob / (DQ * 2);
+        const int pc = (ob % (DQ * 2)) / 16;
+        const int t = min(t0 + j * TT + row, t1 - 1);  // rows past the chunk re-read a valid row (masked)
+        load_lds16_async(seq + t * row_pitch + (pc ^ rkey(row, pc)) * 8, dst + sl * 512);
       }
     }
   };
 
-  const int n_tiles = (t1 - t0 + TT - 1) / TT;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < n_tiles) load_tile(j + 1);
-
-    // S^T for two 16-token groups: lane holds head hc, tokens tg*16 + rg*4 + i
+  auto compute_tile = [&](int j, const uint16_t* Tt) {
     f32x4 sacc[2] = {f32x4{}, f32x4{}};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
 #pragma unroll
       for (int tg = 0; tg < 2; ++tg) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[buf][(tg * 16 + hc) * KP + kk * 32 + rg * 8]);
+        const int ko = kk < 16 ? koff[kk & 3] + 32 * (kk & ~3) : koffr[kk - 16];
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Tt + tg * 16 * DQ + ko);
         sacc[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qreg[kk], sacc[tg], 0, 0, 0);
       }
+      if (kk % 3 == 2) __builtin_amdgcn_sched_barrier(0);  // bound how far LDS reads are hoisted
     }
     const int tbase = t0 + j * TT;
-    float mt = -INFINITY;
+    if (tbase + TT > t1) {
 #pragma unroll
-    for (int tg = 0; tg < 2; ++tg)
+      for (int tg = 0; tg < 2; ++tg)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (tbase + tg * 16 + rg * 4 + i >= t1) sacc[tg][i] = -INFINITY;
-        mt = fmaxf(mt, sacc[tg][i]);
-      }
+        for (int i = 0; i < 4; ++i)
+          if (tbase + tg * 16 + rg * 4 + i >= t1) sacc[tg][i] = -INFINITY;
+    }
+    float mt = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3]));
+    mt = fmaxf(mt, fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
     mt = rows_max(mt);
     const float m_new = fmaxf(m, mt * a.scale_log2);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
@@ -161,7 +168,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mla_kernel(DecodeArgs a) {
         psum += e0 + e1;
         pk[tg * 2 + i / 2] = pack_bf16x2(e0, e1);
       }
-    lsum = lsum * alpha + psum;
+    lsum = fmaf(lsum, alpha, psum);
     if (__ballot(alpha != 1.f)) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
@@ -171,49 +178,82 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mla_kernel(DecodeArgs a) {
     const bf16x8 pb = __builtin_bit_cast(bf16x8, U4{pk[0], pk[1], pk[2], pk[3]});
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const int dim = db * 16 + hc;
-      const int sw = (dim >> 3) & 7;
-      const uint16_t* vr = &Vt[buf][dim * VP];
-      const uint2 lo = *reinterpret_cast<const uint2*>(vr + ((rg) ^ sw) * 4);
-      const uint2 hi = *reinterpret_cast<const uint2*>(vr + ((4 + rg) ^ sw) * 4);
+      const int vo = vbase + 16 * ((db & ~7) + ((db & 7) ^ vx));
+      const uint2 lo = lds_read_tr16(Tt + vo);
+      const uint2 hi = lds_read_tr16(Tt + 16 * DQ + vo);
       const bf16x8 va = __builtin_bit_cast(bf16x8, U4{lo.x, lo.y, hi.x, hi.y});
       o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[db], 0, 0, 0);
+      if (db % 4 == 3) __builtin_amdgcn_sched_barrier(0);
     }
+  };
 
-    if (j + 1 < n_tiles) store_tile(buf ^ 1);
-    __syncthreads();
+  const int n_tiles = (t1 - t0 + TT - 1) / TT;
+  auto wait_tile = [&](int j) {  // this wave's loads of tile j done; those of later tiles may fly
+    const int later = min(n_tiles - 1 - j, NB - 2);
+    if (later >= 2)
+      wait_vmem_n<(2 * WAITN <= 63 ? 2 * WAITN : WAITN)>();  // the smaller count over-waits safely
+    else if (later == 1)
+      wait_vmem_n<WAITN>();
+    else
+      wait_vmem();
+    barrier_only();
+  };
+
+#pragma unroll
+  for (int j = 0; j < NB - 1; ++j)
+    if (j < n_tiles) issue_tile(j, ring[j]);
+  for (int j = 0; j < n_tiles; ++j) {
+    wait_tile(j);
+    if (j + NB - 1 < n_tiles) issue_tile(j + NB - 1, ring[(j + NB - 1) % NB]);
+    compute_tile(j, ring[j % NB]);
   }
 
-  // partial: unnormalised O (lane: head hc, dims db*16 + rg*4 .. +3), max and sum
+  // ---- result: lane holds head hc, dims db*16 + rg*4 .. +3 ----
+  const float ltot = rows_sum(lsum);
+  if (a.nsplit == 1) {
+    const float inv = 1.f / ltot;
+    uint16_t* op = a.out + ((long long)b * a.Nh + h) * DV + rg * 4;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      *reinterpret_cast<uint2*>(op + db * 16) =
+          make_uint2(pack_bf16x2(o[db][0] * inv, o[db][1] * inv), pack_bf16x2(o[db][2] * inv, o[db][3] * inv));
+    return;
+  }
   const long long slot = ((long long)b * a.Nh + h) * a.nsplit + s;
   float* po = a.part_o + slot * DV + rg * 4;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
     *reinterpret_cast<float4*>(po + db * 16) = make_float4(o[db][0], o[db][1], o[db][2], o[db][3]);
-  const float ltot = rows_sum(lsum);
   if (rg == 0) {
     a.part_ml[slot * 2 + 0] = m;
     a.part_ml[slot * 2 + 1] = ltot;
   }
 }
+
+template <int NW>
+hipError_t launch_nw(const DecodeArgs& a, hipStream_t st) {
+  const long long n_hg = a.Nh / (16 * NW);
+  const long long pairs = (long long)a.B * a.nsplit;
+  const long long n_wg = ((pairs + 7) / 8) * 8 * n_hg;
+  if (n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  decode_mla_kernel<NW><<<dim3((unsigned)n_wg), dim3(NW * 64), 0, st>>>(a);
+  return hipGetLastError();
+}
 }  // namespace
 
+int mla_waves_per_group(int Nh) { return Nh % 128 == 0 ? 8 : Nh % 64 == 0 ? 4 : Nh % 32 == 0 ? 2 : 1; }
+
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t st) {
-  int nw = (a.Nh % 64 == 0) ? 4 : (a.Nh % 32 == 0) ? 2 : 1;
-  const long long n_wg = (long long)a.B * (a.Nh / (16 * nw)) * a.nsplit;
-  if (n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  switch (nw) {
+  switch (mla_waves_per_group(a.Nh)) {
+    case 8:
+      return launch_nw<8>(a, st);
     case 4:
-      decode_mla_kernel<4><<<dim3((unsigned)n_wg), dim3(256), 0, st>>>(a);
-      break;
+      return launch_nw<4>(a, st);
     case 2:
-      decode_mla_kernel<2><<<dim3((unsigned)n_wg), dim3(128), 0, st>>>(a);
-      break;
+      return launch_nw<2>(a, st);
     default:
-      decode_mla_kernel<1><<<dim3((unsigned)n_wg), dim3(64), 0, st>>>(a);
-      break;
+      return launch_nw<1>(a, st);
   }
-  return hipGetLastError();
 }
 
 }  // namespace attn

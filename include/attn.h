@@ -92,8 +92,8 @@ int attn_prefill(const void* q, const void* k, const void* v, void* out,
  * out      [B, Nh, Dv]                      written
  * rope_theta > 0 rotates q at position ctx_lens[b]-1 (the cache holds already-rotated keys);
  *          only for Dqk == Dv. scale <= 0 selects 1 / sqrt(Dqk).
- * Supported (ATTN_BF16 only): Dqk == Dv in {64, 128} with any Nh % Nkv == 0 whose group size
- *   Nh / Nkv is a multiple of 1, 2, 4 or 8 (heads are processed in groups of up to 8);
+ * Supported (ATTN_BF16 only): Dqk == Dv in {64, 128} with Nh % Nkv == 0 and a group size
+ *   G = Nh / Nkv of at most 16 or a multiple of 16 (query heads are processed 16 at a time);
  *   and the MLA form Dqk = 576, Dv = 512, Nkv = 1, vcache == kcache, ldv == ldk, Nh % 16 == 0.
  * workspace: at least attn_decode_workspace_bytes(...) bytes (split-KV partial results).
  * ------------------------------------------------------------------------------------------ */
