@@ -108,8 +108,8 @@ def cpu_baseline():
     except Exception:  # noqa: BLE001
         threads = 1
     P, D, M = synth.LLAMA3_PREFILL, synth.LLAMA3_DECODE, synth.MLA_DECODE
-    # prefill: all 8192 rows of query heads 0-3 of sequence 0 (they share KV head 0)
-    hq = 4
+    # prefill: all 8192 rows of query heads 0-7 of sequence 0
+    hq = 8
     q = synth.as_f32(synth.normal(P.wid, 10, (1, P.S, hq, P.Dh), "bf16"), "bf16")
     k = synth.as_f32(synth.normal(P.wid, 11, (1, P.S, 1, P.Dh), "bf16"), "bf16")
     v = synth.as_f32(synth.normal(P.wid, 12, (1, P.S, 1, P.Dh), "bf16"), "bf16")
@@ -146,7 +146,7 @@ def cpu_baseline():
     frac = 0.5 * (p_tflops / acc.PEAK_BF16_TFLOPS + d_gbs / acc.PEAK_HBM_GBS)
     return {
         "value": 100.0 * frac, "unit": "% of peak", "cores": int(threads), "kind": "oracle",
-        "sample": (f"fp64 numpy oracle on the host: every row of query heads 0-3 of sequence 0 of the Llama-3-8B "
+        "sample": (f"fp64 numpy oracle on the host: every row of query heads 0-7 of sequence 0 of the Llama-3-8B "
                    f"prefill ({tp:.1f} s, {p_tflops * 1e3:.2f} GFLOP/s algorithmic); all 64 sequences of the "
                    f"GQA decode ({td:.1f} s) and all 32 of the MLA decode ({tm:.1f} s): {d_gbs:.3f} GB/s "
                    f"algorithmic; {threads} BLAS threads; host {platform.machine()}, {os.cpu_count()} logical CPUs"),
