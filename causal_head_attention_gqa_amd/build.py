@@ -8,6 +8,7 @@ from __future__ import annotations
 
 import concurrent.futures
 import os
+import re
 import subprocess
 import sys
 
@@ -32,8 +33,42 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
+_REG = re.compile(r"([va])\[(\d+):(\d+)\]|([va])(\d+)$")
+
+
+def _regs(tok: str):
+    m = _REG.match(tok.strip())
+    if not m:
+        return None
+    if m.group(1):
+        return m.group(1), int(m.group(2)), int(m.group(3))
+    return m.group(4), int(m.group(5)), int(m.group(5))
+
+
+def mfma_overlaps(asm: str) -> list[str]:
+    """Matrix-core instructions whose destination registers overlap their A or B operand.
+
+    The compiler may allocate an MFMA's destination over a source that dies at the instruction;
+    on gfx950 such code has produced run-to-run different results, so the build rejects it (the
+    kernels keep their sources live through the mfma wrappers in common.hpp instead).
+    """
+    bad = []
+    for line in asm.splitlines():
+        t = line.strip()
+        if not t.startswith("v_mfma"):
+            continue
+        ops = t.split(None, 1)[1].split(",")
+        d, a, b = (_regs(o) for o in ops[:3])
+        for s in (a, b):
+            if d and s and d[0] == s[0] and not (d[2] < s[1] or s[2] < d[1]):
+                bad.append(t)
+                break
+    return bad
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
+    asm = os.path.join(BUILD, os.path.basename(src)[:-4] + ".s")
     cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -41,6 +76,13 @@ def _compile(src: str) -> str:
     errs = [ln for ln in r.stderr.splitlines() if "packed-fp32-ops" not in ln and ln.strip()]
     if errs:
         sys.stderr.write("\n".join(errs) + "\n")
+    r = subprocess.run([HIPCC, *FLAGS, "--cuda-device-only", "-S", src, "-o", asm], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed for {src}:\n{r.stderr}")
+    with open(asm) as f:
+        bad = mfma_overlaps(f.read())
+    if bad:
+        raise RuntimeError(f"{src}: MFMA destination overlaps a source operand:\n" + "\n".join(bad[:5]))
     return obj
 
 

@@ -65,6 +65,23 @@ __device__ __forceinline__ void load_lds16(const void* gptr, void* lds_base) {
   __builtin_amdgcn_global_load_lds(gptr, (lds_void_t*)lds_base, 16, 0, 0);
 }
 
+// v_mfma_f32_16x16x32_bf16 / v_mfma_f32_32x32x16_bf16 whose destination is never allocated over
+// the A or B operand registers: the compiler may otherwise reuse a source that dies at the
+// instruction as its destination, which on gfx950 has given run-to-run different (wrong)
+// results. The empty asm keeps both sources live until the result exists; it also pins the
+// result to VGPRs, so accumulators the compiler keeps in AGPRs use the plain builtin (the build
+// scans the generated code and rejects any remaining overlap).
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  asm volatile("" ::"v"(a), "v"(b), "v"(d));
+  return d;
+}
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  const f32x16 d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  asm volatile("" ::"v"(a), "v"(b), "v"(d));
+  return d;
+}
+
 // Transposing LDS read (ds_read_b64_tr_b16). Within each group of 16 lanes, lanes 4j..4j+3 each
 // address 4 consecutive 16-bit elements of "row" j (16 elements per row); afterwards lane i holds
 // element i of rows 0..3. With a row-major [key][dim] tile this yields 4 consecutive keys of one

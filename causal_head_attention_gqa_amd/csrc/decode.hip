@@ -163,12 +163,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     const uint16_t* Ks = ring[w][i % NB][0];
     const uint16_t* Vs = ring[w][i % NB][1];
 
-    f32x4 sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(Ks + koff[0]), qreg[0],
-                                                          f32x4{}, 0, 0, 0);
+    f32x4 sacc = mfma16x16x32(*reinterpret_cast<const bf16x8*>(Ks + koff[0]), qreg[0], f32x4{});
 #pragma unroll
     for (int kk = 1; kk < NKK; ++kk)
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(Ks + koff[kk]), qreg[kk],
-                                                     sacc, 0, 0, 0);
+      sacc = mfma16x16x32(*reinterpret_cast<const bf16x8*>(Ks + koff[kk]), qreg[kk], sacc);
     const int tb = t0 + k * ROWS + rg * 4;  // tokens of this lane's 4 scores
     if (t0 + k * ROWS + ROWS > t1) {
 #pragma unroll

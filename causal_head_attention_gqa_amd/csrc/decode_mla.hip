@@ -136,7 +136,7 @@ __global__ __launch_bounds__(NW * 64, (NW >= 8 ? 2 : 1)) void decode_mla_kernel(
       for (int tg = 0; tg < 2; ++tg) {
         const int ko = koff[kk & 3] + 32 * (kk & ~3);
         const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Tt + tg * 16 * DQ + ko);
-        sacc[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qreg[kk], sacc[tg], 0, 0, 0);
+        sacc[tg] = mfma16x16x32(ka, qreg[kk], sacc[tg]);
       }
       if (kk % 3 == 2) __builtin_amdgcn_sched_barrier(0);  // bound how far LDS reads are hoisted
     }

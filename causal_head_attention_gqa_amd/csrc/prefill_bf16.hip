@@ -183,21 +183,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     const bool act1 = key0 + 32 < S && (!causal || key0 + 32 <= wp0 + 31);
     f32x16 sacc[2];
     if (act0) {
-      sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(Kt + koff[0]), qreg[0],
-                                                         f32x16{}, 0, 0, 0);
+      sacc[0] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(Kt + koff[0]), qreg[0], f32x16{});
 #pragma unroll
       for (int kk = 1; kk < NQ; ++kk)
-        sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(Kt + koff[kk]),
-                                                           qreg[kk], sacc[0], 0, 0, 0);
+        sacc[0] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(Kt + koff[kk]), qreg[kk], sacc[0]);
     }
     if (act1) {
       const uint16_t* K1 = Kt + 32 * D;
-      sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(K1 + koff[0]), qreg[0],
-                                                         f32x16{}, 0, 0, 0);
+      sacc[1] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(K1 + koff[0]), qreg[0], f32x16{});
 #pragma unroll
       for (int kk = 1; kk < NQ; ++kk)
-        sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(K1 + koff[kk]),
-                                                           qreg[kk], sacc[1], 0, 0, 0);
+        sacc[1] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(K1 + koff[kk]), qreg[kk], sacc[1]);
     }
 
 #pragma unroll
@@ -247,7 +243,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
           const uint2 lo = lds_read_tr16(Vb + voff_par[db & 1] + vimm(0, db));
           const uint2 hi = lds_read_tr16(Vb + voff_par[db & 1] + vimm(1, db));
           const bf16x8 aop = __builtin_bit_cast(bf16x8, U4{lo.x, lo.y, hi.x, hi.y});
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop, bop, o[db], 0, 0, 0);
+          o[db] = mfma32x32x16(aop, bop, o[db]);
         }
       }
     }
