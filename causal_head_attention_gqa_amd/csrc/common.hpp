@@ -96,11 +96,16 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 // The same 16-byte direct-to-LDS load issued as inline assembly. The compiler then neither knows
 // that LDS is written nor waits for it: the caller owns every vmcnt wait for these loads (with
 // vmcnt(N) it can keep the newest N loads in flight, e.g. a ring of LDS stages). The LDS base of
-// the wave (byte address) goes through M0. The loads carry the non-temporal hint: the callers
-// stream each cache row once, and the hint measurably raises the achieved HBM bandwidth.
+// the wave (byte address) goes through M0. kStream adds the non-temporal hint, for rows that are
+// read once (the decode caches; it measurably raises the achieved HBM bandwidth there); tiles that
+// other work-groups read again (prefill K/V) keep the default policy.
+template <bool kStream = true>
 __device__ __forceinline__ void load_lds16_async(const void* gptr, const void* lds_base) {
   const uint32_t lds_addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
-  asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(gptr), "{m0}"(lds_addr) : "memory");
+  if constexpr (kStream)
+    asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(gptr), "{m0}"(lds_addr) : "memory");
+  else
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(lds_addr) : "memory");
 }
 
 // Work-group barrier without the memory fences of __syncthreads(): for tiles filled by

@@ -10,19 +10,19 @@
 //   - each wave owns 32 query rows of one head and computes the transposed score block
 //     S^T = K Q^T, so that one lane holds one query's scores: the row max needs a single
 //     lane-pair exchange and the row sum none until the end;
-//   - K/V tiles of 64 keys go from HBM straight into LDS (global_load_lds_dwordx4, no staging
-//     registers), double-buffered in two distinct LDS arrays so the next tile's loads overlap the
-//     current tile's math; rows are stored as in memory with their 16-byte chunks XOR-swizzled by
-//     a permutation of the row index, so the K operand reads (16 B per lane, 32 rows) and the
-//     transposing V reads (ds_read_b64_tr_b16: 4 consecutive keys of one dim per lane) spread
-//     over the LDS banks;
+//   - K/V tiles of 32 keys go from HBM straight into LDS (global_load_lds_dwordx4, no staging
+//     registers) through a ring of three stages, so two tiles load while one is computed; rows are
+//     stored as in memory with their 16-byte chunks XOR-swizzled by a permutation of the row
+//     index, so the K operand reads (16 B per lane, 32 rows) and the transposing V reads
+//     (ds_read_b64_tr_b16: 4 consecutive keys of one dim per lane) spread over the LDS banks;
+//     the small tiles (48 KiB of LDS per work-group) and 168 registers per lane let three
+//     work-groups share a CU;
 //   - tiles past the work-group's last query are never visited and 32-key blocks above a wave's
 //     diagonal are skipped ("2.7 Transformer Decoder Block完整解析" §3.3); the element mask is
 //     applied only on blocks that cross the diagonal or the sequence end;
 //   - online softmax per 32-key block ("Transformer 架构完全深度解析" §十三: running max and sum;
 //     the output accumulator is rescaled by the same factor, and only when some row's max
-//     moved). Both blocks' Q.K products are issued before the first block's exponentials so the
-//     matrix core works while the vector ALUs do the softmax.
+//     moved).
 // All per-wave control values are scalar (wave-uniform branches); per-lane LDS and global
 // offsets are computed once. Grid order puts the work-groups with the most tiles first.
 #include "kernels.hpp"
@@ -30,7 +30,8 @@
 namespace attn {
 
 namespace {
-constexpr int kBC = 64;
+constexpr int kBC = 32;     // keys per tile (one 32x32 score block per wave)
+constexpr int kStages = 3;  // LDS ring depth: tiles j+1 and j+2 load while tile j is computed
 constexpr int kThreads = 256;
 
 // Physical 16-byte chunk of logical chunk c in tile row `row` (CH chunks per row). The XOR key
@@ -44,7 +45,7 @@ __device__ __forceinline__ int swz(int c, int row) {
 }
 
 template <int D, int HPW>
-__global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
+__global__ __launch_bounds__(kThreads, 3) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ out, const float2* __restrict__ table, int B, int S, int Nh, int Nkv, float c,
     int causal, int n_ptiles) {
@@ -55,10 +56,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
   constexpr int NQ = D / 16;              // MFMA k-steps over the head dim
   constexpr int NDB = D / 32;             // 32-row blocks of the output's head dim
 
+  // one array per ring stage, so the compiler can tell which direct-to-LDS loads a read depends on
   __shared__ __attribute__((aligned(1024))) uint16_t Ks0[kBC * D];
   __shared__ __attribute__((aligned(1024))) uint16_t Vs0[kBC * D];
   __shared__ __attribute__((aligned(1024))) uint16_t Ks1[kBC * D];
   __shared__ __attribute__((aligned(1024))) uint16_t Vs1[kBC * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Ks2[kBC * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vs2[kBC * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -106,6 +110,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
     }
 #pragma unroll
     for (int kk = 0; kk < NQ; ++kk) qreg[kk] = as_bf16x8(raw[kk]);
+    retire_vmem();  // from here on only the tile loads count in vmcnt (they complete in order)
   }
 
   f32x16 o[NDB];
@@ -160,8 +165,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < LPW; ++r) {
         const int slot = w * LPW + r;
-        load_lds16(kbase + tbase + loff[r], kdst + slot * 512);
-        load_lds16(vbase + tbase + loff[r], vdst + slot * 512);
+        load_lds16_async<false>(kbase + tbase + loff[r], kdst + slot * 512);
+        load_lds16_async<false>(vbase + tbase + loff[r], vdst + slot * 512);
       }
     } else {  // last, partial tile: rows past the end re-read row S-1 (finite data, masked)
 #pragma unroll
@@ -170,99 +175,87 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(
         const int row = slot * RPL + lane / CH;
         const int key = min(jt * kBC + row, S - 1);
         const long long off = (long long)key * kv_stride + swz<CH>(lane % CH, row) * 8;
-        load_lds16(kbase + off, kdst + slot * 512);
-        load_lds16(vbase + off, vdst + slot * 512);
+        load_lds16_async<false>(kbase + off, kdst + slot * 512);
+        load_lds16_async<false>(vbase + off, vdst + slot * 512);
       }
     }
   };
 
   auto compute_tile = [&](int jt, const uint16_t* Kt, const uint16_t* Vt) {
-    const int key0 = jt * kBC;
-    // blocks of 32 keys: active unless past the sequence or entirely above this wave's diagonal
-    const bool act0 = !causal || key0 <= wp0 + 31;
-    const bool act1 = key0 + 32 < S && (!causal || key0 + 32 <= wp0 + 31);
-    f32x16 sacc[2];
-    if (act0) {
-      sacc[0] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(Kt + koff[0]), qreg[0], f32x16{});
+    const int kb0 = jt * kBC;
+    // skip the block when it lies entirely above this wave's diagonal
+    if (causal && kb0 > wp0 + 31) return;
+    f32x16 sv = mfma32x32x16(*reinterpret_cast<const bf16x8*>(Kt + koff[0]), qreg[0], f32x16{});
 #pragma unroll
-      for (int kk = 1; kk < NQ; ++kk)
-        sacc[0] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(Kt + koff[kk]), qreg[kk], sacc[0]);
+    for (int kk = 1; kk < NQ; ++kk) sv = mfma32x32x16(*reinterpret_cast<const bf16x8*>(Kt + koff[kk]), qreg[kk], sv);
+    // ---- mask (only on blocks crossing the diagonal or the sequence end) ----
+    if ((causal && kb0 + 31 > wp0) || kb0 + 32 > S) {
+      const int lim = (causal ? min(p, S - 1) : S - 1) - kb0 - hh * 4;  // keys with offset > lim are out
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if ((i >> 2) * 8 + (i & 3) > lim) sv[i] = -INFINITY;
     }
-    if (act1) {
-      const uint16_t* K1 = Kt + 32 * D;
-      sacc[1] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(K1 + koff[0]), qreg[0], f32x16{});
+    float mt = sv[0];
 #pragma unroll
-      for (int kk = 1; kk < NQ; ++kk)
-        sacc[1] = mfma32x32x16(*reinterpret_cast<const bf16x8*>(K1 + koff[kk]), qreg[kk], sacc[1]);
+    for (int i = 1; i < 16; ++i) mt = fmaxf(mt, sv[i]);
+    mt = pair_max32(mt);
+    const float m_new = fmaxf(m, mt * c);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m - m_use);
+    m = m_new;
+    uint32_t pk[2][4];
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      const float e0 = fast_exp2(fmaf(sv[i], c, -m_use));
+      const float e1 = fast_exp2(fmaf(sv[i + 1], c, -m_use));
+      psum += e0 + e1;
+      pk[i >> 3][(i & 7) >> 1] = pack_bf16x2(e0, e1);
+    }
+    lsum = fmaf(lsum, alpha, psum);
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
     }
 
+    // ---- O^T += V^T P^T over this block's 32 keys ----
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (!(kb == 0 ? act0 : act1)) continue;
-      const int kb0 = key0 + kb * 32;
-      f32x16 sv = sacc[kb];
-      // ---- mask (only on blocks crossing the diagonal or the sequence end) ----
-      if ((causal && kb0 + 31 > wp0) || kb0 + 32 > S) {
-        const int lim = (causal ? min(p, S - 1) : S - 1) - kb0 - hh * 4;  // keys with offset > lim are out
+    for (int s = 0; s < 2; ++s) {
+      const bf16x8 bop = __builtin_bit_cast(bf16x8, U4{pk[s][0], pk[s][1], pk[s][2], pk[s][3]});
+      const uint16_t* Vb = Vt + 16 * s * D;
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if ((i >> 2) * 8 + (i & 3) > lim) sv[i] = -INFINITY;
-      }
-      float mt = sv[0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mt = fmaxf(mt, sv[i]);
-      mt = pair_max32(mt);
-      const float m_new = fmaxf(m, mt * c);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m - m_use);
-      m = m_new;
-      uint32_t pk[2][4];
-      float psum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const float e0 = fast_exp2(fmaf(sv[i], c, -m_use));
-        const float e1 = fast_exp2(fmaf(sv[i + 1], c, -m_use));
-        psum += e0 + e1;
-        pk[i >> 3][(i & 7) >> 1] = pack_bf16x2(e0, e1);
-      }
-      lsum = fmaf(lsum, alpha, psum);
-      if (__ballot(alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-      }
-
-      // ---- O^T += V^T P^T over this block's 32 keys ----
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const bf16x8 bop = __builtin_bit_cast(bf16x8, U4{pk[s][0], pk[s][1], pk[s][2], pk[s][3]});
-        const uint16_t* Vb = Vt + (kb * 32 + 16 * s) * D;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const uint2 lo = lds_read_tr16(Vb + voff_par[db & 1] + vimm(0, db));
-          const uint2 hi = lds_read_tr16(Vb + voff_par[db & 1] + vimm(1, db));
-          const bf16x8 aop = __builtin_bit_cast(bf16x8, U4{lo.x, lo.y, hi.x, hi.y});
-          o[db] = mfma32x32x16(aop, bop, o[db]);
-        }
+      for (int db = 0; db < NDB; ++db) {
+        const uint2 lo = lds_read_tr16(Vb + voff_par[db & 1] + vimm(0, db));
+        const uint2 hi = lds_read_tr16(Vb + voff_par[db & 1] + vimm(1, db));
+        const bf16x8 aop = __builtin_bit_cast(bf16x8, U4{lo.x, lo.y, hi.x, hi.y});
+        o[db] = mfma32x32x16(aop, bop, o[db]);
       }
     }
   };
 
+  // ---- ring of kStages tiles: wait for this wave's loads of tile jt (those of tile jt+1 may
+  // fly), then a barrier makes every wave's part of the tile visible. A load past the last tile
+  // re-reads the last one into a stage that is never read again, so every step issues the same
+  // loads and each wait keeps one fixed count (the compiler's own waits stay exact as well). ----
   issue_tile(0, Ks0, Vs0);
-  wait_vmem();
-  __syncthreads();
-  for (int jt = 0; jt < n_tiles; jt += 2) {
-    if (jt + 1 < n_tiles) issue_tile(jt + 1, Ks1, Vs1);
-    compute_tile(jt, Ks0, Vs0);
-    wait_vmem();
-    __syncthreads();
+  issue_tile(min(1, n_tiles - 1), Ks1, Vs1);
+  auto step = [&](int jt, const uint16_t* Kt, const uint16_t* Vt, uint16_t* kn, uint16_t* vn) {
+    wait_vmem_n<2 * LPW>();
+    barrier_only();
+    issue_tile(min(jt + 2, n_tiles - 1), kn, vn);
+    compute_tile(jt, Kt, Vt);
+  };
+  for (int jt = 0; jt < n_tiles; jt += 3) {
+    step(jt, Ks0, Vs0, Ks2, Vs2);
     if (jt + 1 >= n_tiles) break;
-    if (jt + 2 < n_tiles) issue_tile(jt + 2, Ks0, Vs0);
-    compute_tile(jt + 1, Ks1, Vs1);
-    wait_vmem();
-    __syncthreads();
+    step(jt + 1, Ks1, Vs1, Ks0, Vs0);
+    if (jt + 2 >= n_tiles) break;
+    step(jt + 2, Ks2, Vs2, Ks1, Vs1);
   }
+
+  wait_vmem();  // the re-read past the last tile must land before the work-group's LDS is released
 
   // ---- epilogue: O / l, round to bf16, store BSHD ----
   const float inv = 1.f / pair_sum32(lsum);
