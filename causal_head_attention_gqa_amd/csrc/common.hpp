@@ -108,6 +108,13 @@ __device__ __forceinline__ void load_lds16_async(const void* gptr, const void* l
     asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(lds_addr) : "memory");
 }
 
+// The same load with a wave-uniform base in SGPRs and a 32-bit per-lane byte offset: the
+// address needs no vector arithmetic per load.
+__device__ __forceinline__ void load_lds16_async_sv(const void* sbase, uint32_t voff, const void* lds_base) {
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
+}
+
 // Work-group barrier without the memory fences of __syncthreads(): for tiles filled by
 // load_lds16_async after an explicit vmcnt wait, where the fence's wait for every outstanding
 // load (including later stages still in flight) is not wanted.

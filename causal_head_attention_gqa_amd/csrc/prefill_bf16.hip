@@ -32,6 +32,7 @@ namespace attn {
 namespace {
 constexpr int kBC = 32;     // keys per tile (one 32x32 score block per wave)
 constexpr int kStages = 3;  // LDS ring depth: tiles j+1 and j+2 load while tile j is computed
+constexpr float kSlack = 8.f;  // log2 units: how far a row max may exceed the softmax reference max
 constexpr int kThreads = 256;
 
 // Physical 16-byte chunk of logical chunk c in tile row `row` (CH chunks per row). The XOR key
@@ -165,8 +166,8 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < LPW; ++r) {
         const int slot = w * LPW + r;
-        load_lds16_async<false>(kbase + tbase + loff[r], kdst + slot * 512);
-        load_lds16_async<false>(vbase + tbase + loff[r], vdst + slot * 512);
+        load_lds16_async_sv(kbase + tbase, 2u * (uint32_t)loff[r], kdst + slot * 512);
+        load_lds16_async_sv(vbase + tbase, 2u * (uint32_t)loff[r], vdst + slot * 512);
       }
     } else {  // last, partial tile: rows past the end re-read row S-1 (finite data, masked)
 #pragma unroll
@@ -199,9 +200,14 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_bf16_kernel(
 #pragma unroll
     for (int i = 1; i < 16; ++i) mt = fmaxf(mt, sv[i]);
     mt = pair_max32(mt);
-    const float m_new = fmaxf(m, mt * c);
+    // Lazy reference max: the exponentials use m, which moves only when this block's max exceeds it
+    // by more than kSlack (p then stays below 2^kSlack; O / l is unchanged), so rescaling the
+    // accumulator is rare.
+    const float mb = mt * c;
+    const bool move = mb > m + kSlack;  // also true on the first live block (m = -inf)
+    const float m_new = move ? mb : m;
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m - m_use);
+    const float alpha = move ? fast_exp2(m - m_use) : 1.f;
     m = m_new;
     uint32_t pk[2][4];
     float psum = 0.f;
