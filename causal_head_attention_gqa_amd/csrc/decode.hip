@@ -175,9 +175,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     }
     float mt = fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3]));
     mt = rows_max4(mt);
-    const float m_new = fmaxf(m, mt * a.scale_log2);
+    // lazy reference max (moves only when a head's max grows by more than 2^8; see prefill)
+    const float mb = mt * a.scale_log2;
+    const bool move = mb > m + 8.f;
+    const float m_new = move ? mb : m;
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m - m_use);
+    const float alpha = move ? fast_exp2(m - m_use) : 1.f;
     m = m_new;
     float pe[4];
 #pragma unroll

@@ -151,9 +151,12 @@ __global__ __launch_bounds__(NW * 64, (NW >= 8 ? 2 : 1)) void decode_mla_kernel(
     float mt = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3]));
     mt = fmaxf(mt, fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
     mt = rows_max(mt);
-    const float m_new = fmaxf(m, mt * a.scale_log2);
+    // lazy reference max (moves only when a head's max grows by more than 2^8; see prefill)
+    const float mb = mt * a.scale_log2;
+    const bool move = mb > m + 8.f;
+    const float m_new = move ? mb : m;
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m - m_use);
+    const float alpha = move ? fast_exp2(m - m_use) : 1.f;
     m = m_new;
     uint32_t pk[4];
     float psum = 0.f;
