@@ -11,6 +11,7 @@ from .attention import (  # noqa: F401
     head_attention,
     kv_head_of,
     prefill,
+    prefill_chunk,
     prefill_rows,
     rope_angles,
     rope_inv_freq,

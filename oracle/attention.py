@@ -152,6 +152,42 @@ def prefill(q, k, v, *, causal: bool = True, scale: float | None = None, rope_th
 
 
 # ---------------------------------------------------------------------------------------------
+# Prefill against a KV cache: a chunk of new tokens after a cached prefix ([P3] §九, [P4] slide 07)
+# ---------------------------------------------------------------------------------------------
+def prefill_chunk(q, k, v, q_start, *, causal: bool = True, scale: float | None = None,
+                  rope_theta: float = 0.0) -> np.ndarray:
+    """Output [B, S, Nh, Dv] of S new queries per sequence that follow q_start[b] cached tokens.
+
+    q [B, S, Nh, D]: query s of sequence b has absolute position q_start[b] + s.
+    k, v [B, T, Nkv, D]: the sequence's keys/values at positions 0 .. T-1 (un-rotated);
+    positions 0 .. q_start[b]+S-1 are used, i.e. the chunk's own K/V are appended before the
+    queries attend ([P3] §九: concat to the cache, then attend).
+    Reading (the pages only draw square masks, [P1] §3.1): the causal rule "no key after the
+    query" is applied in absolute positions, so the query at position p sees keys 0 .. p; the
+    chunk's last query sees every key (the mask is the square one's bottom-right block).
+    RoPE, when rope_theta > 0, rotates q and k at their absolute positions ([P1] §4).
+    """
+    B, S, Nh, D = q.shape
+    Nkv = k.shape[2]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    out = np.empty((B, S, Nh, v.shape[3]), dtype=np.float64)
+    for b in range(B):
+        n = int(q_start[b]) + S
+        pos = int(q_start[b]) + np.arange(S)
+        for h in range(Nh):
+            g = kv_head_of(h, Nh, Nkv)
+            qh = _f64(q[b:b + 1, :, h:h + 1, :])
+            kh = _f64(k[b:b + 1, :n, g:g + 1, :])
+            if rope_theta > 0:
+                qh = rope_rotate(qh, pos, rope_theta)
+                kh = rope_rotate(kh, np.arange(n), rope_theta)
+            mask = causal_mask(pos, n) if causal else None
+            out[b, :, h, :] = head_attention(qh[0, :, 0, :], kh[0, :, 0, :], v[b, :n, g, :], scale, mask)
+    return out
+
+
+# ---------------------------------------------------------------------------------------------
 # KV-cache decode ([P2] §13.2, [P3] §九) and the MLA-absorbed form ([P4] slide 06)
 # ---------------------------------------------------------------------------------------------
 def decode(q, kcache, vcache, ctx_lens, *, scale: float | None = None, rope_theta: float = 0.0) -> np.ndarray:

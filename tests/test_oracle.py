@@ -308,3 +308,41 @@ def test_prefill_flop_count():
     assert accounting.prefill_flops(4, 8192, 32, 128, causal=True) == 2_199_291_691_008
     assert accounting.prefill_flops(8, 1024, 12, 64, causal=True) == 12_897_484_800
     assert accounting.prefill_flops(1, 3, 1, 4, causal=False) == 4 * 4 * 9
+
+
+# ------------------------------------------------------------------ prefill against a cache --
+@pytest.mark.parametrize("rope", [0.0, 1e4])
+def test_prefill_chunk_equals_rows_of_the_full_prefill(rope):
+    """Chunks after a cached prefix reproduce the matching rows of the whole-sequence prefill
+    (absolute positions for the mask and for RoPE): a chunk masked or rotated with local
+    positions fails this."""
+    rng = np.random.default_rng(21)
+    B, T, Nh, Nkv, D = 2, 37, 4, 2, 8
+    q, k, v = _rand(rng, B, T, Nh, D), _rand(rng, B, T, Nkv, D), _rand(rng, B, T, Nkv, D)
+    full = oracle.prefill(q, k, v, rope_theta=rope)
+    for off, S in [(0, 37), (0, 5), (11, 9), (30, 7), (36, 1)]:
+        got = oracle.prefill_chunk(q[:, off:off + S], k, v, [off] * B, rope_theta=rope)
+        np.testing.assert_allclose(got, full[:, off:off + S], rtol=1e-12, atol=1e-13)
+
+
+def test_prefill_chunk_single_token_is_decode():
+    """A one-token chunk at position p is the decode step with p+1 cached keys."""
+    rng = np.random.default_rng(22)
+    B, T, Nh, Nkv, D = 3, 20, 4, 1, 8
+    q, k, v = _rand(rng, B, 1, Nh, D), _rand(rng, B, T, Nkv, D), _rand(rng, B, T, Nkv, D)
+    start = np.array([0, 7, 19])
+    got = oracle.prefill_chunk(q, k, v, start, rope_theta=5e5)[:, 0]
+    krot = oracle.rope_rotate(k, np.arange(T), 5e5)
+    want = oracle.decode(q[:, 0], krot, v, start + 1, rope_theta=5e5)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+
+
+def test_prefill_chunk_non_causal_sees_the_whole_prefix():
+    """Without the mask every query sees keys 0 .. q_start+S-1: the last chunk of a non-causal
+    prefill equals those rows of the full non-causal prefill."""
+    rng = np.random.default_rng(23)
+    B, T, Nh, Nkv, D = 1, 24, 2, 2, 8
+    q, k, v = _rand(rng, B, T, Nh, D), _rand(rng, B, T, Nkv, D), _rand(rng, B, T, Nkv, D)
+    full = oracle.prefill(q, k, v, causal=False)
+    got = oracle.prefill_chunk(q[:, 16:], k, v, [16], causal=False)
+    np.testing.assert_allclose(got, full[:, 16:], rtol=1e-12, atol=1e-13)
