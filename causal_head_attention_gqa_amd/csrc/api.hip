@@ -125,6 +125,11 @@ int attn_prefill(const void* q, const void* k, const void* v, void* out, int B, 
   a.D = Dh;
   a.scale_log2 = (float)(sc * 1.4426950408889634);
   a.causal = causal ? 1 : 0;
+  a.kv_tok = (long long)Nkv * Dh;
+  a.kv_batch = (long long)S * Nkv * Dh;
+  a.kv_head = Dh;
+  a.q_start = nullptr;
+  a.max_keys = S;
 
   if (rope) {
     float2* table = static_cast<float2*>(workspace);
@@ -144,6 +149,74 @@ int attn_prefill(const void* q, const void* k, const void* v, void* out, int B, 
   }
   const hipError_t e = dtype == ATTN_BF16 ? launch_prefill_bf16(a, st) : launch_prefill_f32(a, st);
   return hip_status(e);
+}
+
+size_t attn_prefill_cached_workspace_bytes(int max_ctx, int Dh, float rope_theta) {
+  if (!(rope_theta > 0.f) || max_ctx <= 0 || Dh <= 0) return 0;
+  return align_up((size_t)max_ctx * (size_t)(Dh / 2) * sizeof(float2));
+}
+
+int attn_prefill_cached(const void* q, const void* kcache, const void* vcache, const int32_t* q_start, void* out,
+                        int B, int S, int Nh, int Nkv, int Dh, int max_ctx, long long ld, float rope_theta,
+                        int causal, float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || S < 0 || Nh <= 0 || Nkv <= 0 || Dh <= 0 || max_ctx <= 0) return ATTN_ERR_INVALID;
+  if (Nh % Nkv != 0 || S > max_ctx || ld < Dh || ld % 8 != 0) return ATTN_ERR_INVALID;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVALID;
+  if (!std::isfinite(rope_theta) || !std::isfinite(scale)) return ATTN_ERR_INVALID;
+  if (dtype != ATTN_BF16 || (Dh != 64 && Dh != 128)) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)B * max_ctx * Nkv * ld > (1LL << 40) || (long long)Nkv * ld * 32 > 0x7fffffffLL)
+    return ATTN_ERR_INVALID;
+  if (B == 0 || S == 0) return ATTN_OK;
+  if (!q || !kcache || !vcache || !q_start || !out) return ATTN_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned16(out)) return ATTN_ERR_INVALID;
+  const size_t need = attn_prefill_cached_workspace_bytes(max_ctx, Dh, rope_theta);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
+    return ATTN_ERR_WORKSPACE;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const double sc = scale > 0.f ? (double)scale : 1.0 / std::sqrt((double)Dh);
+  PrefillArgs a{};
+  a.q = q;
+  a.k = kcache;
+  a.v = vcache;
+  a.out = out;
+  a.table = nullptr;
+  a.B = B;
+  a.S = S;
+  a.Nh = Nh;
+  a.Nkv = Nkv;
+  a.D = Dh;
+  a.scale_log2 = (float)(sc * 1.4426950408889634);
+  a.causal = causal ? 1 : 0;
+  a.kv_tok = (long long)Nkv * ld;
+  a.kv_batch = (long long)max_ctx * Nkv * ld;
+  a.kv_head = (int)ld;
+  a.q_start = q_start;
+  a.max_keys = max_ctx;
+  if (rope_theta > 0.f) {
+    float2* table = static_cast<float2*>(workspace);
+    const hipError_t e = launch_rope_table(table, max_ctx, Dh, (double)rope_theta, st);
+    if (e != hipSuccess) return hip_status(e);
+    a.table = table;
+  }
+  return hip_status(launch_prefill_bf16(a, st));
+}
+
+int attn_kv_append(const void* k_new, const void* v_new, void* kcache, void* vcache, const int32_t* start, int B,
+                   int S, int Nkv, int Dh, int max_ctx, long long ldk, long long ldv, float rope_theta,
+                   int interleaved, int dtype, void* stream) {
+  if (B < 0 || S < 0 || Nkv <= 0 || Dh <= 0 || max_ctx <= 0 || S > max_ctx) return ATTN_ERR_INVALID;
+  if (ldk < Dh || ldv < Dh) return ATTN_ERR_INVALID;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVALID;
+  if (!std::isfinite(rope_theta)) return ATTN_ERR_INVALID;
+  if (dtype != ATTN_BF16 || Dh % 16 != 0 || Dh > 1024) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)B * max_ctx * Nkv * (ldk > ldv ? ldk : ldv) > (1LL << 40)) return ATTN_ERR_INVALID;
+  if (B == 0 || S == 0) return ATTN_OK;
+  if (!k_new || !v_new || !kcache || !vcache || !start) return ATTN_ERR_INVALID;
+  return hip_status(launch_kv_append(static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                                     static_cast<uint16_t*>(kcache), static_cast<uint16_t*>(vcache), start, B, S,
+                                     Nkv, Dh, max_ctx, ldk, ldv, (double)rope_theta, interleaved,
+                                     static_cast<hipStream_t>(stream)));
 }
 
 size_t attn_decode_workspace_bytes(int B, int Nh, int Nkv, int Dqk, int Dv, int max_ctx, int dtype) {

@@ -28,6 +28,9 @@ hipError_t launch_rope_rotate_table(const T* src, T* dst, const float2* table, l
 template <typename T>
 hipError_t launch_rope_apply(T* x, const int* positions, long long rows, int S, int N, int D, double theta,
                              int interleaved, hipStream_t st);
+hipError_t launch_kv_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* kc, uint16_t* vc,
+                            const int* start, int B, int S, int Nkv, int D, int max_ctx, long long ldk, long long ldv,
+                            double theta, int interleaved, hipStream_t st);
 
 // ---- Prefill (prefill_f32.hip, prefill_bf16.hip) ----
 struct PrefillArgs {
@@ -39,6 +42,11 @@ struct PrefillArgs {
   int B, S, Nh, Nkv, D;
   float scale_log2;  // softmax scale * log2(e)
   int causal;
+  // K/V addressing (bf16 path): element (b, t, g, d) at b*kv_batch + t*kv_tok + g*kv_head + d
+  long long kv_tok, kv_batch;
+  int kv_head;
+  const int* q_start;  // device [B]: absolute position of query 0 of each sequence, or nullptr (0)
+  int max_keys;        // keys available per sequence (q_start[b] + S is clamped to it)
 };
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t st);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st);

@@ -49,7 +49,8 @@ template <int D, int HPW>
 __global__ __launch_bounds__(kThreads, 3) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ out, const float2* __restrict__ table, int B, int S, int Nh, int Nkv, float c,
-    int causal, int n_ptiles) {
+    int causal, int n_ptiles, long long kv_tok, long long kv_batch, int kv_head, const int* __restrict__ q_start,
+    int max_keys) {
   constexpr int BP = 32 * (4 / HPW);      // query positions per work-group
   constexpr int CH = D / 8;               // 16-byte chunks per row
   constexpr int RPL = 64 / CH;            // rows per 1 KiB load instruction
@@ -76,6 +77,10 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_bf16_kernel(
   const int h0 = (bh % HGn) * HPW;
   const int g = h0 / (Nh / Nkv);
   const int p0 = pt * BP;
+  // queries sit at absolute positions off .. off+S-1 and see keys 0 .. Sk-1 (off = 0: plain prefill;
+  // a chunk of a longer sequence otherwise, with the causal mask aligned to the last key)
+  const int off = q_start ? min(max(q_start[b], 0), max_keys - S) : 0;
+  const int Sk = off + S;
   const int h = h0 + (w % HPW);
   const int wp0 = p0 + (w / HPW) * 32;  // wave's first query position (scalar)
   const int col = lane & 31, hh = lane >> 5;
@@ -90,7 +95,7 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_bf16_kernel(
 #pragma unroll
       for (int kk = 0; kk < NQ; ++kk) raw[kk] = ldg16(qp + kk * 16);
       if (table) {
-        const float2* tb = table + (long long)p * (D / 2) + hh * 8;
+        const float2* tb = table + (long long)(off + p) * (D / 2) + hh * 8;
 #pragma unroll
         for (int kk = 0; kk < NQ / 2; ++kk) {
           uint32_t* pa = &raw[kk].x;
@@ -121,17 +126,16 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_bf16_kernel(
   float lsum = 0.f;     // running sum over the keys this lane holds
 
   // ---- per-lane global source offsets of the tile loads (row r of a tile, swizzled chunk) ----
-  const long long kv_stride = (long long)Nkv * D;
-  const uint16_t* kbase = k + ((long long)b * S * Nkv + g) * D;
-  const uint16_t* vbase = v + ((long long)b * S * Nkv + g) * D;
+  const uint16_t* kbase = k + (long long)b * kv_batch + (long long)g * kv_head;
+  const uint16_t* vbase = v + (long long)b * kv_batch + (long long)g * kv_head;
   // (offsets within one 64-row tile stay far below 2^31 elements)
   int loff[LPW];
 #pragma unroll
   for (int r = 0; r < LPW; ++r) {
     const int row = (w * LPW + r) * RPL + lane / CH;
-    loff[r] = row * (int)kv_stride + swz<CH>(lane % CH, row) * 8;
+    loff[r] = row * (int)kv_tok + swz<CH>(lane % CH, row) * 8;
   }
-  const long long tile_step = kBC * kv_stride;
+  const long long tile_step = kBC * kv_tok;
 
   // ---- per-lane LDS read offsets (elements), identical for every tile ----
   // K operand: row kb*32 + col, logical chunk 2*kk + hh; the swizzle only sees the row's low 4 bits.
@@ -157,27 +161,27 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_bf16_kernel(
     return dbase + t * (8 * D + tshift);
   };
 
-  const int last = causal ? min(S, p0 + BP) : S;
+  const int last = causal ? min(Sk, off + p0 + BP) : Sk;
   const int n_tiles = (last + kBC - 1) / kBC;
 
   auto issue_tile = [&](int jt, uint16_t* kdst, uint16_t* vdst) {
     const long long tbase = (long long)jt * tile_step;
-    if (jt * kBC + kBC <= S) {
+    if (jt * kBC + kBC <= Sk) {
 #pragma unroll
       for (int r = 0; r < LPW; ++r) {
         const int slot = w * LPW + r;
         load_lds16_async_sv(kbase + tbase, 2u * (uint32_t)loff[r], kdst + slot * 512);
         load_lds16_async_sv(vbase + tbase, 2u * (uint32_t)loff[r], vdst + slot * 512);
       }
-    } else {  // last, partial tile: rows past the end re-read row S-1 (finite data, masked)
+    } else {  // last, partial tile: rows past the end re-read row Sk-1 (finite data, masked)
 #pragma unroll
       for (int r = 0; r < LPW; ++r) {
         const int slot = w * LPW + r;
         const int row = slot * RPL + lane / CH;
-        const int key = min(jt * kBC + row, S - 1);
-        const long long off = (long long)key * kv_stride + swz<CH>(lane % CH, row) * 8;
-        load_lds16_async<false>(kbase + off, kdst + slot * 512);
-        load_lds16_async<false>(vbase + off, vdst + slot * 512);
+        const int key = min(jt * kBC + row, Sk - 1);
+        const long long ro = (long long)key * kv_tok + swz<CH>(lane % CH, row) * 8;
+        load_lds16_async<false>(kbase + ro, kdst + slot * 512);
+        load_lds16_async<false>(vbase + ro, vdst + slot * 512);
       }
     }
   };
@@ -185,13 +189,13 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_bf16_kernel(
   auto compute_tile = [&](int jt, const uint16_t* Kt, const uint16_t* Vt) {
     const int kb0 = jt * kBC;
     // skip the block when it lies entirely above this wave's diagonal
-    if (causal && kb0 > wp0 + 31) return;
+    if (causal && kb0 > off + wp0 + 31) return;
     f32x16 sv = mfma32x32x16(*reinterpret_cast<const bf16x8*>(Kt + koff[0]), qreg[0], f32x16{});
 #pragma unroll
     for (int kk = 1; kk < NQ; ++kk) sv = mfma32x32x16(*reinterpret_cast<const bf16x8*>(Kt + koff[kk]), qreg[kk], sv);
     // ---- mask (only on blocks crossing the diagonal or the sequence end) ----
-    if ((causal && kb0 + 31 > wp0) || kb0 + 32 > S) {
-      const int lim = (causal ? min(p, S - 1) : S - 1) - kb0 - hh * 4;  // keys with offset > lim are out
+    if ((causal && kb0 + 31 > off + wp0) || kb0 + 32 > Sk) {
+      const int lim = (causal ? min(off + p, Sk - 1) : Sk - 1) - kb0 - hh * 4;  // keys with offset > lim are out
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         if ((i >> 2) * 8 + (i & 3) > lim) sv[i] = -INFINITY;
@@ -286,7 +290,8 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t st) {
   if (n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   prefill_bf16_kernel<D, HPW><<<dim3((unsigned)n_wg), dim3(kThreads), 0, st>>>(
       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
-      static_cast<uint16_t*>(a.out), a.table, a.B, a.S, a.Nh, a.Nkv, a.scale_log2, a.causal, n_ptiles);
+      static_cast<uint16_t*>(a.out), a.table, a.B, a.S, a.Nh, a.Nkv, a.scale_log2, a.causal, n_ptiles, a.kv_tok,
+      a.kv_batch, a.kv_head, a.q_start, a.max_keys);
   return hipGetLastError();
 }
 

@@ -10,16 +10,25 @@
 
 namespace attn {
 
+// (cos, sin) of position * theta_i: fp64 angle, one rounding to fp32. The angle table and the
+// fused cache append both use this, so a key rotated by either carries identical bits.
+__device__ __forceinline__ float2 rope_cs(int pos, int i, double neg2_log2theta_over_d) {
+  const double inv_freq = exp2(neg2_log2theta_over_d * (double)i);
+  double s, c;
+  sincos((double)pos * inv_freq, &s, &c);
+  return make_float2((float)c, (float)s);
+}
+
+// Rotation of the pair (a, b) by (cos, sin) in fp32 with fixed fused-multiply-add rounding.
+__device__ __forceinline__ float2 rope_rot(float a, float b, float2 cs) {
+  return make_float2(fmaf(a, cs.x, -(b * cs.y)), fmaf(a, cs.y, b * cs.x));
+}
+
 // table[pos * half + i] = (cos(pos * theta_i), sin(pos * theta_i)), fp64 angle, fp32 result.
 __global__ void rope_table_kernel(float2* __restrict__ table, int S, int half, double neg2_log2theta_over_d) {
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (long long)S * half) return;
-  const int pos = (int)(idx / half);
-  const int i = (int)(idx % half);
-  const double inv_freq = exp2(neg2_log2theta_over_d * (double)i);
-  double s, c;
-  sincos((double)pos * inv_freq, &s, &c);
-  table[idx] = make_float2((float)c, (float)s);
+  table[idx] = rope_cs((int)(idx / half), (int)(idx % half), neg2_log2theta_over_d);
 }
 
 // Rotates half-split pairs of src [rows, D] (row r has position (r / N) % S) into dst with the
@@ -45,11 +54,9 @@ __global__ void rope_rotate_table_kernel(const T* __restrict__ src, T* __restric
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float2 cs = tb[e];
-    const float ra = a[e] * cs.x - b[e] * cs.y;
-    const float rb = a[e] * cs.y + b[e] * cs.x;
-    y[i0 + e] = from_f32<T>(ra);
-    y[i0 + D / 2 + e] = from_f32<T>(rb);
+    const float2 r = rope_rot(a[e], b[e], tb[e]);
+    y[i0 + e] = from_f32<T>(r.x);
+    y[i0 + D / 2 + e] = from_f32<T>(r.y);
   }
 }
 
@@ -75,6 +82,61 @@ __global__ void rope_apply_kernel(T* __restrict__ x, const int* __restrict__ pos
   const double b = (double)to_f32(p[ib]);
   p[ia] = from_f32<T>((float)(a * c - b * s));
   p[ib] = from_f32<T>((float)(a * s + b * c));
+}
+
+// KV-cache append with RoPE fused ("Transformer 架构完全深度解析" §九: new K/V are concatenated to
+// the cache; K is rotated at its absolute position first, "2.7 ..." §4). Token s of sequence b goes
+// to cache row t = start[b] + s (clamped to max_ctx - S). One thread per (token, KV head, group of
+// 8 pairs): rotates 8 half-split (or adjacent) pairs of K with rope_cs/rope_rot and copies the
+// matching 16 elements of V.
+__global__ void kv_append_kernel(const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+                                 uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
+                                 const int* __restrict__ start, int B, int S, int Nkv, int D, int max_ctx,
+                                 long long ldk, long long ldv, double neg2_log2theta_over_d, int rope,
+                                 int interleaved) {
+  const int groups = D / 16;
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long long)B * S * Nkv * groups) return;
+  const int gi = (int)(idx % groups);
+  const long long row = idx / groups;  // (b * S + s) * Nkv + g
+  const int g = (int)(row % Nkv);
+  const long long tok = row / Nkv;
+  const int s = (int)(tok % S);
+  const int b = (int)(tok / S);
+  const int t = min(max(start[b], 0), max_ctx - S) + s;
+  const uint16_t* kx = k_new + row * D;
+  const uint16_t* vx = v_new + row * D;
+  uint16_t* ky = kc + ((long long)b * max_ctx + t) * Nkv * ldk + (long long)g * ldk;
+  uint16_t* vy = vc + ((long long)b * max_ctx + t) * Nkv * ldv + (long long)g * ldv;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int i = gi * 8 + e;  // pair index
+    const int ia = interleaved ? 2 * i : i;
+    const int ib = interleaved ? 2 * i + 1 : i + D / 2;
+    float a = bf16_to_f32(kx[ia]), bb = bf16_to_f32(kx[ib]);
+    if (rope) {
+      const float2 r = rope_rot(a, bb, rope_cs(t, i, neg2_log2theta_over_d));
+      a = r.x;
+      bb = r.y;
+    }
+    ky[ia] = f32_to_bf16(a);
+    ky[ib] = f32_to_bf16(bb);
+    vy[ia] = vx[ia];
+    vy[ib] = vx[ib];
+  }
+}
+
+hipError_t launch_kv_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* kc, uint16_t* vc,
+                            const int* start, int B, int S, int Nkv, int D, int max_ctx, long long ldk, long long ldv,
+                            double theta, int interleaved, hipStream_t st) {
+  const long long n = (long long)B * S * Nkv * (D / 16);
+  if (n == 0) return hipSuccess;
+  const bool rope = theta > 0.0;
+  const double k = rope ? -2.0 * log2(theta) / (double)D : 0.0;
+  kv_append_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(k_new, v_new, kc, vc, start, B, S, Nkv, D,
+                                                                           max_ctx, ldk, ldv, k, rope ? 1 : 0,
+                                                                           interleaved ? 1 : 0);
+  return hipGetLastError();
 }
 
 hipError_t launch_rope_table(float2* table, int S, int D, double theta, hipStream_t st) {

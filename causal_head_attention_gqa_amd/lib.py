@@ -23,6 +23,9 @@ EXPORTS = (
     "attn_decode_workspace_bytes",
     "attn_decode",
     "rope_apply",
+    "attn_prefill_cached_workspace_bytes",
+    "attn_prefill_cached",
+    "attn_kv_append",
 )
 
 _lib = None
@@ -57,6 +60,14 @@ def load() -> ctypes.CDLL:
                                 c_float, c_float, c_int, c_vp, c_size, c_vp]
     lib.rope_apply.restype = c_int
     lib.rope_apply.argtypes = [c_vp, c_vp, c_int, c_int, c_int, c_int, c_float, c_int, c_int, c_vp]
+    lib.attn_prefill_cached_workspace_bytes.restype = c_size
+    lib.attn_prefill_cached_workspace_bytes.argtypes = [c_int, c_int, c_float]
+    lib.attn_prefill_cached.restype = c_int
+    lib.attn_prefill_cached.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_int, c_ll,
+                                        c_float, c_int, c_float, c_int, c_vp, c_size, c_vp]
+    lib.attn_kv_append.restype = c_int
+    lib.attn_kv_append.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_ll, c_ll,
+                                   c_float, c_int, c_int, c_vp]
     _lib = lib
     return lib
 
@@ -184,3 +195,68 @@ def rope_apply_(x, *, theta: float, positions=None, interleaved: bool = False):
                            _dtype_code(x), _stream_ptr(x.device))
     _check(st, "rope_apply")
     return x
+
+
+def _cache_dims(t):
+    """[B, max_ctx, Nkv, row] cache view -> (B, max_ctx, Nkv, row pitch in elements)."""
+    if not t.is_cuda:
+        raise ValueError("caches must live on the GPU")
+    B_, T_, N_, _ = t.shape
+    if t.stride(3) != 1 or t.stride(1) != N_ * t.stride(2) or t.stride(0) != T_ * t.stride(1):
+        raise ValueError("cache must be [B, max_ctx, Nkv, row] with a dense row pitch")
+    return B_, T_, N_, t.stride(2)
+
+
+def prefill_cached_workspace_bytes(max_ctx: int, Dh: int, rope_theta: float) -> int:
+    return int(load().attn_prefill_cached_workspace_bytes(max_ctx, Dh, float(rope_theta)))
+
+
+def prefill_cached(q, kcache, vcache, q_start, *, rope_theta: float = 0.0, causal: bool = True,
+                   scale: float | None = None, out=None, workspace=None):
+    """Chunked prefill: q [B, S, Nh, Dh] at absolute positions q_start[b] + s against the cached
+    keys 0 .. q_start[b]+S-1 (already appended). kcache/vcache [B, max_ctx, Nkv, row] with the
+    same row pitch; q_start int32 [B] on the GPU. Returns out [B, S, Nh, Dh]."""
+    torch = _torch()
+    _need_cuda(q, q_start)
+    B, S, Nh, Dh = q.shape
+    Bk, max_ctx, Nkv, ld = _cache_dims(kcache)
+    if _cache_dims(vcache) != (Bk, max_ctx, Nkv, ld) or Bk != B:
+        raise ValueError("kcache and vcache must share shape and row pitch with q's batch")
+    if kcache.shape[3] < Dh or vcache.shape[3] < Dh:
+        raise ValueError("cache rows shorter than the head dim")
+    if q_start.dtype != torch.int32 or q_start.shape != (B,):
+        raise ValueError("q_start must be int32 [B]")
+    if out is None:
+        out = torch.empty_like(q)
+    need = prefill_cached_workspace_bytes(max_ctx, Dh, rope_theta)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load().attn_prefill_cached(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), q_start.data_ptr(),
+                                    out.data_ptr(), B, S, Nh, Nkv, Dh, max_ctx, ld, float(rope_theta),
+                                    1 if causal else 0, float(scale or 0.0), _dtype_code(q), ws_ptr, ws_bytes,
+                                    _stream_ptr(q.device))
+    _check(st, "attn_prefill_cached")
+    return out
+
+
+def kv_append(k_new, v_new, kcache, vcache, start, *, rope_theta: float = 0.0, interleaved: bool = False):
+    """Write k_new/v_new [B, S, Nkv, Dh] into the caches at rows start[b] .. start[b]+S-1,
+    rotating K at those positions when rope_theta > 0. start: int32 [B] on the GPU."""
+    torch = _torch()
+    _need_cuda(k_new, v_new, start)
+    B, S, Nkv, Dh = k_new.shape
+    if v_new.shape != k_new.shape:
+        raise ValueError("k_new and v_new must have the same shape")
+    Bk, max_ctx, Nk, ldk = _cache_dims(kcache)
+    Bv, max_v, Nv, ldv = _cache_dims(vcache)
+    if (Bk, Nk) != (B, Nkv) or (Bv, max_v, Nv) != (B, max_ctx, Nkv):
+        raise ValueError("cache shapes disagree with k_new")
+    if start.dtype != torch.int32 or start.shape != (B,):
+        raise ValueError("start must be int32 [B]")
+    st = load().attn_kv_append(k_new.data_ptr(), v_new.data_ptr(), kcache.data_ptr(), vcache.data_ptr(),
+                               start.data_ptr(), B, S, Nkv, Dh, max_ctx, ldk, ldv, float(rope_theta),
+                               1 if interleaved else 0, _dtype_code(k_new), _stream_ptr(k_new.device))
+    _check(st, "attn_kv_append")
+    return kcache, vcache

@@ -77,6 +77,55 @@ int attn_prefill(const void* q, const void* k, const void* v, void* out,
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * Prefill with a KV cache (chunked prefill): S new query tokens of each sequence attend to the
+ * cached keys, their own included. "Transformer 架构完全深度解析" §九 (new K/V are appended to
+ * the cache, then the new queries attend to all of it); "Transformer 与 LLM：结构、实现与算量"
+ * slide 07 (a long prompt is prefilled in chunks so one request does not hold the GPU).
+ *
+ * q        [B, S, Nh, Dh]                    read only; query s of sequence b has absolute
+ *          position q_start[b] + s
+ * kcache   element (b, t, g, d) at ((b * max_ctx + t) * Nkv + g) * ld + d    (ld = row pitch)
+ * vcache   same layout and pitch as kcache; rows 0 .. q_start[b] + S - 1 must hold the
+ *          sequence's keys/values, already rotated when RoPE is used (attn_kv_append does both)
+ * q_start  device int32 [B]: tokens already in the cache before this chunk. A value outside
+ *          [0, max_ctx - S] is clamped into it for memory safety (the result is then not
+ *          meaningful).
+ * out      [B, S, Nh, Dh]                    written
+ * causal != 0: the query at position p attends keys 0 .. p (the square causal mask shifted so
+ *          that the chunk's last query sees the last key); causal == 0: all q_start[b] + S keys.
+ * rope_theta > 0 rotates q (half-split pairs, as attn_prefill) at its absolute position; the
+ *          cached keys are used as stored. scale <= 0 selects 1 / sqrt(Dh).
+ * Supported: ATTN_BF16, Dh in {64, 128}, 1 <= S <= max_ctx, ld % 8 == 0, ld >= Dh.
+ * workspace: at least attn_prefill_cached_workspace_bytes(...) bytes (the RoPE angle table).
+ * With q_start[b] = 0 and S = max_ctx this is exactly attn_prefill on the cached keys.
+ * ------------------------------------------------------------------------------------------ */
+size_t attn_prefill_cached_workspace_bytes(int max_ctx, int Dh, float rope_theta);
+
+int attn_prefill_cached(const void* q, const void* kcache, const void* vcache, const int32_t* q_start,
+                        void* out, int B, int S, int Nh, int Nkv, int Dh, int max_ctx, long long ld,
+                        float rope_theta, int causal, float scale, int dtype,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------
+ * KV-cache append with RoPE fused: writes S new tokens of each sequence into the caches at rows
+ * start[b] .. start[b] + S - 1, rotating K at those absolute positions.
+ *   "Transformer 架构完全深度解析" §九 (concat of the new K/V to the cache), "2.7 ..." §4 and
+ *   "Transformer 架构快速入门" §8.2-8.3 (RoPE on K: frequency theta^(-2i/Dh), fp64 angle,
+ *   cos/sin rounded once to fp32, rotation in fp32, one rounding to bf16).
+ *
+ * k_new, v_new [B, S, Nkv, Dh]  read only
+ * kcache, vcache: layout of attn_prefill_cached / attn_decode (pitches ldk, ldv), written only
+ *          at the appended rows. start: device int32 [B], clamped to [0, max_ctx - S].
+ * rope_theta > 0 rotates K (interleaved == 0: pairs (i, i + Dh/2); != 0: pairs (2i, 2i + 1));
+ *          rope_theta <= 0 copies K unchanged. V is copied unchanged.
+ * Supported: ATTN_BF16, Dh % 16 == 0 and Dh <= 1024, 1 <= S <= max_ctx.
+ * A key appended here and a key rotated by attn_prefill's RoPE step carry identical bits.
+ * ------------------------------------------------------------------------------------------ */
+int attn_kv_append(const void* k_new, const void* v_new, void* kcache, void* vcache, const int32_t* start,
+                   int B, int S, int Nkv, int Dh, int max_ctx, long long ldk, long long ldv,
+                   float rope_theta, int interleaved, int dtype, void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * KV-cache decode: one new query token per sequence attends to every cached key of its head.
  *   "Transformer 架构完全深度解析" §九 (append new K/V, then attend the new query to the cache),
  *   "Transformer 与 LLM：结构、实现与算量" slide 06 (absorbed MLA = MQA over one shared row).

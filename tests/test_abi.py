@@ -26,7 +26,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     fns = declared_functions()
     for name in ("attn_prefill", "attn_decode", "rope_apply", "attn_prefill_workspace_bytes",
-                 "attn_decode_workspace_bytes", "attn_status_str"):
+                 "attn_decode_workspace_bytes", "attn_status_str", "attn_prefill_cached",
+                 "attn_prefill_cached_workspace_bytes", "attn_kv_append"):
         assert name in fns
 
 
@@ -102,3 +103,45 @@ def test_workspace_queries():
     assert lib.prefill_workspace_bytes(4, 8192, 8, 128, 5e5, 1) == 8192 * 64 * 8 + 4 * 8192 * 8 * 128 * 2
     ws = lib.decode_workspace_bytes(64, 32, 8, 128, 128, 8192, 1)
     assert ws > 0 and ws % 256 == 0
+
+
+def test_prefill_cached_argument_errors():
+    L = _lib()
+    def call(**kw):
+        return L.attn_prefill_cached(kw.get("q", P), kw.get("kc", P), kw.get("vc", P), kw.get("st", P),
+                                     kw.get("o", P), kw.get("B", 2), kw.get("S", 16), kw.get("Nh", 8),
+                                     kw.get("Nkv", 2), kw.get("Dh", 128), kw.get("T", 100), kw.get("ld", 128),
+                                     kw.get("rope", 0.0), 1, 0.0, kw.get("dt", 1), kw.get("ws", None),
+                                     kw.get("wsb", 0), None)
+    assert call(S=101) == 1                     # chunk longer than the cache
+    assert call(ld=64) == 1                     # row pitch shorter than the head dim
+    assert call(ld=132) == 1                    # rows not 16-byte aligned
+    assert call(Nh=6, Nkv=4) == 1
+    assert call(Dh=96, ld=96) == 2
+    assert call(dt=0) == 2                      # bf16 only
+    assert call(st=None) == 1
+    assert call(rope=5e5) == 3                  # the angle table needs a workspace
+    assert call(B=0) == 0 and call(S=0) == 0
+
+
+def test_kv_append_argument_errors():
+    L = _lib()
+    def call(**kw):
+        return L.attn_kv_append(kw.get("k", P), kw.get("v", P), kw.get("kc", P), kw.get("vc", P), kw.get("st", P),
+                                kw.get("B", 2), kw.get("S", 16), kw.get("Nkv", 2), kw.get("Dh", 128),
+                                kw.get("T", 100), kw.get("ldk", 128), kw.get("ldv", 128), kw.get("rope", 1e4), 0,
+                                kw.get("dt", 1), None)
+    assert call(S=101) == 1
+    assert call(ldv=100) == 1
+    assert call(Dh=72, ldk=72, ldv=72) == 2     # head dim not a multiple of 16
+    assert call(dt=0) == 2
+    assert call(st=None) == 1
+    assert call(rope=float("inf")) == 1
+    assert call(B=0) == 0
+
+
+def test_prefill_cached_workspace_query():
+    from causal_head_attention_gqa_amd import lib
+    _lib()
+    assert lib.prefill_cached_workspace_bytes(8192, 128, 0.0) == 0
+    assert lib.prefill_cached_workspace_bytes(8192, 128, 5e5) == 8192 * 64 * 8

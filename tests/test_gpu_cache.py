@@ -1,0 +1,117 @@
+"""KV-cache append (RoPE fused) and prefill against the cache (chunked prefill) on the GPU.
+
+Parity against the oracle (fp64, tolerance BF16_TOL): the appended rows against the oracle's
+RoPE at absolute positions; a chunk after a cached prefix against oracle.prefill_chunk.
+Consistency inside the library: prefilling a sequence chunk by chunk through the cache gives
+bit-for-bit the rows of the single whole-sequence prefill (same rotated keys, same 32-key
+blocks in the same order).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import BF16_TOL, max_abs, to_dev, values
+
+pytestmark = pytest.mark.gpu
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _bits(t):
+    return t.view(_torch().int16).cpu().numpy()
+
+
+def _empty_cache(B, T, Nkv, D, ld=None, fill=0x3F80):
+    """bf16 cache [B, T, Nkv, ld] filled with a sentinel (1.0), returned as its [..., :D] view."""
+    torch = _torch()
+    ld = ld or D
+    c = torch.full((B, T, Nkv, ld), fill, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    return c[..., :D], c
+
+
+@pytest.mark.parametrize("D,interleaved,rope", [(128, False, 5e5), (64, True, 1e4), (128, False, 0.0)])
+def test_kv_append_rotates_and_places(D, interleaved, rope):
+    import causal_head_attention_gqa_amd as attn
+    torch = _torch()
+    B, S, Nkv, T = 2, 37, 2, 100
+    start = np.array([0, 50], np.int32)
+    kn = synth.normal(800 + D, 0, (B, S, Nkv, D), "bf16")
+    vn = synth.normal(800 + D, 1, (B, S, Nkv, D), "bf16")
+    kc, kc_full = _empty_cache(B, T, Nkv, D, ld=D + 8)
+    vc, _ = _empty_cache(B, T, Nkv, D)
+    attn.kv_append(to_dev(kn, "bf16"), to_dev(vn, "bf16"), kc, vc, torch.as_tensor(start, device="cuda"),
+                   rope_theta=rope, interleaved=interleaved)
+    kh = kc.float().cpu().numpy()
+    vh = _bits(vc)
+    for b in range(B):
+        rows = slice(start[b], start[b] + S)
+        want = values(kn[b:b + 1], "bf16")
+        if rope > 0:
+            want = oracle.rope_rotate(want, start[b] + np.arange(S), rope, interleaved=interleaved)
+        assert max_abs(kh[b, rows], want[0]) <= BF16_TOL
+        if rope == 0:
+            assert np.array_equal(_bits(kc[b, rows].contiguous()), kn[b].view(np.int16))
+        assert np.array_equal(vh[b, rows], vn[b].view(np.int16))
+        others = np.ones(T, bool)
+        others[rows] = False
+        assert np.all(kh[b, others] == 1.0) and np.all(vh[b, others] == 0x3F80)
+    # the row padding beyond D is never written
+    assert np.all(kc_full[..., D:].float().cpu().numpy() == 1.0)
+
+
+CHUNK_CASES = [
+    # B, S, Nh, Nkv, D, T, starts, rope, causal
+    (2, 33, 8, 2, 128, 128, [0, 45], 5e5, True),
+    (2, 70, 4, 4, 64, 200, [130, 3], 0.0, True),
+    (3, 1, 8, 1, 128, 64, [0, 17, 63], 1e4, True),
+    (1, 40, 4, 2, 128, 96, [56], 0.0, False),
+]
+
+
+@pytest.mark.parametrize("case", CHUNK_CASES, ids=lambda c: "S%dH%dK%dD%d" % c[1:5])
+def test_prefill_cached_matches_oracle(case):
+    import causal_head_attention_gqa_amd as attn
+    torch = _torch()
+    B, S, Nh, Nkv, D, T, starts, rope, causal = case
+    wid = 820 + S
+    starts = np.asarray(starts, np.int32)
+    k_all = synth.normal(wid, 1, (B, T, Nkv, D), "bf16")
+    v_all = synth.normal(wid, 2, (B, T, Nkv, D), "bf16")
+    q = synth.normal(wid, 0, (B, S, Nh, D), "bf16")
+    kc, _ = _empty_cache(B, T, Nkv, D)
+    vc, _ = _empty_cache(B, T, Nkv, D)
+    # fill each sequence's first start+S rows through the append kernel (rotated keys)
+    n_max = int((starts + S).max())
+    zeros = torch.zeros(B, dtype=torch.int32, device="cuda")
+    attn.kv_append(to_dev(k_all[:, :n_max], "bf16"), to_dev(v_all[:, :n_max], "bf16"), kc, vc, zeros,
+                   rope_theta=rope)
+    got = attn.prefill_cached(to_dev(q, "bf16"), kc, vc, torch.as_tensor(starts, device="cuda"),
+                              rope_theta=rope, causal=causal).float().cpu().numpy()
+    want = oracle.prefill_chunk(values(q, "bf16"), values(k_all, "bf16"), values(v_all, "bf16"), starts,
+                                causal=causal, rope_theta=rope)
+    assert max_abs(got, want) <= BF16_TOL
+
+
+@pytest.mark.parametrize("chunks,rope", [([64, 100, 93], 5e5), ([1, 31, 32, 33, 160], 0.0)])
+def test_chunked_prefill_is_bitwise_the_full_prefill(chunks, rope):
+    import causal_head_attention_gqa_amd as attn
+    torch = _torch()
+    B, Nh, Nkv, D = 2, 8, 2, 128
+    T = sum(chunks)
+    q = to_dev(synth.normal(840, 0, (B, T, Nh, D), "bf16"), "bf16")
+    k = to_dev(synth.normal(840, 1, (B, T, Nkv, D), "bf16"), "bf16")
+    v = to_dev(synth.normal(840, 2, (B, T, Nkv, D), "bf16"), "bf16")
+    full = attn.prefill(q, k, v, rope_theta=rope)
+    kc, _ = _empty_cache(B, T, Nkv, D)
+    vc, _ = _empty_cache(B, T, Nkv, D)
+    outs, s0 = [], 0
+    for n in chunks:
+        st = torch.full((B,), s0, dtype=torch.int32, device="cuda")
+        attn.kv_append(k[:, s0:s0 + n].contiguous(), v[:, s0:s0 + n].contiguous(), kc, vc, st, rope_theta=rope)
+        outs.append(attn.prefill_cached(q[:, s0:s0 + n].contiguous(), kc, vc, st, rope_theta=rope))
+        s0 += n
+    assert np.array_equal(_bits(torch.cat(outs, dim=1)), _bits(full))
