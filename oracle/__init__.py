@@ -17,4 +17,5 @@ from .attention import (  # noqa: F401
     rope_inv_freq,
     rope_rotate,
     softmax_rows,
+    window_mask,
 )

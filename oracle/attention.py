@@ -87,6 +87,17 @@ def causal_mask(q_positions, n_keys: int) -> np.ndarray:
     return np.where(j[None, :] > np.asarray(q_positions)[:, None], -np.inf, 0.0)
 
 
+def window_mask(q_positions, n_keys: int, window: int, sinks: int = 0) -> np.ndarray:
+    """Causal sliding-window mask with attention sinks ([P4] slide 07: a window of W keys, plus the
+    first few tokens kept). Reading: the query at position p sees keys p-W+1 .. p (its own key
+    included, W keys at most) and the sink keys 0 .. sinks-1; every other key is masked with -inf.
+    """
+    j = np.arange(n_keys)[None, :]
+    p = np.asarray(q_positions)[:, None]
+    hidden = (j > p) | ((j < p - window + 1) & (j >= sinks))
+    return np.where(hidden, -np.inf, 0.0)
+
+
 def softmax_rows(s: np.ndarray) -> np.ndarray:
     """Row softmax over the key axis ([P2] §4.4, [P3] §五 step 4): exp(s - max) / sum."""
     m = np.max(s, axis=-1, keepdims=True)
@@ -155,7 +166,7 @@ def prefill(q, k, v, *, causal: bool = True, scale: float | None = None, rope_th
 # Prefill against a KV cache: a chunk of new tokens after a cached prefix ([P3] §九, [P4] slide 07)
 # ---------------------------------------------------------------------------------------------
 def prefill_chunk(q, k, v, q_start, *, causal: bool = True, scale: float | None = None,
-                  rope_theta: float = 0.0) -> np.ndarray:
+                  rope_theta: float = 0.0, window: int = 0, sinks: int = 0) -> np.ndarray:
     """Output [B, S, Nh, Dv] of S new queries per sequence that follow q_start[b] cached tokens.
 
     q [B, S, Nh, D]: query s of sequence b has absolute position q_start[b] + s.
@@ -166,6 +177,7 @@ def prefill_chunk(q, k, v, q_start, *, causal: bool = True, scale: float | None 
     query" is applied in absolute positions, so the query at position p sees keys 0 .. p; the
     chunk's last query sees every key (the mask is the square one's bottom-right block).
     RoPE, when rope_theta > 0, rotates q and k at their absolute positions ([P1] §4).
+    window > 0 (with causal) replaces the causal mask by window_mask(..., window, sinks).
     """
     B, S, Nh, D = q.shape
     Nkv = k.shape[2]
@@ -182,7 +194,10 @@ def prefill_chunk(q, k, v, q_start, *, causal: bool = True, scale: float | None 
             if rope_theta > 0:
                 qh = rope_rotate(qh, pos, rope_theta)
                 kh = rope_rotate(kh, np.arange(n), rope_theta)
-            mask = causal_mask(pos, n) if causal else None
+            if window > 0:
+                mask = window_mask(pos, n, window, sinks)
+            else:
+                mask = causal_mask(pos, n) if causal else None
             out[b, :, h, :] = head_attention(qh[0, :, 0, :], kh[0, :, 0, :], v[b, :n, g, :], scale, mask)
     return out
 

@@ -346,3 +346,35 @@ def test_prefill_chunk_non_causal_sees_the_whole_prefix():
     full = oracle.prefill(q, k, v, causal=False)
     got = oracle.prefill_chunk(q[:, 16:], k, v, [16], causal=False)
     np.testing.assert_allclose(got, full[:, 16:], rtol=1e-12, atol=1e-13)
+
+
+# ------------------------------------------------------------ sliding window + attention sinks --
+def test_window_sink_visibility_matches_hand_table(golden):
+    """W = 3, one sink, six tokens: the hand-written visibility table of the rule."""
+    table = np.array([[int(x) for x in row] for row in golden("window_sink_visibility_s6_w3_k1.txt")])
+    vis = (oracle.window_mask(np.arange(6), 6, 3, 1) == 0).astype(int)
+    assert np.array_equal(vis, table)
+
+
+def test_window_of_one_returns_own_value():
+    """W = 1 without sinks: every query sees only its own key, so the output row is v_p exactly."""
+    rng = np.random.default_rng(31)
+    B, T, Nh, Nkv, D = 1, 12, 2, 1, 8
+    q, k, v = _rand(rng, B, T, Nh, D), _rand(rng, B, T, Nkv, D), _rand(rng, B, T, Nkv, D)
+    got = oracle.prefill_chunk(q, k, v, [0], window=1)
+    for h in range(Nh):
+        np.testing.assert_array_equal(got[0, :, h], v[0, :, 0])
+
+
+@pytest.mark.parametrize("window,sinks", [(40, 0), (12, 40), (5, 12)])
+def test_wide_window_or_all_sinks_is_causal(window, sinks):
+    """A window covering the whole prefix, or sinks covering it, leaves the causal mask; a narrow
+    window differs from it (the mask is not a no-op)."""
+    rng = np.random.default_rng(32)
+    B, T, Nh, Nkv, D = 2, 12, 2, 2, 8
+    q, k, v = _rand(rng, B, T, Nh, D), _rand(rng, B, T, Nkv, D), _rand(rng, B, T, Nkv, D)
+    full = oracle.prefill(q, k, v)
+    got = oracle.prefill_chunk(q, k, v, [0, 0], window=window, sinks=sinks)
+    np.testing.assert_allclose(got, full, rtol=1e-12, atol=1e-13)
+    narrow = oracle.prefill_chunk(q, k, v, [0, 0], window=3, sinks=1)
+    assert np.abs(narrow - full).max() > 1e-3
