@@ -130,6 +130,8 @@ int attn_prefill(const void* q, const void* k, const void* v, void* out, int B, 
   a.kv_head = Dh;
   a.q_start = nullptr;
   a.max_keys = S;
+  a.window = 0;
+  a.sinks = 0;
 
   if (rope) {
     float2* table = static_cast<float2*>(workspace);
@@ -158,8 +160,10 @@ size_t attn_prefill_cached_workspace_bytes(int max_ctx, int Dh, float rope_theta
 
 int attn_prefill_cached(const void* q, const void* kcache, const void* vcache, const int32_t* q_start, void* out,
                         int B, int S, int Nh, int Nkv, int Dh, int max_ctx, long long ld, float rope_theta,
-                        int causal, float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+                        int causal, int window, int sinks, float scale, int dtype, void* workspace,
+                        size_t workspace_bytes, void* stream) {
   if (B < 0 || S < 0 || Nh <= 0 || Nkv <= 0 || Dh <= 0 || max_ctx <= 0) return ATTN_ERR_INVALID;
+  if (window < 0 || sinks < 0 || (window > 0 && !causal) || (window == 0 && sinks > 0)) return ATTN_ERR_INVALID;
   if (Nh % Nkv != 0 || S > max_ctx || ld < Dh || ld % 8 != 0) return ATTN_ERR_INVALID;
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVALID;
   if (!std::isfinite(rope_theta) || !std::isfinite(scale)) return ATTN_ERR_INVALID;
@@ -193,6 +197,8 @@ int attn_prefill_cached(const void* q, const void* kcache, const void* vcache, c
   a.kv_head = (int)ld;
   a.q_start = q_start;
   a.max_keys = max_ctx;
+  a.window = window;
+  a.sinks = sinks;
   if (rope_theta > 0.f) {
     float2* table = static_cast<float2*>(workspace);
     const hipError_t e = launch_rope_table(table, max_ctx, Dh, (double)rope_theta, st);

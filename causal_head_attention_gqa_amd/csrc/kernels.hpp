@@ -47,6 +47,8 @@ struct PrefillArgs {
   int kv_head;
   const int* q_start;  // device [B]: absolute position of query 0 of each sequence, or nullptr (0)
   int max_keys;        // keys available per sequence (q_start[b] + S is clamped to it)
+  int window;          // > 0: a query at position p sees keys p-window+1 .. p only (plus the sinks)
+  int sinks;           // with a window: keys 0 .. sinks-1 stay visible to every later query
 };
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t st);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st);

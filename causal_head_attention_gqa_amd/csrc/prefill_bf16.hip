@@ -45,12 +45,14 @@ __device__ __forceinline__ int swz(int c, int row) {
   return c ^ key;
 }
 
-template <int D, int HPW>
+// kCache: queries start at q_start[b] (a chunk against a cache); kWin: sliding window + sinks.
+// Both are compile-time switches so that the whole-sequence prefill carries none of their code.
+template <int D, int HPW, bool kCache, bool kWin>
 __global__ __launch_bounds__(kThreads, 3) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ out, const float2* __restrict__ table, int B, int S, int Nh, int Nkv, float c,
     int causal, int n_ptiles, long long kv_tok, long long kv_batch, int kv_head, const int* __restrict__ q_start,
-    int max_keys) {
+    int max_keys, int window, int sinks) {
   constexpr int BP = 32 * (4 / HPW);      // query positions per work-group
   constexpr int CH = D / 8;               // 16-byte chunks per row
   constexpr int RPL = 64 / CH;            // rows per 1 KiB load instruction
@@ -79,7 +81,7 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_bf16_kernel(
   const int p0 = pt * BP;
   // queries sit at absolute positions off .. off+S-1 and see keys 0 .. Sk-1 (off = 0: plain prefill;
   // a chunk of a longer sequence otherwise, with the causal mask aligned to the last key)
-  const int off = q_start ? min(max(q_start[b], 0), max_keys - S) : 0;
+  const int off = kCache ? min(max(q_start[b], 0), max_keys - S) : 0;
   const int Sk = off + S;
   const int h = h0 + (w % HPW);
   const int wp0 = p0 + (w / HPW) * 32;  // wave's first query position (scalar)
@@ -163,6 +165,15 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_bf16_kernel(
 
   const int last = causal ? min(Sk, off + p0 + BP) : Sk;
   const int n_tiles = (last + kBC - 1) / kBC;
+  // Key tiles visited: with a sliding window, the sink tiles 0 .. ns-1 and then the tiles from the
+  // work-group's earliest window start w0 on; without one, every tile (ns = w0 = 0).
+  int ns = 0, w0 = 0;
+  if (kWin) {
+    w0 = max(off + p0 - window + 1, 0) / kBC;
+    ns = min((sinks + kBC - 1) / kBC, w0);
+  }
+  const int n_vt = ns + (n_tiles - w0);
+  auto tile_of = [&](int vt) { return vt < ns ? vt : w0 + (vt - ns); };
 
   auto issue_tile = [&](int jt, uint16_t* kdst, uint16_t* vdst) {
     const long long tbase = (long long)jt * tile_step;
@@ -188,17 +199,24 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_bf16_kernel(
 
   auto compute_tile = [&](int jt, const uint16_t* Kt, const uint16_t* Vt) {
     const int kb0 = jt * kBC;
-    // skip the block when it lies entirely above this wave's diagonal
+    // skip the block when it lies entirely above this wave's diagonal, or entirely before every
+    // row's window and past the sinks
     if (causal && kb0 > off + wp0 + 31) return;
+    if (kWin && kb0 + 31 < off + wp0 - window + 1 && kb0 >= sinks) return;
     f32x16 sv = mfma32x32x16(*reinterpret_cast<const bf16x8*>(Kt + koff[0]), qreg[0], f32x16{});
 #pragma unroll
     for (int kk = 1; kk < NQ; ++kk) sv = mfma32x32x16(*reinterpret_cast<const bf16x8*>(Kt + koff[kk]), qreg[kk], sv);
     // ---- mask (only on blocks crossing the diagonal or the sequence end) ----
-    if ((causal && kb0 + 31 > off + wp0) || kb0 + 32 > Sk) {
-      const int lim = (causal ? min(off + p, Sk - 1) : Sk - 1) - kb0 - hh * 4;  // keys with offset > lim are out
+    if ((causal && kb0 + 31 > off + wp0) || kb0 + 32 > Sk || (kWin && kb0 < off + wp0 + 32 - window)) {
+      const int base = kb0 + hh * 4;  // key of this lane's score offset 0
+      const int hi = (causal ? min(off + p, Sk - 1) : Sk - 1) - base;  // offsets above: after the query
+      const int lo = kWin ? off + p - window + 1 - base : -64;  // offsets below: before the window
+      const int sk = sinks - base;                                    // offsets below: sinks (kept)
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if ((i >> 2) * 8 + (i & 3) > lim) sv[i] = -INFINITY;
+      for (int i = 0; i < 16; ++i) {
+        const int o = (i >> 2) * 8 + (i & 3);
+        if (o > hi || (o < lo && o >= sk)) sv[i] = -INFINITY;
+      }
     }
     float mt = sv[0];
 #pragma unroll
@@ -249,19 +267,19 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_bf16_kernel(
   // fly), then a barrier makes every wave's part of the tile visible. A load past the last tile
   // re-reads the last one into a stage that is never read again, so every step issues the same
   // loads and each wait keeps one fixed count (the compiler's own waits stay exact as well). ----
-  issue_tile(0, Ks0, Vs0);
-  issue_tile(min(1, n_tiles - 1), Ks1, Vs1);
+  issue_tile(tile_of(0), Ks0, Vs0);
+  issue_tile(tile_of(min(1, n_vt - 1)), Ks1, Vs1);
   auto step = [&](int jt, const uint16_t* Kt, const uint16_t* Vt, uint16_t* kn, uint16_t* vn) {
     wait_vmem_n<2 * LPW>();
     barrier_only();
-    issue_tile(min(jt + 2, n_tiles - 1), kn, vn);
-    compute_tile(jt, Kt, Vt);
+    issue_tile(tile_of(min(jt + 2, n_vt - 1)), kn, vn);
+    compute_tile(tile_of(jt), Kt, Vt);
   };
-  for (int jt = 0; jt < n_tiles; jt += 3) {
+  for (int jt = 0; jt < n_vt; jt += 3) {
     step(jt, Ks0, Vs0, Ks2, Vs2);
-    if (jt + 1 >= n_tiles) break;
+    if (jt + 1 >= n_vt) break;
     step(jt + 1, Ks1, Vs1, Ks0, Vs0);
-    if (jt + 2 >= n_tiles) break;
+    if (jt + 2 >= n_vt) break;
     step(jt + 2, Ks2, Vs2, Ks1, Vs1);
   }
 
@@ -282,25 +300,32 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_bf16_kernel(
   }
 }
 
-template <int D, int HPW>
+template <int D, int HPW, bool kCache, bool kWin>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t st) {
   constexpr int BP = 32 * (4 / HPW);
   const int n_ptiles = (a.S + BP - 1) / BP;
   const long long n_wg = (long long)n_ptiles * a.B * (a.Nh / HPW);
   if (n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  prefill_bf16_kernel<D, HPW><<<dim3((unsigned)n_wg), dim3(kThreads), 0, st>>>(
+  prefill_bf16_kernel<D, HPW, kCache, kWin><<<dim3((unsigned)n_wg), dim3(kThreads), 0, st>>>(
       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
       static_cast<uint16_t*>(a.out), a.table, a.B, a.S, a.Nh, a.Nkv, a.scale_log2, a.causal, n_ptiles, a.kv_tok,
-      a.kv_batch, a.kv_head, a.q_start, a.max_keys);
+      a.kv_batch, a.kv_head, a.q_start, a.max_keys, a.window, a.sinks);
   return hipGetLastError();
+}
+
+template <int D, int HPW>
+hipError_t launch_m(const PrefillArgs& a, hipStream_t st) {
+  if (a.window > 0) return launch_t<D, HPW, true, true>(a, st);  // windows come through the cache entry point
+  if (a.q_start) return launch_t<D, HPW, true, false>(a, st);
+  return launch_t<D, HPW, false, false>(a, st);
 }
 
 template <int D>
 hipError_t launch_d(const PrefillArgs& a, hipStream_t st) {
   const int G = a.Nh / a.Nkv;
-  if (G % 4 == 0) return launch_t<D, 4>(a, st);
-  if (G % 2 == 0) return launch_t<D, 2>(a, st);
-  return launch_t<D, 1>(a, st);
+  if (G % 4 == 0) return launch_m<D, 4>(a, st);
+  if (G % 2 == 0) return launch_m<D, 2>(a, st);
+  return launch_m<D, 1>(a, st);
 }
 }  // namespace
 

@@ -64,7 +64,7 @@ def load() -> ctypes.CDLL:
     lib.attn_prefill_cached_workspace_bytes.argtypes = [c_int, c_int, c_float]
     lib.attn_prefill_cached.restype = c_int
     lib.attn_prefill_cached.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_int, c_ll,
-                                        c_float, c_int, c_float, c_int, c_vp, c_size, c_vp]
+                                        c_float, c_int, c_int, c_int, c_float, c_int, c_vp, c_size, c_vp]
     lib.attn_kv_append.restype = c_int
     lib.attn_kv_append.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_ll, c_ll,
                                    c_float, c_int, c_int, c_vp]
@@ -212,10 +212,11 @@ def prefill_cached_workspace_bytes(max_ctx: int, Dh: int, rope_theta: float) -> 
 
 
 def prefill_cached(q, kcache, vcache, q_start, *, rope_theta: float = 0.0, causal: bool = True,
-                   scale: float | None = None, out=None, workspace=None):
+                   window: int = 0, sinks: int = 0, scale: float | None = None, out=None, workspace=None):
     """Chunked prefill: q [B, S, Nh, Dh] at absolute positions q_start[b] + s against the cached
     keys 0 .. q_start[b]+S-1 (already appended). kcache/vcache [B, max_ctx, Nkv, row] with the
-    same row pitch; q_start int32 [B] on the GPU. Returns out [B, S, Nh, Dh]."""
+    same row pitch; q_start int32 [B] on the GPU. window > 0: sliding window of that many keys
+    plus `sinks` leading keys. Returns out [B, S, Nh, Dh]."""
     torch = _torch()
     _need_cuda(q, q_start)
     B, S, Nh, Dh = q.shape
@@ -235,7 +236,8 @@ def prefill_cached(q, kcache, vcache, q_start, *, rope_theta: float = 0.0, causa
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = load().attn_prefill_cached(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), q_start.data_ptr(),
                                     out.data_ptr(), B, S, Nh, Nkv, Dh, max_ctx, ld, float(rope_theta),
-                                    1 if causal else 0, float(scale or 0.0), _dtype_code(q), ws_ptr, ws_bytes,
+                                    1 if causal else 0, int(window), int(sinks), float(scale or 0.0),
+                                    _dtype_code(q), ws_ptr, ws_bytes,
                                     _stream_ptr(q.device))
     _check(st, "attn_prefill_cached")
     return out

@@ -93,6 +93,11 @@ int attn_prefill(const void* q, const void* k, const void* v, void* out,
  * out      [B, S, Nh, Dh]                    written
  * causal != 0: the query at position p attends keys 0 .. p (the square causal mask shifted so
  *          that the chunk's last query sees the last key); causal == 0: all q_start[b] + S keys.
+ * window > 0 (causal only): sliding window, the query at position p attends keys
+ *          max(0, p - window + 1) .. p, plus the first `sinks` keys 0 .. sinks-1 (attention sinks)
+ *          - "Transformer 与 LLM：结构、实现与算量" slide 07 (window W, e.g. 4096; sink = the first 4
+ *          tokens kept). window == 0: no window (sinks must be 0). Tiles outside every row's window
+ *          and past the sinks are neither loaded nor computed.
  * rope_theta > 0 rotates q (half-split pairs, as attn_prefill) at its absolute position; the
  *          cached keys are used as stored. scale <= 0 selects 1 / sqrt(Dh).
  * Supported: ATTN_BF16, Dh in {64, 128}, 1 <= S <= max_ctx, ld % 8 == 0, ld >= Dh.
@@ -103,7 +108,7 @@ size_t attn_prefill_cached_workspace_bytes(int max_ctx, int Dh, float rope_theta
 
 int attn_prefill_cached(const void* q, const void* kcache, const void* vcache, const int32_t* q_start,
                         void* out, int B, int S, int Nh, int Nkv, int Dh, int max_ctx, long long ld,
-                        float rope_theta, int causal, float scale, int dtype,
+                        float rope_theta, int causal, int window, int sinks, float scale, int dtype,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------

@@ -111,8 +111,8 @@ def test_prefill_cached_argument_errors():
         return L.attn_prefill_cached(kw.get("q", P), kw.get("kc", P), kw.get("vc", P), kw.get("st", P),
                                      kw.get("o", P), kw.get("B", 2), kw.get("S", 16), kw.get("Nh", 8),
                                      kw.get("Nkv", 2), kw.get("Dh", 128), kw.get("T", 100), kw.get("ld", 128),
-                                     kw.get("rope", 0.0), 1, 0.0, kw.get("dt", 1), kw.get("ws", None),
-                                     kw.get("wsb", 0), None)
+                                     kw.get("rope", 0.0), kw.get("causal", 1), kw.get("win", 0), kw.get("sinks", 0),
+                                     0.0, kw.get("dt", 1), kw.get("ws", None), kw.get("wsb", 0), None)
     assert call(S=101) == 1                     # chunk longer than the cache
     assert call(ld=64) == 1                     # row pitch shorter than the head dim
     assert call(ld=132) == 1                    # rows not 16-byte aligned
@@ -121,6 +121,9 @@ def test_prefill_cached_argument_errors():
     assert call(dt=0) == 2                      # bf16 only
     assert call(st=None) == 1
     assert call(rope=5e5) == 3                  # the angle table needs a workspace
+    assert call(win=-1) == 1
+    assert call(win=64, causal=0) == 1          # a window needs the causal mask
+    assert call(sinks=4) == 1                   # sinks only with a window
     assert call(B=0) == 0 and call(S=0) == 0
 
 

@@ -115,3 +115,35 @@ def test_chunked_prefill_is_bitwise_the_full_prefill(chunks, rope):
         outs.append(attn.prefill_cached(q[:, s0:s0 + n].contiguous(), kc, vc, st, rope_theta=rope))
         s0 += n
     assert np.array_equal(_bits(torch.cat(outs, dim=1)), _bits(full))
+
+
+WINDOW_CASES = [
+    # B, S, Nh, Nkv, D, T, starts, rope, window, sinks
+    (2, 200, 8, 2, 128, 256, [0, 56], 5e5, 64, 4),
+    (1, 96, 4, 4, 64, 300, [204], 0.0, 100, 0),
+    (2, 130, 4, 1, 128, 130, [0, 0], 1e4, 33, 40),
+    (1, 64, 4, 2, 128, 64, [0], 0.0, 1, 0),
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES, ids=lambda c: "S%dD%dW%dK%d" % (c[1], c[4], c[8], c[9]))
+def test_sliding_window_with_sinks_matches_oracle(case):
+    import causal_head_attention_gqa_amd as attn
+    torch = _torch()
+    B, S, Nh, Nkv, D, T, starts, rope, window, sinks = case
+    wid = 860 + S + window
+    starts = np.asarray(starts, np.int32)
+    k_all = synth.normal(wid, 1, (B, T, Nkv, D), "bf16")
+    v_all = synth.normal(wid, 2, (B, T, Nkv, D), "bf16")
+    q = synth.normal(wid, 0, (B, S, Nh, D), "bf16")
+    kc, _ = _empty_cache(B, T, Nkv, D)
+    vc, _ = _empty_cache(B, T, Nkv, D)
+    n_max = int((starts + S).max())
+    zeros = torch.zeros(B, dtype=torch.int32, device="cuda")
+    attn.kv_append(to_dev(k_all[:, :n_max], "bf16"), to_dev(v_all[:, :n_max], "bf16"), kc, vc, zeros,
+                   rope_theta=rope)
+    got = attn.prefill_cached(to_dev(q, "bf16"), kc, vc, torch.as_tensor(starts, device="cuda"),
+                              rope_theta=rope, window=window, sinks=sinks).float().cpu().numpy()
+    want = oracle.prefill_chunk(values(q, "bf16"), values(k_all, "bf16"), values(v_all, "bf16"), starts,
+                                rope_theta=rope, window=window, sinks=sinks)
+    assert max_abs(got, want) <= BF16_TOL
