@@ -48,7 +48,8 @@ def rope_angles(positions, head_dim: int, theta: float) -> np.ndarray:
     return _f64(positions)[..., None] * rope_inv_freq(head_dim, theta)
 
 
-def rope_rotate(x, positions, theta: float, interleaved: bool = False) -> np.ndarray:
+def rope_rotate(x, positions, theta: float, interleaved: bool = False, rot_dims: int | None = None,
+                rot_offset: int = 0) -> np.ndarray:
     """Rotate every head vector of x [B, S, N, D] by its position's angles, in fp64.
 
     positions: [S] (shared by the batch) or [B, S].
@@ -56,22 +57,29 @@ def rope_rotate(x, positions, theta: float, interleaved: bool = False) -> np.nda
         (x_i cos a - x_{i+D/2} sin a,  x_i sin a + x_{i+D/2} cos a).
     interleaved=True rotates adjacent pairs (x_{2i}, x_{2i+1}) with the same 2x2 rotation
     ([P2] §8.3, [P3] §七). [P2] §8.1 notes that either pairing works when used consistently.
+    rot_dims = D_r < D rotates only the D_r dims starting at rot_offset, with frequencies
+    base^(-2i/D_r) ([P2] §8.2: D_r is the rotary dimension, possibly a part of the head); the other
+    dims pass unchanged. Reading: the rotary span is the leading D_r dims (rot_offset = 0), or the
+    decoupled k^R / q^R block of MLA ([P4] slide 06), which sits after the 512 latent dims.
     """
     x = _f64(x)
     B, S, N, D = x.shape
+    Dr = D if rot_dims is None else int(rot_dims)
     pos = np.broadcast_to(_f64(positions), (B, S))
-    ang = rope_angles(pos, D, theta)[:, :, None, :]  # [B, S, 1, D/2]
+    ang = rope_angles(pos, Dr, theta)[:, :, None, :]  # [B, S, 1, D_r/2]
     c, s = np.cos(ang), np.sin(ang)
-    out = np.empty_like(x)
+    out = x.copy()
+    xr = x[..., rot_offset:rot_offset + Dr]
+    rr = out[..., rot_offset:rot_offset + Dr]
     if interleaved:
-        a, b = x[..., 0::2], x[..., 1::2]
-        out[..., 0::2] = a * c - b * s
-        out[..., 1::2] = a * s + b * c
+        a, b = xr[..., 0::2], xr[..., 1::2]
+        rr[..., 0::2] = a * c - b * s
+        rr[..., 1::2] = a * s + b * c
     else:
-        h = D // 2
-        a, b = x[..., :h], x[..., h:]
-        out[..., :h] = a * c - b * s
-        out[..., h:] = a * s + b * c
+        h = Dr // 2
+        a, b = xr[..., :h], xr[..., h:]
+        rr[..., :h] = a * c - b * s
+        rr[..., h:] = a * s + b * c
     return out
 
 
@@ -166,7 +174,8 @@ def prefill(q, k, v, *, causal: bool = True, scale: float | None = None, rope_th
 # Prefill against a KV cache: a chunk of new tokens after a cached prefix ([P3] §九, [P4] slide 07)
 # ---------------------------------------------------------------------------------------------
 def prefill_chunk(q, k, v, q_start, *, causal: bool = True, scale: float | None = None,
-                  rope_theta: float = 0.0, window: int = 0, sinks: int = 0) -> np.ndarray:
+                  rope_theta: float = 0.0, window: int = 0, sinks: int = 0, rope_interleaved: bool = False,
+                  rope_dims: int | None = None) -> np.ndarray:
     """Output [B, S, Nh, Dv] of S new queries per sequence that follow q_start[b] cached tokens.
 
     q [B, S, Nh, D]: query s of sequence b has absolute position q_start[b] + s.
@@ -178,6 +187,7 @@ def prefill_chunk(q, k, v, q_start, *, causal: bool = True, scale: float | None 
     chunk's last query sees every key (the mask is the square one's bottom-right block).
     RoPE, when rope_theta > 0, rotates q and k at their absolute positions ([P1] §4).
     window > 0 (with causal) replaces the causal mask by window_mask(..., window, sinks).
+    rope_interleaved / rope_dims select the pairing and the rotary dimension (see rope_rotate).
     """
     B, S, Nh, D = q.shape
     Nkv = k.shape[2]
@@ -192,8 +202,8 @@ def prefill_chunk(q, k, v, q_start, *, causal: bool = True, scale: float | None 
             qh = _f64(q[b:b + 1, :, h:h + 1, :])
             kh = _f64(k[b:b + 1, :n, g:g + 1, :])
             if rope_theta > 0:
-                qh = rope_rotate(qh, pos, rope_theta)
-                kh = rope_rotate(kh, np.arange(n), rope_theta)
+                qh = rope_rotate(qh, pos, rope_theta, rope_interleaved, rope_dims)
+                kh = rope_rotate(kh, np.arange(n), rope_theta, rope_interleaved, rope_dims)
             if window > 0:
                 mask = window_mask(pos, n, window, sinks)
             else:
@@ -213,7 +223,8 @@ def decode(q, kcache, vcache, ctx_lens, *, scale: float | None = None, rope_thet
     K/V before attending, so no mask is applied. The cache holds already-rotated keys ([P3] §七:
     cached keys carry their position); with rope_theta > 0 the query is rotated at position
     ctx_b - 1. For the MLA-absorbed form pass vcache = kcache[..., :Dv], i.e. V is the latent
-    part c^KV of the same cached row ([P4] slide 06).
+    part c^KV of the same cached row ([P4] slide 06); there RoPE touches only the decoupled q^R
+    block (the last Dqk - Dv dims, half-split pairs, frequencies base^(-2i/(Dqk - Dv))).
     Returns [B, Nh, Dv] in fp64.
     """
     B, Nh, Dqk = q.shape
@@ -228,6 +239,9 @@ def decode(q, kcache, vcache, ctx_lens, *, scale: float | None = None, rope_thet
             g = kv_head_of(h, Nh, Nkv)
             qh = _f64(q[b, h, :])[None, None, None, :]
             if rope_theta > 0:
-                qh = rope_rotate(qh, [c - 1], rope_theta)
+                if Dqk != Dv:  # MLA: decoupled RoPE block after the latent dims
+                    qh = rope_rotate(qh, [c - 1], rope_theta, rot_dims=Dqk - Dv, rot_offset=Dv)
+                else:
+                    qh = rope_rotate(qh, [c - 1], rope_theta)
             out[b, h, :] = head_attention(qh[0, 0], kcache[b, :c, g, :], vcache[b, :c, g, :], scale)[0]
     return out

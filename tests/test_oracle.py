@@ -378,3 +378,45 @@ def test_wide_window_or_all_sinks_is_causal(window, sinks):
     np.testing.assert_allclose(got, full, rtol=1e-12, atol=1e-13)
     narrow = oracle.prefill_chunk(q, k, v, [0, 0], window=3, sinks=1)
     assert np.abs(narrow - full).max() > 1e-3
+
+
+# ------------------------------------------------------------- partial and decoupled RoPE --
+def test_partial_rotary_rotates_only_its_span():
+    """rot_dims = D_r: the span is rotated exactly as a D_r-dim head (frequencies base^(-2i/D_r)),
+    the rest passes through; the full span is the default rotation."""
+    rng = np.random.default_rng(41)
+    x = _rand(rng, 2, 9, 3, 16)
+    pos = np.arange(9) * 7
+    np.testing.assert_array_equal(oracle.rope_rotate(x, pos, 1e4, rot_dims=16), oracle.rope_rotate(x, pos, 1e4))
+    for inter in (False, True):
+        got = oracle.rope_rotate(x, pos, 1e4, interleaved=inter, rot_dims=8)
+        np.testing.assert_allclose(got[..., :8], oracle.rope_rotate(x[..., :8], pos, 1e4, interleaved=inter),
+                                   rtol=0, atol=1e-14)
+        np.testing.assert_array_equal(got[..., 8:], x[..., 8:])
+        got = oracle.rope_rotate(x, pos, 1e4, interleaved=inter, rot_dims=4, rot_offset=12)
+        np.testing.assert_allclose(got[..., 12:], oracle.rope_rotate(x[..., 12:], pos, 1e4, interleaved=inter),
+                                   rtol=0, atol=1e-14)
+        np.testing.assert_array_equal(got[..., :12], x[..., :12])
+
+
+def test_mla_decoupled_rope_absorbed_equals_per_head():
+    """[P4] slide 06: RoPE acts only on the 64-dim q^R / k^R block, so it cannot be absorbed; the
+    absorbed decode with q^R rotated at ctx-1 (cache rows holding rotated k^R) equals per-head
+    attention with q^R and k^R rotated at their positions."""
+    rng = np.random.default_rng(42)
+    H, T, dc, dr, dh, theta = 4, 21, 32, 8, 16, 1e4
+    c = _rand(rng, T, dc) * 0.2
+    kr = _rand(rng, T, dr)
+    qc, qr = _rand(rng, H, dh) * 0.3, _rand(rng, H, dr)
+    w_uk, w_uv = _rand(rng, H, dh, dc) * 0.2, _rand(rng, H, dh, dc) * 0.2
+    scale = 1.0 / math.sqrt(dh + dr)
+    kr_rot = oracle.rope_rotate(kr[None, :, None, :], np.arange(T), theta)[0, :, 0]
+    qr_rot = oracle.rope_rotate(qr[None, None], [T - 1], theta)[0, 0]
+    ref = np.stack([
+        oracle.head_attention(np.concatenate([qc[h], qr_rot[h]])[None],
+                              np.concatenate([c @ w_uk[h].T, kr_rot], axis=1), c @ w_uv[h].T, scale)[0]
+        for h in range(H)])
+    q_abs = np.concatenate([np.einsum("hd,hdc->hc", qc, w_uk), qr], axis=1)[None]
+    row = np.concatenate([c, kr_rot], axis=1)[None, :, None, :]
+    lat = oracle.decode(q_abs, row, row[..., :dc], np.array([T]), scale=scale, rope_theta=theta)[0]
+    np.testing.assert_allclose(np.einsum("hdc,hc->hd", w_uv, lat), ref, rtol=1e-10, atol=1e-12)
