@@ -132,6 +132,8 @@ int attn_prefill(const void* q, const void* k, const void* v, void* out, int B, 
   a.max_keys = S;
   a.window = 0;
   a.sinks = 0;
+  a.rope_dims = Dh;
+  a.rope_inter = 0;
 
   if (rope) {
     float2* table = static_cast<float2*>(workspace);
@@ -160,14 +162,17 @@ size_t attn_prefill_cached_workspace_bytes(int max_ctx, int Dh, float rope_theta
 
 int attn_prefill_cached(const void* q, const void* kcache, const void* vcache, const int32_t* q_start, void* out,
                         int B, int S, int Nh, int Nkv, int Dh, int max_ctx, long long ld, float rope_theta,
-                        int causal, int window, int sinks, float scale, int dtype, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+                        int rope_dims, int rope_interleaved, int causal, int window, int sinks, float scale,
+                        int dtype, void* workspace, size_t workspace_bytes, void* stream) {
   if (B < 0 || S < 0 || Nh <= 0 || Nkv <= 0 || Dh <= 0 || max_ctx <= 0) return ATTN_ERR_INVALID;
   if (window < 0 || sinks < 0 || (window > 0 && !causal) || (window == 0 && sinks > 0)) return ATTN_ERR_INVALID;
+  if (rope_dims == 0) rope_dims = Dh;
+  if (rope_dims < 0 || rope_dims > Dh) return ATTN_ERR_INVALID;
   if (Nh % Nkv != 0 || S > max_ctx || ld < Dh || ld % 8 != 0) return ATTN_ERR_INVALID;
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVALID;
   if (!std::isfinite(rope_theta) || !std::isfinite(scale)) return ATTN_ERR_INVALID;
   if (dtype != ATTN_BF16 || (Dh != 64 && Dh != 128)) return ATTN_ERR_UNSUPPORTED;
+  if (rope_dims % 32 != 0) return ATTN_ERR_UNSUPPORTED;  // q is rotated in 32-dim register groups
   if ((long long)B * max_ctx * Nkv * ld > (1LL << 40) || (long long)Nkv * ld * 32 > 0x7fffffffLL)
     return ATTN_ERR_INVALID;
   if (B == 0 || S == 0) return ATTN_OK;
@@ -199,9 +204,11 @@ int attn_prefill_cached(const void* q, const void* kcache, const void* vcache, c
   a.max_keys = max_ctx;
   a.window = window;
   a.sinks = sinks;
+  a.rope_dims = rope_dims;
+  a.rope_inter = rope_interleaved ? 1 : 0;
   if (rope_theta > 0.f) {
     float2* table = static_cast<float2*>(workspace);
-    const hipError_t e = launch_rope_table(table, max_ctx, Dh, (double)rope_theta, st);
+    const hipError_t e = launch_rope_table(table, max_ctx, rope_dims, (double)rope_theta, st);
     if (e != hipSuccess) return hip_status(e);
     a.table = table;
   }
@@ -210,18 +217,20 @@ int attn_prefill_cached(const void* q, const void* kcache, const void* vcache, c
 
 int attn_kv_append(const void* k_new, const void* v_new, void* kcache, void* vcache, const int32_t* start, int B,
                    int S, int Nkv, int Dh, int max_ctx, long long ldk, long long ldv, float rope_theta,
-                   int interleaved, int dtype, void* stream) {
+                   int rope_dims, int interleaved, int dtype, void* stream) {
   if (B < 0 || S < 0 || Nkv <= 0 || Dh <= 0 || max_ctx <= 0 || S > max_ctx) return ATTN_ERR_INVALID;
+  if (rope_dims == 0) rope_dims = Dh;
+  if (rope_dims < 0 || rope_dims > Dh || rope_dims % 2 != 0) return ATTN_ERR_INVALID;
   if (ldk < Dh || ldv < Dh) return ATTN_ERR_INVALID;
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVALID;
   if (!std::isfinite(rope_theta)) return ATTN_ERR_INVALID;
-  if (dtype != ATTN_BF16 || Dh % 16 != 0 || Dh > 1024) return ATTN_ERR_UNSUPPORTED;
+  if (dtype != ATTN_BF16 || Dh % 8 != 0 || Dh > 1024) return ATTN_ERR_UNSUPPORTED;
   if ((long long)B * max_ctx * Nkv * (ldk > ldv ? ldk : ldv) > (1LL << 40)) return ATTN_ERR_INVALID;
   if (B == 0 || S == 0) return ATTN_OK;
   if (!k_new || !v_new || !kcache || !vcache || !start) return ATTN_ERR_INVALID;
   return hip_status(launch_kv_append(static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
                                      static_cast<uint16_t*>(kcache), static_cast<uint16_t*>(vcache), start, B, S,
-                                     Nkv, Dh, max_ctx, ldk, ldv, (double)rope_theta, interleaved,
+                                     Nkv, Dh, max_ctx, ldk, ldv, (double)rope_theta, rope_dims, interleaved,
                                      static_cast<hipStream_t>(stream)));
 }
 
@@ -245,7 +254,6 @@ int attn_decode(const void* q, const void* kcache, const void* vcache, const int
   const bool mla = is_mla_shape(Nkv, Dqk, Dv);
   if (mla) {
     if (vcache != kcache || ldv != ldk || Nh % 16 != 0) return ATTN_ERR_UNSUPPORTED;
-    if (rope_theta > 0.f) return ATTN_ERR_UNSUPPORTED;
   } else {
     if (Dqk != Dv || (Dqk != 64 && Dqk != 128)) return ATTN_ERR_UNSUPPORTED;
     if (Nh / Nkv > 16 && (Nh / Nkv) % 16 != 0) return ATTN_ERR_UNSUPPORTED;  // heads go in groups of 16

@@ -85,8 +85,35 @@ __global__ __launch_bounds__(NW * 64, (NW >= 8 ? 2 : 1)) void decode_mla_kernel(
   bf16x8 qreg[NKK];
   {
     const uint16_t* qp = a.q + ((long long)b * a.Nh + h) * DQ + rg * 8;
+    U4 raw[NKK];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) qreg[kk] = as_bf16x8(ldg16(qp + kk * 32));
+    for (int kk = 0; kk < NKK; ++kk) raw[kk] = ldg16(qp + kk * 32);
+    if (a.rope_theta > 0) {
+      // decoupled RoPE on the q^R block (dims 512..575, slide 06 of "Transformer 与 LLM"): half-split
+      // pairs (512 + i, 544 + i), frequency theta^(-2i/64), position ctx-1; the cache holds rotated
+      // k^R. Dims 512 + rg*8 + j sit in raw[16], their partners in raw[17] of the same lane.
+      const double k2 = -2.0 * log2(a.rope_theta) / (double)(DQ - DV);
+      uint32_t* pa = &raw[DV / 32].x;
+      uint32_t* pb = &raw[DV / 32 + 1].x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float ra[2], rb[2];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int i = rg * 8 + 2 * e + hf;
+          double sn, cs;
+          sincos((double)(ctx - 1) * exp2(k2 * (double)i), &sn, &cs);
+          const double x = hf ? bf16hi(pa[e]) : bf16lo(pa[e]);
+          const double y = hf ? bf16hi(pb[e]) : bf16lo(pb[e]);
+          ra[hf] = (float)(x * cs - y * sn);
+          rb[hf] = (float)(x * sn + y * cs);
+        }
+        pa[e] = pack_bf16x2(ra[0], ra[1]);
+        pb[e] = pack_bf16x2(rb[0], rb[1]);
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) qreg[kk] = as_bf16x8(raw[kk]);
     retire_vmem();
   }
 

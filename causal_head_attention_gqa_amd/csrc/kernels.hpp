@@ -30,7 +30,7 @@ hipError_t launch_rope_apply(T* x, const int* positions, long long rows, int S, 
                              int interleaved, hipStream_t st);
 hipError_t launch_kv_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* kc, uint16_t* vc,
                             const int* start, int B, int S, int Nkv, int D, int max_ctx, long long ldk, long long ldv,
-                            double theta, int interleaved, hipStream_t st);
+                            double theta, int Dr, int interleaved, hipStream_t st);
 
 // ---- Prefill (prefill_f32.hip, prefill_bf16.hip) ----
 struct PrefillArgs {
@@ -49,6 +49,8 @@ struct PrefillArgs {
   int max_keys;        // keys available per sequence (q_start[b] + S is clamped to it)
   int window;          // > 0: a query at position p sees keys p-window+1 .. p only (plus the sinks)
   int sinks;           // with a window: keys 0 .. sinks-1 stay visible to every later query
+  int rope_dims;       // with a table: rotary span = the leading rope_dims dims (multiple of 32)
+  int rope_inter;      // with a table: adjacent pairs (2j, 2j+1) instead of (i, i + rope_dims/2)
 };
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t st);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st);

@@ -25,6 +25,8 @@
 //     moved).
 // All per-wave control values are scalar (wave-uniform branches); per-lane LDS and global
 // offsets are computed once. Grid order puts the work-groups with the most tiles first.
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace attn {
@@ -52,7 +54,7 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ out, const float2* __restrict__ table, int B, int S, int Nh, int Nkv, float c,
     int causal, int n_ptiles, long long kv_tok, long long kv_batch, int kv_head, const int* __restrict__ q_start,
-    int max_keys, int window, int sinks) {
+    int max_keys, int window, int sinks, int rope_dims, int rope_inter) {
   constexpr int BP = 32 * (4 / HPW);      // query positions per work-group
   constexpr int CH = D / 8;               // 16-byte chunks per row
   constexpr int RPL = 64 / CH;            // rows per 1 KiB load instruction
@@ -97,19 +99,40 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_bf16_kernel(
 #pragma unroll
       for (int kk = 0; kk < NQ; ++kk) raw[kk] = ldg16(qp + kk * 16);
       if (table) {
-        const float2* tb = table + (long long)(off + p) * (D / 2) + hh * 8;
+        // rotary span: the leading rope_dims dims (a multiple of 32), table row = rope_dims / 2 pairs
+        const float2* tb = table + (long long)(off + p) * (rope_dims / 2);
+        if (rope_inter) {  // adjacent pairs (2j, 2j+1): both halves of one 32-bit word
 #pragma unroll
-        for (int kk = 0; kk < NQ / 2; ++kk) {
-          uint32_t* pa = &raw[kk].x;
-          uint32_t* pb = &raw[kk + NQ / 2].x;
+          for (int kk = 0; kk < NQ; ++kk) {
+            if (kk * 16 >= rope_dims) break;
+            uint32_t* pw = &raw[kk].x;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float2 c0 = tb[kk * 16 + 2 * e], c1 = tb[kk * 16 + 2 * e + 1];
-            const float a0 = bf16lo(pa[e]), a1 = bf16hi(pa[e]);
-            const float b0 = bf16lo(pb[e]), b1 = bf16hi(pb[e]);
-            pa[e] = pack_bf16x2(a0 * c0.x - b0 * c0.y, a1 * c1.x - b1 * c1.y);
-            pb[e] = pack_bf16x2(a0 * c0.y + b0 * c0.x, a1 * c1.y + b1 * c1.x);
+            for (int e = 0; e < 4; ++e) {
+              const float2 cs = tb[kk * 8 + hh * 4 + e];
+              const float a = bf16lo(pw[e]), bb = bf16hi(pw[e]);
+              pw[e] = pack_bf16x2(fmaf(a, cs.x, -(bb * cs.y)), fmaf(a, cs.y, bb * cs.x));
+            }
           }
+        } else {  // half-split pairs (i, i + rope_dims/2): registers kk and kk + rope_dims/32
+          auto half = [&](auto nr_c) {
+            constexpr int NR = decltype(nr_c)::value;
+#pragma unroll
+            for (int kk = 0; kk < NR; ++kk) {
+              uint32_t* pa = &raw[kk].x;
+              uint32_t* pb = &raw[kk + NR].x;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float2 c0 = tb[kk * 16 + hh * 8 + 2 * e], c1 = tb[kk * 16 + hh * 8 + 2 * e + 1];
+                const float a0 = bf16lo(pa[e]), a1 = bf16hi(pa[e]);
+                const float b0 = bf16lo(pb[e]), b1 = bf16hi(pb[e]);
+                pa[e] = pack_bf16x2(fmaf(a0, c0.x, -(b0 * c0.y)), fmaf(a1, c1.x, -(b1 * c1.y)));
+                pb[e] = pack_bf16x2(fmaf(a0, c0.y, b0 * c0.x), fmaf(a1, c1.y, b1 * c1.x));
+              }
+            }
+          };
+          if (rope_dims == 32) half(std::integral_constant<int, 1>{});
+          else if (rope_dims == 64) half(std::integral_constant<int, 2>{});
+          else if constexpr (D >= 128) half(std::integral_constant<int, 4>{});
         }
       }
     } else {
@@ -309,7 +332,7 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t st) {
   prefill_bf16_kernel<D, HPW, kCache, kWin><<<dim3((unsigned)n_wg), dim3(kThreads), 0, st>>>(
       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
       static_cast<uint16_t*>(a.out), a.table, a.B, a.S, a.Nh, a.Nkv, a.scale_log2, a.causal, n_ptiles, a.kv_tok,
-      a.kv_batch, a.kv_head, a.q_start, a.max_keys, a.window, a.sinks);
+      a.kv_batch, a.kv_head, a.q_start, a.max_keys, a.window, a.sinks, a.rope_dims, a.rope_inter);
   return hipGetLastError();
 }
 

@@ -85,19 +85,20 @@ __global__ void rope_apply_kernel(T* __restrict__ x, const int* __restrict__ pos
 }
 
 // KV-cache append with RoPE fused ("Transformer 架构完全深度解析" §九: new K/V are concatenated to
-// the cache; K is rotated at its absolute position first, "2.7 ..." §4). Token s of sequence b goes
-// to cache row t = start[b] + s (clamped to max_ctx - S). One thread per (token, KV head, group of
-// 8 pairs): rotates 8 half-split (or adjacent) pairs of K with rope_cs/rope_rot and copies the
-// matching 16 elements of V.
+// the cache; K is rotated at its absolute position first, "2.7 ..." §4, "Transformer 架构快速入门"
+// §8.2 for a rotary span of Dr <= D dims). Token s of sequence b goes to cache row
+// t = start[b] + s (clamped to max_ctx - S). One thread per (token, KV head, 8 consecutive dims):
+// copies those 8 dims of V, and of K outside the rotary span; inside it, each output element is
+// its pair's rotation (rope_cs / rope_rot, the same bits as the prefill's key pre-pass).
 __global__ void kv_append_kernel(const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
                                  uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
                                  const int* __restrict__ start, int B, int S, int Nkv, int D, int max_ctx,
-                                 long long ldk, long long ldv, double neg2_log2theta_over_d, int rope,
+                                 long long ldk, long long ldv, double neg2_log2theta_over_dr, int rope, int Dr,
                                  int interleaved) {
-  const int groups = D / 16;
+  const int groups = D / 8;
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (long long)B * S * Nkv * groups) return;
-  const int gi = (int)(idx % groups);
+  const int d0 = (int)(idx % groups) * 8;
   const long long row = idx / groups;  // (b * S + s) * Nkv + g
   const int g = (int)(row % Nkv);
   const long long tok = row / Nkv;
@@ -108,33 +109,34 @@ __global__ void kv_append_kernel(const uint16_t* __restrict__ k_new, const uint1
   const uint16_t* vx = v_new + row * D;
   uint16_t* ky = kc + ((long long)b * max_ctx + t) * Nkv * ldk + (long long)g * ldk;
   uint16_t* vy = vc + ((long long)b * max_ctx + t) * Nkv * ldv + (long long)g * ldv;
+  const int half = Dr / 2;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const int i = gi * 8 + e;  // pair index
-    const int ia = interleaved ? 2 * i : i;
-    const int ib = interleaved ? 2 * i + 1 : i + D / 2;
-    float a = bf16_to_f32(kx[ia]), bb = bf16_to_f32(kx[ib]);
-    if (rope) {
-      const float2 r = rope_rot(a, bb, rope_cs(t, i, neg2_log2theta_over_d));
-      a = r.x;
-      bb = r.y;
+    const int d = d0 + e;
+    vy[d] = vx[d];
+    if (!rope || d >= Dr) {
+      ky[d] = kx[d];
+      continue;
     }
-    ky[ia] = f32_to_bf16(a);
-    ky[ib] = f32_to_bf16(bb);
-    vy[ia] = vx[ia];
-    vy[ib] = vx[ib];
+    // the pair (da, db) holding d, its index i, and whether d is the pair's first element
+    const bool first = interleaved ? (d & 1) == 0 : d < half;
+    const int da = first ? d : (interleaved ? d - 1 : d - half);
+    const int db = interleaved ? da + 1 : da + half;
+    const int i = interleaved ? da / 2 : da;
+    const float2 r = rope_rot(bf16_to_f32(kx[da]), bf16_to_f32(kx[db]), rope_cs(t, i, neg2_log2theta_over_dr));
+    ky[d] = f32_to_bf16(first ? r.x : r.y);
   }
 }
 
 hipError_t launch_kv_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* kc, uint16_t* vc,
                             const int* start, int B, int S, int Nkv, int D, int max_ctx, long long ldk, long long ldv,
-                            double theta, int interleaved, hipStream_t st) {
-  const long long n = (long long)B * S * Nkv * (D / 16);
+                            double theta, int Dr, int interleaved, hipStream_t st) {
+  const long long n = (long long)B * S * Nkv * (D / 8);
   if (n == 0) return hipSuccess;
   const bool rope = theta > 0.0;
-  const double k = rope ? -2.0 * log2(theta) / (double)D : 0.0;
+  const double k = rope ? -2.0 * log2(theta) / (double)Dr : 0.0;
   kv_append_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(k_new, v_new, kc, vc, start, B, S, Nkv, D,
-                                                                           max_ctx, ldk, ldv, k, rope ? 1 : 0,
+                                                                           max_ctx, ldk, ldv, k, rope ? 1 : 0, Dr,
                                                                            interleaved ? 1 : 0);
   return hipGetLastError();
 }

@@ -64,10 +64,11 @@ def load() -> ctypes.CDLL:
     lib.attn_prefill_cached_workspace_bytes.argtypes = [c_int, c_int, c_float]
     lib.attn_prefill_cached.restype = c_int
     lib.attn_prefill_cached.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_int, c_ll,
-                                        c_float, c_int, c_int, c_int, c_float, c_int, c_vp, c_size, c_vp]
+                                        c_float, c_int, c_int, c_int, c_int, c_int, c_float, c_int, c_vp, c_size,
+                                        c_vp]
     lib.attn_kv_append.restype = c_int
     lib.attn_kv_append.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_ll, c_ll,
-                                   c_float, c_int, c_int, c_vp]
+                                   c_float, c_int, c_int, c_int, c_vp]
     _lib = lib
     return lib
 
@@ -211,8 +212,9 @@ def prefill_cached_workspace_bytes(max_ctx: int, Dh: int, rope_theta: float) -> 
     return int(load().attn_prefill_cached_workspace_bytes(max_ctx, Dh, float(rope_theta)))
 
 
-def prefill_cached(q, kcache, vcache, q_start, *, rope_theta: float = 0.0, causal: bool = True,
-                   window: int = 0, sinks: int = 0, scale: float | None = None, out=None, workspace=None):
+def prefill_cached(q, kcache, vcache, q_start, *, rope_theta: float = 0.0, rope_dims: int = 0,
+                   rope_interleaved: bool = False, causal: bool = True, window: int = 0, sinks: int = 0,
+                   scale: float | None = None, out=None, workspace=None):
     """Chunked prefill: q [B, S, Nh, Dh] at absolute positions q_start[b] + s against the cached
     keys 0 .. q_start[b]+S-1 (already appended). kcache/vcache [B, max_ctx, Nkv, row] with the
     same row pitch; q_start int32 [B] on the GPU. window > 0: sliding window of that many keys
@@ -235,17 +237,20 @@ def prefill_cached(q, kcache, vcache, q_start, *, rope_theta: float = 0.0, causa
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = load().attn_prefill_cached(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), q_start.data_ptr(),
-                                    out.data_ptr(), B, S, Nh, Nkv, Dh, max_ctx, ld, float(rope_theta),
-                                    1 if causal else 0, int(window), int(sinks), float(scale or 0.0),
+                                    out.data_ptr(), B, S, Nh, Nkv, Dh, max_ctx, ld, float(rope_theta), int(rope_dims),
+                                    1 if rope_interleaved else 0, 1 if causal else 0, int(window), int(sinks),
+                                    float(scale or 0.0),
                                     _dtype_code(q), ws_ptr, ws_bytes,
                                     _stream_ptr(q.device))
     _check(st, "attn_prefill_cached")
     return out
 
 
-def kv_append(k_new, v_new, kcache, vcache, start, *, rope_theta: float = 0.0, interleaved: bool = False):
+def kv_append(k_new, v_new, kcache, vcache, start, *, rope_theta: float = 0.0, rope_dims: int = 0,
+              interleaved: bool = False):
     """Write k_new/v_new [B, S, Nkv, Dh] into the caches at rows start[b] .. start[b]+S-1,
-    rotating K at those positions when rope_theta > 0. start: int32 [B] on the GPU."""
+    rotating the leading rope_dims dims of K (0: all) at those positions when rope_theta > 0.
+    start: int32 [B] on the GPU."""
     torch = _torch()
     _need_cuda(k_new, v_new, start)
     B, S, Nkv, Dh = k_new.shape
@@ -258,7 +263,7 @@ def kv_append(k_new, v_new, kcache, vcache, start, *, rope_theta: float = 0.0, i
     if start.dtype != torch.int32 or start.shape != (B,):
         raise ValueError("start must be int32 [B]")
     st = load().attn_kv_append(k_new.data_ptr(), v_new.data_ptr(), kcache.data_ptr(), vcache.data_ptr(),
-                               start.data_ptr(), B, S, Nkv, Dh, max_ctx, ldk, ldv, float(rope_theta),
+                               start.data_ptr(), B, S, Nkv, Dh, max_ctx, ldk, ldv, float(rope_theta), int(rope_dims),
                                1 if interleaved else 0, _dtype_code(k_new), _stream_ptr(k_new.device))
     _check(st, "attn_kv_append")
     return kcache, vcache

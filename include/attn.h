@@ -98,8 +98,12 @@ int attn_prefill(const void* q, const void* k, const void* v, void* out,
  *          - "Transformer 与 LLM：结构、实现与算量" slide 07 (window W, e.g. 4096; sink = the first 4
  *          tokens kept). window == 0: no window (sinks must be 0). Tiles outside every row's window
  *          and past the sinks are neither loaded nor computed.
- * rope_theta > 0 rotates q (half-split pairs, as attn_prefill) at its absolute position; the
- *          cached keys are used as stored. scale <= 0 selects 1 / sqrt(Dh).
+ * rope_theta > 0 rotates q at its absolute position; the cached keys are used as stored. The
+ *          rotary span is the leading rope_dims dims (0 selects Dh; a multiple of 32), frequencies
+ *          rope_theta^(-2i/rope_dims), pairs (i, i + rope_dims/2), or (2i, 2i + 1) with
+ *          rope_interleaved != 0 - "Transformer 架构快速入门" §8.1-8.2 (either pairing; D_r may be
+ *          a part of the head). It must match the rotation the cached keys received.
+ *          scale <= 0 selects 1 / sqrt(Dh).
  * Supported: ATTN_BF16, Dh in {64, 128}, 1 <= S <= max_ctx, ld % 8 == 0, ld >= Dh.
  * workspace: at least attn_prefill_cached_workspace_bytes(...) bytes (the RoPE angle table).
  * With q_start[b] = 0 and S = max_ctx this is exactly attn_prefill on the cached keys.
@@ -108,8 +112,9 @@ size_t attn_prefill_cached_workspace_bytes(int max_ctx, int Dh, float rope_theta
 
 int attn_prefill_cached(const void* q, const void* kcache, const void* vcache, const int32_t* q_start,
                         void* out, int B, int S, int Nh, int Nkv, int Dh, int max_ctx, long long ld,
-                        float rope_theta, int causal, int window, int sinks, float scale, int dtype,
-                        void* workspace, size_t workspace_bytes, void* stream);
+                        float rope_theta, int rope_dims, int rope_interleaved, int causal, int window,
+                        int sinks, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * KV-cache append with RoPE fused: writes S new tokens of each sequence into the caches at rows
@@ -121,14 +126,16 @@ int attn_prefill_cached(const void* q, const void* kcache, const void* vcache, c
  * k_new, v_new [B, S, Nkv, Dh]  read only
  * kcache, vcache: layout of attn_prefill_cached / attn_decode (pitches ldk, ldv), written only
  *          at the appended rows. start: device int32 [B], clamped to [0, max_ctx - S].
- * rope_theta > 0 rotates K (interleaved == 0: pairs (i, i + Dh/2); != 0: pairs (2i, 2i + 1));
- *          rope_theta <= 0 copies K unchanged. V is copied unchanged.
- * Supported: ATTN_BF16, Dh % 16 == 0 and Dh <= 1024, 1 <= S <= max_ctx.
+ * rope_theta > 0 rotates the leading rope_dims dims of K (0 selects Dh; even), frequencies
+ *          rope_theta^(-2i/rope_dims), pairs (i, i + rope_dims/2), or (2i, 2i + 1) with
+ *          interleaved != 0; the other dims are copied. rope_theta <= 0 copies K unchanged.
+ *          V is copied unchanged.
+ * Supported: ATTN_BF16, Dh % 8 == 0 and Dh <= 1024, 1 <= S <= max_ctx.
  * A key appended here and a key rotated by attn_prefill's RoPE step carry identical bits.
  * ------------------------------------------------------------------------------------------ */
 int attn_kv_append(const void* k_new, const void* v_new, void* kcache, void* vcache, const int32_t* start,
                    int B, int S, int Nkv, int Dh, int max_ctx, long long ldk, long long ldv,
-                   float rope_theta, int interleaved, int dtype, void* stream);
+                   float rope_theta, int rope_dims, int interleaved, int dtype, void* stream);
 
 /* ------------------------------------------------------------------------------------------
  * KV-cache decode: one new query token per sequence attends to every cached key of its head.
@@ -144,8 +151,10 @@ int attn_kv_append(const void* k_new, const void* v_new, void* kcache, void* vca
  *          outside is clamped to [0, max_ctx] for memory safety and 0 keys give an all-zero
  *          output row (the result is then not meaningful).
  * out      [B, Nh, Dv]                      written
- * rope_theta > 0 rotates q at position ctx_lens[b]-1 (the cache holds already-rotated keys);
- *          only for Dqk == Dv. scale <= 0 selects 1 / sqrt(Dqk).
+ * rope_theta > 0 rotates q at position ctx_lens[b]-1 (the cache holds already-rotated keys):
+ *          half-split pairs over all Dqk dims for Dqk == Dv; for the MLA form only the decoupled
+ *          q^R block, dims 512..575 (pairs (512 + i, 544 + i), frequency rope_theta^(-2i/64)) -
+ *          "Transformer 与 LLM：结构、实现与算量" slide 06. scale <= 0 selects 1 / sqrt(Dqk).
  * Supported (ATTN_BF16 only): Dqk == Dv in {64, 128} with Nh % Nkv == 0 and a group size
  *   G = Nh / Nkv of at most 16 or a multiple of 16 (query heads are processed 16 at a time);
  *   and the MLA form Dqk = 576, Dv = 512, Nkv = 1, vcache == kcache, ldv == ldk, Nh % 16 == 0.

@@ -79,7 +79,7 @@ def test_decode_argument_errors():
     assert call(Dqk=96, Dv=96, ldk=96, ldv=96) == 2
     assert call(dt=0) == 2                      # fp32 decode is not built
     assert call(Dqk=576, Dv=512, Nkv=1, Nh=128, ldk=576, ldv=576, vc=P + 4096) == 2  # MLA needs V aliasing K
-    assert call(Dqk=576, Dv=512, Nkv=1, Nh=128, ldk=576, ldv=576, rope=1e4) == 2
+    assert call(Dqk=576, Dv=512, Nkv=1, Nh=128, ldk=576, ldv=576, rope=1e4) == 3  # decoupled RoPE: supported
     assert call() == 3                          # no workspace
     assert call(ws=P, wsb=8) == 3
     assert call(ctx=None) == 1
@@ -111,7 +111,8 @@ def test_prefill_cached_argument_errors():
         return L.attn_prefill_cached(kw.get("q", P), kw.get("kc", P), kw.get("vc", P), kw.get("st", P),
                                      kw.get("o", P), kw.get("B", 2), kw.get("S", 16), kw.get("Nh", 8),
                                      kw.get("Nkv", 2), kw.get("Dh", 128), kw.get("T", 100), kw.get("ld", 128),
-                                     kw.get("rope", 0.0), kw.get("causal", 1), kw.get("win", 0), kw.get("sinks", 0),
+                                     kw.get("rope", 0.0), kw.get("rdims", 0), 0, kw.get("causal", 1), kw.get("win", 0),
+                                     kw.get("sinks", 0),
                                      0.0, kw.get("dt", 1), kw.get("ws", None), kw.get("wsb", 0), None)
     assert call(S=101) == 1                     # chunk longer than the cache
     assert call(ld=64) == 1                     # row pitch shorter than the head dim
@@ -124,6 +125,8 @@ def test_prefill_cached_argument_errors():
     assert call(win=-1) == 1
     assert call(win=64, causal=0) == 1          # a window needs the causal mask
     assert call(sinks=4) == 1                   # sinks only with a window
+    assert call(rdims=256) == 1                 # rotary span longer than the head
+    assert call(rdims=48) == 2                  # q is rotated in 32-dim groups
     assert call(B=0) == 0 and call(S=0) == 0
 
 
@@ -132,11 +135,12 @@ def test_kv_append_argument_errors():
     def call(**kw):
         return L.attn_kv_append(kw.get("k", P), kw.get("v", P), kw.get("kc", P), kw.get("vc", P), kw.get("st", P),
                                 kw.get("B", 2), kw.get("S", 16), kw.get("Nkv", 2), kw.get("Dh", 128),
-                                kw.get("T", 100), kw.get("ldk", 128), kw.get("ldv", 128), kw.get("rope", 1e4), 0,
-                                kw.get("dt", 1), None)
+                                kw.get("T", 100), kw.get("ldk", 128), kw.get("ldv", 128), kw.get("rope", 1e4),
+                                kw.get("rdims", 0), 0, kw.get("dt", 1), None)
     assert call(S=101) == 1
     assert call(ldv=100) == 1
-    assert call(Dh=72, ldk=72, ldv=72) == 2     # head dim not a multiple of 16
+    assert call(Dh=68, ldk=72, ldv=72) == 2     # head dim not a multiple of 8
+    assert call(rdims=33) == 1                  # odd rotary span
     assert call(dt=0) == 2
     assert call(st=None) == 1
     assert call(rope=float("inf")) == 1

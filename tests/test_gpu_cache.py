@@ -33,8 +33,9 @@ def _empty_cache(B, T, Nkv, D, ld=None, fill=0x3F80):
     return c[..., :D], c
 
 
-@pytest.mark.parametrize("D,interleaved,rope", [(128, False, 5e5), (64, True, 1e4), (128, False, 0.0)])
-def test_kv_append_rotates_and_places(D, interleaved, rope):
+@pytest.mark.parametrize("D,interleaved,rope,rdims", [(128, False, 5e5, 0), (64, True, 1e4, 0), (128, False, 0.0, 0),
+                                                      (128, False, 1e4, 64), (64, True, 5e5, 32)])
+def test_kv_append_rotates_and_places(D, interleaved, rope, rdims):
     import causal_head_attention_gqa_amd as attn
     torch = _torch()
     B, S, Nkv, T = 2, 37, 2, 100
@@ -44,14 +45,15 @@ def test_kv_append_rotates_and_places(D, interleaved, rope):
     kc, kc_full = _empty_cache(B, T, Nkv, D, ld=D + 8)
     vc, _ = _empty_cache(B, T, Nkv, D)
     attn.kv_append(to_dev(kn, "bf16"), to_dev(vn, "bf16"), kc, vc, torch.as_tensor(start, device="cuda"),
-                   rope_theta=rope, interleaved=interleaved)
+                   rope_theta=rope, rope_dims=rdims, interleaved=interleaved)
     kh = kc.float().cpu().numpy()
     vh = _bits(vc)
     for b in range(B):
         rows = slice(start[b], start[b] + S)
         want = values(kn[b:b + 1], "bf16")
         if rope > 0:
-            want = oracle.rope_rotate(want, start[b] + np.arange(S), rope, interleaved=interleaved)
+            want = oracle.rope_rotate(want, start[b] + np.arange(S), rope, interleaved=interleaved,
+                                      rot_dims=rdims or None)
         assert max_abs(kh[b, rows], want[0]) <= BF16_TOL
         if rope == 0:
             assert np.array_equal(_bits(kc[b, rows].contiguous()), kn[b].view(np.int16))
@@ -146,4 +148,39 @@ def test_sliding_window_with_sinks_matches_oracle(case):
                               rope_theta=rope, window=window, sinks=sinks).float().cpu().numpy()
     want = oracle.prefill_chunk(values(q, "bf16"), values(k_all, "bf16"), values(v_all, "bf16"), starts,
                                 rope_theta=rope, window=window, sinks=sinks)
+    assert max_abs(got, want) <= BF16_TOL
+
+
+ROPE_CASES = [
+    # D, rope_dims, interleaved, theta
+    (128, 64, False, 1e4),
+    (128, 128, True, 5e5),
+    (64, 32, True, 1e4),
+    (128, 32, False, 5e5),
+]
+
+
+@pytest.mark.parametrize("case", ROPE_CASES, ids=lambda c: "D%dR%d%s" % (c[0], c[1], "i" if c[2] else "h"))
+def test_prefill_cached_rope_variants_match_oracle(case):
+    """Adjacent-pair and partial rotary RoPE in the fused path: the append rotates K, the prefill
+    rotates q in registers, both over the same span and pairing."""
+    import causal_head_attention_gqa_amd as attn
+    torch = _torch()
+    D, rdims, inter, theta = case
+    B, S, Nh, Nkv, T = 2, 48, 8, 2, 128
+    starts = np.array([0, 70], np.int32)
+    wid = 880 + D + rdims
+    k_all = synth.normal(wid, 1, (B, T, Nkv, D), "bf16")
+    v_all = synth.normal(wid, 2, (B, T, Nkv, D), "bf16")
+    q = synth.normal(wid, 0, (B, S, Nh, D), "bf16")
+    kc, _ = _empty_cache(B, T, Nkv, D)
+    vc, _ = _empty_cache(B, T, Nkv, D)
+    n_max = int((starts + S).max())
+    zeros = torch.zeros(B, dtype=torch.int32, device="cuda")
+    attn.kv_append(to_dev(k_all[:, :n_max], "bf16"), to_dev(v_all[:, :n_max], "bf16"), kc, vc, zeros,
+                   rope_theta=theta, rope_dims=rdims, interleaved=inter)
+    got = attn.prefill_cached(to_dev(q, "bf16"), kc, vc, torch.as_tensor(starts, device="cuda"), rope_theta=theta,
+                              rope_dims=rdims, rope_interleaved=inter).float().cpu().numpy()
+    want = oracle.prefill_chunk(values(q, "bf16"), values(k_all, "bf16"), values(v_all, "bf16"), starts,
+                                rope_theta=theta, rope_interleaved=inter, rope_dims=rdims)
     assert max_abs(got, want) <= BF16_TOL

@@ -93,6 +93,18 @@ def test_mla_decode_small():
     assert max_abs(got, want) <= BF16_TOL
 
 
+def test_mla_decode_decoupled_rope():
+    """q^R (dims 512..575) rotated in-kernel at ctx-1; the cache rows hold rotated k^R."""
+    B, Nh, T = 2, 32, 200
+    ctx = np.array([200, 77], np.int32)
+    q = synth.normal(470, 0, (B, Nh, 576), "bf16")
+    kc = synth.normal(470, 1, (B, T, 1, 576), "bf16")
+    scale = 1.0 / math.sqrt(192)
+    got = _gpu_decode(q, kc, None, ctx, scale=scale, rope=1e4, mla=True)
+    want = _oracle_decode(q, kc, None, ctx, scale=scale, rope=1e4, mla=True)
+    assert max_abs(got, want) <= BF16_TOL
+
+
 def test_llama3_decode_full():
     w = synth.LLAMA3_DECODE
     q, kc, vc, ctx = w.inputs()
