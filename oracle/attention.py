@@ -143,9 +143,13 @@ def prefill_rows(q, k, v, b: int, h: int, rows, *, causal: bool = True, scale: f
     Query and key positions are 0..S-1 ([P1] §4 uses arange(seq_len)). RoPE, when
     rope_theta > 0, rotates q and k (not v: [P1] §2, [P2] §8.5) before the scores.
     The full score row over all S keys is materialised and masked with -inf ([P1] §3.3).
+    MLA's non-absorbed prefill ([P4] slide 06) has v narrower than q/k: q = [q^C ; q^R],
+    k = [k^C ; k^R] with v of the width of q^C. There RoPE touches only the decoupled block,
+    the last D - Dv dims (half-split pairs, frequencies base^(-2i/(D - Dv))), as in decode.
     """
     B, S, Nh, D = q.shape
     Nkv = k.shape[2]
+    Dv = v.shape[3]
     g = kv_head_of(h, Nh, Nkv)
     rows = np.asarray(rows, dtype=np.int64)
     if scale is None:
@@ -153,8 +157,9 @@ def prefill_rows(q, k, v, b: int, h: int, rows, *, causal: bool = True, scale: f
     qh = _f64(q[b:b + 1, rows, h:h + 1, :])  # [1, R, 1, D]
     kh = _f64(k[b:b + 1, :, g:g + 1, :])  # [1, S, 1, D]
     if rope_theta > 0:
-        qh = rope_rotate(qh, rows, rope_theta)
-        kh = rope_rotate(kh, np.arange(S), rope_theta)
+        span = {} if Dv == D else {"rot_dims": D - Dv, "rot_offset": Dv}
+        qh = rope_rotate(qh, rows, rope_theta, **span)
+        kh = rope_rotate(kh, np.arange(S), rope_theta, **span)
     mask = causal_mask(rows, S) if causal else None
     return head_attention(qh[0, :, 0, :], kh[0, :, 0, :], v[b, :, g, :], scale, mask)
 

@@ -420,3 +420,31 @@ def test_mla_decoupled_rope_absorbed_equals_per_head():
     row = np.concatenate([c, kr_rot], axis=1)[None, :, None, :]
     lat = oracle.decode(q_abs, row, row[..., :dc], np.array([T]), scale=scale, rope_theta=theta)[0]
     np.testing.assert_allclose(np.einsum("hdc,hc->hd", w_uv, lat), ref, rtol=1e-10, atol=1e-12)
+
+
+def test_mla_non_absorbed_prefill_equals_absorbed_decode():
+    """[P4] slide 06: prefill keeps W_UK / W_UV un-absorbed, per head q = [q^C ; q^R] and
+    k = [k^C ; k^R] (k^R shared by the heads) with v = c W_UV; RoPE only on the
+    decoupled block. Row t of that causal prefill equals the absorbed decode of query t over the
+    first t + 1 cache rows [c ; rotated k^R], mapped back through W_UV."""
+    rng = np.random.default_rng(43)
+    H, T, dc, dr, dh, theta = 3, 11, 24, 8, 16, 1e4
+    c = _rand(rng, T, dc) * 0.2
+    kr = _rand(rng, T, dr)
+    qc, qr = _rand(rng, T, H, dh) * 0.3, _rand(rng, T, H, dr)
+    w_uk, w_uv = _rand(rng, H, dh, dc) * 0.2, _rand(rng, H, dh, dc) * 0.2
+    scale = 1.0 / math.sqrt(dh + dr)
+    q = np.concatenate([qc, qr], axis=2)[None]  # [1, T, H, dh + dr]
+    k = np.concatenate([np.einsum("tc,hdc->thd", c, w_uk), np.repeat(kr[:, None], H, axis=1)], axis=2)[None]
+    v = np.einsum("tc,hdc->thd", c, w_uv)[None]  # [1, T, H, dh]
+    got = oracle.prefill(q, k, v, scale=scale, rope_theta=theta)[0]  # [T, H, dh]
+    kr_rot = oracle.rope_rotate(kr[None, :, None, :], np.arange(T), theta)[0, :, 0]
+    row = np.concatenate([c, kr_rot], axis=1)[None, :, None, :]
+    for t in range(T):
+        q_abs = np.concatenate([np.einsum("hd,hdc->hc", qc[t], w_uk), qr[t]], axis=1)[None]
+        lat = oracle.decode(q_abs, row, row[..., :dc], np.array([t + 1]), scale=scale, rope_theta=theta)[0]
+        np.testing.assert_allclose(got[t], np.einsum("hdc,hc->hd", w_uv, lat), rtol=1e-10, atol=1e-12)
+    # the rotation reaches only the decoupled block: without RoPE on it the result differs
+    plain = oracle.prefill(q, k, v, scale=scale)[0]
+    assert np.abs(plain - got).max() > 1e-3
+    np.testing.assert_array_equal(plain[0], v[0, 0])  # position 0: the only key, no rotation
