@@ -1,5 +1,5 @@
 """MI355X (gfx950) causal attention: prefill, chunked prefill against a KV cache, KV-cache append,
-KV-cache decode (GQA and MLA-absorbed) and RoPE.
+KV-cache decode (GQA and MLA-absorbed), MLA's non-absorbed prefill and RoPE.
 
 The computation lives in the HIP library libattn_gfx950.so (C ABI in include/attn.h);
 ``lib`` is a thin ctypes binding with the same entry points.
@@ -15,6 +15,8 @@ from .lib import (  # noqa: F401
     prefill,
     prefill_cached,
     prefill_cached_workspace_bytes,
+    prefill_mla,
+    prefill_mla_workspace_bytes,
     prefill_workspace_bytes,
     rope_apply_,
     status_str,

@@ -48,8 +48,11 @@ def prefill_pairs(S: int, causal: bool) -> int:
     return S * (S + 1) // 2 if causal else S * S
 
 
-def prefill_flops(B: int, S: int, Nh: int, Dh: int, causal: bool = True) -> int:
-    return 4 * Dh * B * Nh * prefill_pairs(S, causal)
+def prefill_flops(B: int, S: int, Nh: int, Dh: int, causal: bool = True, Dv: int | None = None) -> int:
+    """2 FLOP per multiply-add of Q K^T (Dh per pair) and of P V (Dv per pair, Dv = Dh unless given:
+    MLA's non-absorbed prefill has Dh = 192, Dv = 128) over the unmasked (query, key) pairs."""
+    dv = Dh if Dv is None else Dv
+    return 2 * (Dh + dv) * B * Nh * prefill_pairs(S, causal)
 
 
 def prefill_bytes(B: int, S: int, Nh: int, Nkv: int, Dh: int, bytes_per_elem: int) -> int:

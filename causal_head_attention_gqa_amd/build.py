@@ -66,6 +66,90 @@ def mfma_overlaps(asm: str) -> list[str]:
     return bad
 
 
+_BFE = re.compile(r"^s_bfe_i64\s+(s\[\d+:\d+\]),")
+_LDS_SADDR = re.compile(r"^global_load_lds_dword\w*\s+v\d+,\s*(s\[\d+:\d+\])")
+
+
+def sign_extended_lds_bases(asm: str, window: int = 8) -> list[str]:
+    """Direct-to-LDS loads whose 64-bit SGPR base was built by a signed 32-to-64-bit extension.
+
+    A base pointer rebuilt from two 32-bit halves must zero-extend its low word; a sign
+    extension (s_bfe_i64 ..., 0x200000) turns every address whose bit 31 is set into an address
+    in the top 4 GiB, i.e. a memory fault. The scan looks a few instructions ahead of each
+    s_bfe_i64 for a global_load_lds that takes the same register pair as its base.
+    """
+    lines = [ln.strip() for ln in asm.splitlines()]
+    bad = []
+    for i, t in enumerate(lines):
+        m = _BFE.match(t)
+        if not m:
+            continue
+        for u in lines[i + 1:i + 1 + window]:
+            n = _LDS_SADDR.match(u)
+            if n and n.group(1) == m.group(1):
+                bad.append(t + " -> " + u)
+                break
+    return bad
+
+
+_SREG = re.compile(r"s\[(\d+):(\d+)\]|s(\d+)$")
+
+
+def _sgprs(tok: str):
+    m = _SREG.match(tok.strip())
+    if not m:
+        return None
+    if m.group(1):
+        return int(m.group(1)), int(m.group(2))
+    return int(m.group(3)), int(m.group(3))
+
+
+def valu_sgpr_lds_hazards(asm: str, wait_states: int = 5) -> list[str]:
+    """Direct-to-LDS loads whose SGPR base pair was written by a VALU instruction fewer than 5
+    wait states earlier.
+
+    A VMEM instruction that reads an SGPR written by a VALU instruction (v_readfirstlane_b32,
+    v_readlane_b32, a v_cmp into an SGPR pair) needs 5 wait states in between; the compiler
+    inserts them for the loads it emits itself but not in front of inline assembly, where a
+    stale base gives wrong addresses. Walking back from each load, each instruction counts one
+    wait state and s_nop N counts N + 1; a scalar instruction that writes part of the pair
+    settles that part. A label inside the window ends the walk with the pair still unsettled,
+    which is reported too (another predecessor may have written it).
+    """
+    lines = [ln.strip() for ln in asm.splitlines()]
+    no_dest = ("s_cmp", "s_bitcmp", "s_cbranch", "s_branch", "s_waitcnt", "s_nop", "s_barrier", "s_setprio",
+               "s_sleep", "s_endpgm", "s_dcache", "s_sendmsg")
+    bad = []
+    for i, t in enumerate(lines):
+        n = _LDS_SADDR.match(t)
+        if not n:
+            continue
+        lo, hi = _sgprs(n.group(1))
+        open_regs = set(range(lo, hi + 1))
+        ws = 0
+        for u in reversed(lines[:i]):
+            if not u or u.startswith((";", ".")):
+                continue
+            if u.endswith(":"):
+                bad.append("label " + u + " within the wait window of " + t)
+                break
+            parts = u.split(None, 1)
+            d = _sgprs(parts[1].split(",")[0]) if len(parts) > 1 and not u.startswith(no_dest) else None
+            if d:
+                hit = open_regs & set(range(d[0], d[1] + 1))
+                if hit and u.startswith("v_"):
+                    bad.append(u + " -> " + t)
+                    break
+                open_regs -= hit
+                if not open_regs:
+                    break
+            m = re.match(r"s_nop\s+(\d+)", u)
+            ws += int(m.group(1)) + 1 if m else 1
+            if ws >= wait_states:
+                break
+    return bad
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
     asm = os.path.join(BUILD, os.path.basename(src)[:-4] + ".s")
@@ -83,6 +167,15 @@ def _compile(src: str) -> str:
         bad = mfma_overlaps(f.read())
     if bad:
         raise RuntimeError(f"{src}: MFMA destination overlaps a source operand:\n" + "\n".join(bad[:5]))
+    with open(asm) as f:
+        text = f.read()
+    bad = sign_extended_lds_bases(text)
+    if bad:
+        raise RuntimeError(f"{src}: sign-extended base address of a direct-to-LDS load:\n" + "\n".join(bad[:5]))
+    bad = valu_sgpr_lds_hazards(text)
+    if bad:
+        raise RuntimeError(f"{src}: direct-to-LDS load reads an SGPR a VALU wrote < 5 wait states earlier:\n"
+                           + "\n".join(bad[:5]))
     return obj
 
 

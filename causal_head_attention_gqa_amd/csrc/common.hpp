@@ -109,7 +109,11 @@ __device__ __forceinline__ void load_lds16_async(const void* gptr, const void* l
 }
 
 // The same load with a wave-uniform base in SGPRs and a 32-bit per-lane byte offset: the
-// address needs no vector arithmetic per load.
+// address needs no vector arithmetic per load. The base must be computed by scalar instructions
+// (kernel arguments, block indices, loop counters): the "s" constraint then holds, and the SGPR
+// pair is never the result of a vector instruction such as v_readfirstlane. A VMEM instruction
+// that reads an SGPR written by a VALU instruction needs 5 wait states, which the compiler does not
+// insert in front of inline assembly (the build rejects such sequences in the generated code).
 __device__ __forceinline__ void load_lds16_async_sv(const void* sbase, uint32_t voff, const void* lds_base) {
   const uint32_t lds_addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");

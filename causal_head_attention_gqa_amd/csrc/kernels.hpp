@@ -28,6 +28,8 @@ hipError_t launch_rope_rotate_table(const T* src, T* dst, const float2* table, l
 template <typename T>
 hipError_t launch_rope_apply(T* x, const int* positions, long long rows, int S, int N, int D, double theta,
                              int interleaved, hipStream_t st);
+hipError_t launch_rope_span_table(const uint16_t* src, uint16_t* dst, const float2* table, long long rows, int S,
+                                  int N, int D, int roff, int Dr, hipStream_t st);
 hipError_t launch_kv_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* kc, uint16_t* vc,
                             const int* start, int B, int S, int Nkv, int D, int max_ctx, long long ldk, long long ldv,
                             double theta, int Dr, int interleaved, hipStream_t st);
@@ -40,11 +42,15 @@ struct PrefillArgs {
   void* out;
   const float2* table;  // [S][D/2] (cos, sin) or nullptr: q used as given
   int B, S, Nh, Nkv, D;
+  int Dv;            // head dim of v and out (bf16 path; D is the q/k head dim)
   float scale_log2;  // softmax scale * log2(e)
   int causal;
-  // K/V addressing (bf16 path): element (b, t, g, d) at b*kv_batch + t*kv_tok + g*kv_head + d
+  // K/V addressing (bf16 path): element (b, t, g, d) of K at b*kv_batch + t*kv_tok + g*kv_head + d,
+  // of V at b*v_batch + t*v_tok + g*v_head + d
   long long kv_tok, kv_batch;
   int kv_head;
+  long long v_tok, v_batch;
+  int v_head;
   const int* q_start;  // device [B]: absolute position of query 0 of each sequence, or nullptr (0)
   int max_keys;        // keys available per sequence (q_start[b] + S is clamped to it)
   int window;          // > 0: a query at position p sees keys p-window+1 .. p only (plus the sinks)

@@ -60,6 +60,46 @@ __global__ void rope_rotate_table_kernel(const T* __restrict__ src, T* __restric
   }
 }
 
+// Copy of src [rows, D] into dst with the half-split pairs of the span [roff, roff + Dr) rotated by
+// the table [S][Dr/2] (row r has position (r / N) % S); dims outside the span are copied. One
+// thread per (row, 8 consecutive dims). Used for MLA's decoupled RoPE block ("Transformer 与 LLM"
+// slide 06: only the 64-dim k^R / q^R part carries position).
+__global__ void rope_span_table_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
+                                       const float2* __restrict__ table, long long rows, int S, int N, int D,
+                                       int roff, int Dr) {
+  const int groups = D / 8;
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= rows * groups) return;
+  const long long row = idx / groups;
+  const int d0 = (int)(idx % groups) * 8;
+  const int pos = (int)((row / N) % S);
+  const uint16_t* x = src + row * D;
+  uint16_t* y = dst + row * D;
+  const int half = Dr / 2;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int d = d0 + e;
+    const int j = d - roff;  // position inside the span
+    if (j < 0 || j >= Dr) {
+      y[d] = x[d];
+      continue;
+    }
+    const int i = j < half ? j : j - half;
+    const float2 r = rope_rot(bf16_to_f32(x[roff + i]), bf16_to_f32(x[roff + i + half]),
+                              table[(long long)pos * half + i]);
+    y[d] = f32_to_bf16(j < half ? r.x : r.y);
+  }
+}
+
+hipError_t launch_rope_span_table(const uint16_t* src, uint16_t* dst, const float2* table, long long rows, int S,
+                                  int N, int D, int roff, int Dr, hipStream_t st) {
+  const long long n = rows * (D / 8);
+  if (n == 0) return hipSuccess;
+  rope_span_table_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(src, dst, table, rows, S, N, D,
+                                                                                   roff, Dr);
+  return hipGetLastError();
+}
+
 // In-place rotation with explicit positions; fp64 angle and fp64 rotation, one rounding at the
 // store. One thread per pair.
 template <typename T>

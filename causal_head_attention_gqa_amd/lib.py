@@ -26,6 +26,8 @@ EXPORTS = (
     "attn_prefill_cached_workspace_bytes",
     "attn_prefill_cached",
     "attn_kv_append",
+    "attn_prefill_mla_workspace_bytes",
+    "attn_prefill_mla",
 )
 
 _lib = None
@@ -69,6 +71,11 @@ def load() -> ctypes.CDLL:
     lib.attn_kv_append.restype = c_int
     lib.attn_kv_append.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_ll, c_ll,
                                    c_float, c_int, c_int, c_int, c_vp]
+    lib.attn_prefill_mla_workspace_bytes.restype = c_size
+    lib.attn_prefill_mla_workspace_bytes.argtypes = [c_int, c_int, c_int, c_float]
+    lib.attn_prefill_mla.restype = c_int
+    lib.attn_prefill_mla.argtypes = [c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_float, c_int, c_float,
+                                     c_vp, c_size, c_vp]
     _lib = lib
     return lib
 
@@ -141,6 +148,39 @@ def prefill(q, k, v, *, rope_theta: float = 0.0, causal: bool = True, scale: flo
                              float(rope_theta), 1 if causal else 0, float(scale or 0.0), dt, ws_ptr, ws_len,
                              _stream_ptr(q.device))
     _check(st, "attn_prefill")
+    return out
+
+
+def prefill_mla_workspace_bytes(B: int, S: int, Nkv: int, rope_theta: float) -> int:
+    return int(load().attn_prefill_mla_workspace_bytes(B, S, Nkv, float(rope_theta)))
+
+
+def prefill_mla(q, k, v, *, rope_theta: float = 0.0, causal: bool = True, scale: float | None = None, out=None,
+                workspace=None):
+    """MLA's non-absorbed prefill: q [B, S, Nh, 192], k [B, S, Nkv, 192], v [B, S, Nkv, 128]
+    (bf16); RoPE on dims 128..191 only. Returns out [B, S, Nh, 128]."""
+    torch = _torch()
+    _need_cuda(q, k, v)
+    B, S, Nh, Dqk = q.shape
+    Nkv = k.shape[2]
+    if Dqk != 192 or k.shape != (B, S, Nkv, 192) or v.shape != (B, S, Nkv, 128):
+        raise ValueError("MLA prefill expects q/k [..., 192] and v [..., 128] over the same B, S")
+    if q.dtype != torch.bfloat16 or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("MLA prefill takes bf16 q, k, v")
+    if out is None:
+        out = torch.empty((B, S, Nh, 128), dtype=q.dtype, device=q.device)
+    _need_cuda(out)
+    if out.shape != (B, S, Nh, 128) or out.dtype != q.dtype:
+        raise ValueError("out must be [B, S, Nh, 128] bf16")
+    need = prefill_mla_workspace_bytes(B, S, Nkv, rope_theta)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load().attn_prefill_mla(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, S, Nh, Nkv,
+                                 float(rope_theta), 1 if causal else 0, float(scale or 0.0), ws_ptr, ws_len,
+                                 _stream_ptr(q.device))
+    _check(st, "attn_prefill_mla")
     return out
 
 

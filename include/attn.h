@@ -77,6 +77,29 @@ int attn_prefill(const void* q, const void* k, const void* v, void* out,
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * MLA prefill, non-absorbed: "Transformer 与 LLM：结构、实现与算量" slide 06 (prefill keeps W_UK / W_UV
+ * un-absorbed: per head, q and k are [128 latent-projected dims ; 64 decoupled RoPE dims] and v is
+ * 128 dims; scores use 1/sqrt(192)). Causal self-attention with Dqk = 192 != Dv = 128.
+ *
+ * q   [B, S, Nh,  192]  read only (q^C ; q^R)
+ * k   [B, S, Nkv, 192]  read only (k^C ; k^R; the shared k^R is repeated per KV head)
+ * v   [B, S, Nkv, 128]  read only
+ * out [B, S, Nh,  128]  written
+ * rope_theta > 0 rotates only dims 128..191 of q and k (the decoupled block; half-split pairs
+ *   (128 + i, 160 + i), frequency rope_theta^(-2i/64), positions 0 .. S-1); the rotated keys go
+ *   to the workspace. causal as attn_prefill; scale <= 0 selects 1 / sqrt(192).
+ * Supported: bf16 storage (fp32 accumulation), Nh % Nkv == 0.
+ * workspace: at least attn_prefill_mla_workspace_bytes(...) bytes (0 without RoPE).
+ * Status: the kernel is built but not enabled yet; after validating its arguments (the errors
+ * above) the call returns ATTN_ERR_UNSUPPORTED without launching anything.
+ * ------------------------------------------------------------------------------------------ */
+size_t attn_prefill_mla_workspace_bytes(int B, int S, int Nkv, float rope_theta);
+
+int attn_prefill_mla(const void* q, const void* k, const void* v, void* out, int B, int S, int Nh, int Nkv,
+                     float rope_theta, int causal, float scale, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * Prefill with a KV cache (chunked prefill): S new query tokens of each sequence attend to the
  * cached keys, their own included. "Transformer 架构完全深度解析" §九 (new K/V are appended to
  * the cache, then the new queries attend to all of it); "Transformer 与 LLM：结构、实现与算量"

@@ -73,15 +73,20 @@ class Prefill:
     dtype: str
     rope_theta: float
     causal: bool = True
+    Dv: int = 0  # head dim of v / out when it differs from the q/k head dim Dh (MLA prefill)
 
     @property
     def scale(self) -> float:
         return 1.0 / math.sqrt(self.Dh)
 
+    @property
+    def dv(self) -> int:
+        return self.Dv or self.Dh
+
     def inputs(self):
         q = normal(self.wid, TENSOR_Q, (self.B, self.S, self.Nh, self.Dh), self.dtype)
         k = normal(self.wid, TENSOR_K, (self.B, self.S, self.Nkv, self.Dh), self.dtype)
-        v = normal(self.wid, TENSOR_V, (self.B, self.S, self.Nkv, self.Dh), self.dtype)
+        v = normal(self.wid, TENSOR_V, (self.B, self.S, self.Nkv, self.dv), self.dtype)
         return q, k, v
 
 
@@ -123,5 +128,8 @@ LLAMA3_DECODE = Decode(4, "Llama-3-8B GQA KV-cache decode", B=64, Nh=32, Nkv=8, 
                        ctx_lo=1024, ctx_hi=8192, dtype="bf16", scale=1.0 / math.sqrt(128))
 MLA_DECODE = Decode(5, "MLA-absorbed decode (MQA form)", B=32, Nh=128, Nkv=1, Dqk=576, Dv=512, max_ctx=4096,
                     ctx_lo=4096, ctx_hi=4096, dtype="bf16", scale=1.0 / math.sqrt(192), mla=True)
+# DeepSeek-V3-shaped non-absorbed MLA prefill: per head q/k = [128 ; 64 decoupled RoPE] dims, v 128
+MLA_PREFILL = Prefill(6, "MLA non-absorbed causal prefill", B=1, S=4096, Nh=128, Nkv=128, Dh=192, Dv=128,
+                      dtype="bf16", rope_theta=10000.0)
 
-WORKLOADS = {w.wid: w for w in (TINY_F32, GPT2_PREFILL, LLAMA3_PREFILL, LLAMA3_DECODE, MLA_DECODE)}
+WORKLOADS = {w.wid: w for w in (TINY_F32, GPT2_PREFILL, LLAMA3_PREFILL, LLAMA3_DECODE, MLA_DECODE, MLA_PREFILL)}

@@ -27,7 +27,8 @@ def test_header_declares_the_entry_points():
     fns = declared_functions()
     for name in ("attn_prefill", "attn_decode", "rope_apply", "attn_prefill_workspace_bytes",
                  "attn_decode_workspace_bytes", "attn_status_str", "attn_prefill_cached",
-                 "attn_prefill_cached_workspace_bytes", "attn_kv_append"):
+                 "attn_prefill_cached_workspace_bytes", "attn_kv_append", "attn_prefill_mla",
+                 "attn_prefill_mla_workspace_bytes"):
         assert name in fns
 
 
@@ -152,3 +153,29 @@ def test_prefill_cached_workspace_query():
     _lib()
     assert lib.prefill_cached_workspace_bytes(8192, 128, 0.0) == 0
     assert lib.prefill_cached_workspace_bytes(8192, 128, 5e5) == 8192 * 64 * 8
+
+
+def test_prefill_mla_argument_errors():
+    L = _lib()
+    def call(**kw):
+        return L.attn_prefill_mla(kw.get("q", P), kw.get("k", P), kw.get("v", P), kw.get("o", P), kw.get("B", 2),
+                                  kw.get("S", 16), kw.get("Nh", 8), kw.get("Nkv", 8), kw.get("rope", 0.0), 1,
+                                  kw.get("scale", 0.0), kw.get("ws", None), kw.get("wsb", 0), None)
+    assert call(Nh=6, Nkv=4) == 1
+    assert call(Nkv=0) == 1
+    assert call(v=None) == 1
+    assert call(o=P + 8) == 1                   # misaligned
+    assert call(rope=1e4) == 3                  # k^R rotation needs a workspace
+    assert call(rope=1e4, ws=P, wsb=64) == 3
+    assert call(rope=float("nan")) == 1
+    assert call(scale=float("inf")) == 1
+    assert call(B=0) == 0 and call(S=0) == 0
+    assert call() == 2                          # valid arguments: the variant is not enabled yet
+
+
+def test_prefill_mla_workspace_query():
+    from causal_head_attention_gqa_amd import lib
+    _lib()
+    assert lib.prefill_mla_workspace_bytes(1, 4096, 128, 0.0) == 0
+    # fp32 (cos, sin) table [S, 32] plus keys with the rotated k^R block
+    assert lib.prefill_mla_workspace_bytes(1, 4096, 128, 1e4) == 4096 * 32 * 8 + 4096 * 128 * 192 * 2
