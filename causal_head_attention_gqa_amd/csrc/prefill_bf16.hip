@@ -182,10 +182,17 @@ __global__ __launch_bounds__(kThreads, (DQK > 128 ? 2 : 3)) void prefill_bf16_ke
   }
 
   // ---- per-lane LDS read offsets (elements), identical for every tile ----
-  // K operand: row kb*32 + col, logical chunk 2*kk + hh; the swizzle only sees the row's low 4 bits.
+  // K operand: row kb*32 + col, logical chunk 2*kk + hh. For DQK = 64 / 128 the element offset of
+  // chunk 2kk + hh is kb_lane ^ (16 kk): the XOR key only changes bits below DQK and col * DQK is a
+  // multiple of DQK; 192-dim rows keep one offset per k-step.
   int koff[NQ];
 #pragma unroll
   for (int kk = 0; kk < NQ; ++kk) koff[kk] = col * DQK + swz<CHK>(2 * kk + hh, col) * 8;
+  const int kb_lane = col * DQK + swz<CHK>(hh, col) * 8;
+  auto kaddr = [&](int kk) {
+    if constexpr (DQK <= 128) return kb_lane ^ (16 * kk);
+    else return koff[kk];
+  };
   // V operand (transposing read): rows kb*32 + 16s + 8t + hh*4 + j, dims db*32 + dq*16 + 4c.
   // With row = hh*4 + j (< 8) the swizzle key has bit 3 clear, so the physical chunk of
   // db*4 + x is ((db ^ key>>2) * 4) + (x ^ (key & 3)): only db's parity interacts with the lane,
@@ -256,9 +263,17 @@ __global__ __launch_bounds__(kThreads, (DQK > 128 ? 2 : 3)) void prefill_bf16_ke
     // row's window and past the sinks
     if (causal && kb0 > off + wp0 + 31) return;
     if (kWin && kb0 + 31 < off + wp0 - window + 1 && kb0 >= sinks) return;
-    f32x16 sv = mfma32x32x16(*reinterpret_cast<const bf16x8*>(Kt + koff[0]), qreg[0], f32x16{});
+    // four K operands in flight: the read of k-step kk + 4 is issued behind the product of kk
+    constexpr int R = 4 < NQ ? 4 : NQ;
+    bf16x8 ka[R];
 #pragma unroll
-    for (int kk = 1; kk < NQ; ++kk) sv = mfma32x32x16(*reinterpret_cast<const bf16x8*>(Kt + koff[kk]), qreg[kk], sv);
+    for (int i = 0; i < R; ++i) ka[i] = *reinterpret_cast<const bf16x8*>(Kt + kaddr(i));
+    f32x16 sv = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < NQ; ++kk) {
+      sv = mfma32x32x16(ka[kk % R], qreg[kk], sv);
+      if (kk + R < NQ) ka[kk % R] = *reinterpret_cast<const bf16x8*>(Kt + kaddr(kk + R));
+    }
     // ---- mask (only on blocks crossing the diagonal or the sequence end) ----
     if ((causal && kb0 + 31 > off + wp0) || kb0 + 32 > Sk || (kWin && kb0 < off + wp0 + 32 - window)) {
       const int base = kb0 + hh * 4;  // key of this lane's score offset 0
@@ -306,12 +321,19 @@ __global__ __launch_bounds__(kThreads, (DQK > 128 ? 2 : 3)) void prefill_bf16_ke
     for (int s = 0; s < 2; ++s) {
       const bf16x8 bop = __builtin_bit_cast(bf16x8, U4{pk[s][0], pk[s][1], pk[s][2], pk[s][3]});
       const uint16_t* Vb = Vt + 16 * s * DV;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
+      auto vread = [&](int db) {
         const uint2 lo = lds_read_tr16(Vb + voff_par[db & 1] + vimm(0, db));
         const uint2 hi = lds_read_tr16(Vb + voff_par[db & 1] + vimm(1, db));
-        const bf16x8 aop = __builtin_bit_cast(bf16x8, U4{lo.x, lo.y, hi.x, hi.y});
-        o[db] = mfma32x32x16(aop, bop, o[db]);
+        return __builtin_bit_cast(bf16x8, U4{lo.x, lo.y, hi.x, hi.y});
+      };
+      // two V operands in flight (the read of block db + 2 behind the product of db)
+      bf16x8 va[2];
+      va[0] = vread(0);
+      va[1] = vread(1);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        o[db] = mfma32x32x16(va[db & 1], bop, o[db]);
+        if (db + 2 < NDB) va[db & 1] = vread(db + 2);
       }
     }
   };
