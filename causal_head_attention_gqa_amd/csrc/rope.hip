@@ -6,6 +6,8 @@
 // positions keep full fp32 accuracy after the single rounding of cos/sin. Half-split pairs
 // (i, i + D/2) follow the first page's apply_rope; adjacent pairs (2i, 2i+1) follow
 // "Transformer 架构快速入门" §8.3. Only Q and K are rotated (same page, §8.5).
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace attn {
@@ -57,6 +59,39 @@ __global__ void rope_rotate_table_kernel(const T* __restrict__ src, T* __restric
     const float2 r = rope_rot(a[e], b[e], tb[e]);
     y[i0 + e] = from_f32<T>(r.x);
     y[i0 + D / 2 + e] = from_f32<T>(r.y);
+  }
+}
+
+// bf16 form of the same rotation, for K of shape [B, S, N, D]: a thread owns 8 consecutive pair
+// indices of the rows (b, s, g) for every b, so its 8 (cos, sin) entries are read once and used B
+// times, and it moves whole 16-byte vectors (a wave covers the N*D contiguous elements of one
+// (b, s) for N*D/16 = 64 threads, e.g. N = 8, D = 128).
+__global__ void rope_rotate_table_bf16_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
+                                              const float2* __restrict__ table, int B, int S, int N, int D) {
+  const int groups = D / 16;
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long long)S * N * groups) return;
+  const int i0 = (int)(idx % groups) * 8;
+  const long long sg = idx / groups;  // s * N + g
+  const int pos = (int)(sg / N);
+  const float2* tb = table + (long long)pos * (D / 2) + i0;
+  float2 cs[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) cs[e] = tb[e];
+  for (int b = 0; b < B; ++b) {
+    const long long off = ((long long)b * S * N + sg) * D + i0;
+    const U4 xa = ldg16(src + off), xb = ldg16(src + off + D / 2);
+    const uint32_t wa[4] = {xa.x, xa.y, xa.z, xa.w}, wb[4] = {xb.x, xb.y, xb.z, xb.w};
+    uint32_t ya[4], yb[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float2 r0 = rope_rot(bf16lo(wa[q]), bf16lo(wb[q]), cs[2 * q]);
+      const float2 r1 = rope_rot(bf16hi(wa[q]), bf16hi(wb[q]), cs[2 * q + 1]);
+      ya[q] = pack_bf16x2(r0.x, r1.x);
+      yb[q] = pack_bf16x2(r0.y, r1.y);
+    }
+    stg16(dst + off, U4{ya[0], ya[1], ya[2], ya[3]});
+    stg16(dst + off + D / 2, U4{yb[0], yb[1], yb[2], yb[3]});
   }
 }
 
@@ -192,6 +227,16 @@ hipError_t launch_rope_table(float2* table, int S, int D, double theta, hipStrea
 template <typename T>
 hipError_t launch_rope_rotate_table(const T* src, T* dst, const float2* table, long long rows, int S, int N,
                                     int D, hipStream_t st) {
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    if (D % 16 == 0 && rows % ((long long)S * N) == 0) {
+      const long long n = (long long)S * N * (D / 16);
+      if (n == 0) return hipSuccess;
+      rope_rotate_table_bf16_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(
+          reinterpret_cast<const uint16_t*>(src), reinterpret_cast<uint16_t*>(dst), table, (int)(rows / ((long long)S * N)),
+          S, N, D);
+      return hipGetLastError();
+    }
+  }
   const long long n = rows * (D / 16);
   if (n == 0) return hipSuccess;
   rope_rotate_table_kernel<T><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(src, dst, table, rows,
