@@ -79,6 +79,7 @@ def test_decode_argument_errors():
     assert call(ldk=64) == 1                    # row pitch shorter than the row
     assert call(Dqk=96, Dv=96, ldk=96, ldv=96) == 2
     assert call(dt=0) == 2                      # fp32 decode is not built
+    assert call(Nh=24, Nkv=1) == 2              # more than 16 heads per KV head only in groups of 16
     assert call(Dqk=576, Dv=512, Nkv=1, Nh=128, ldk=576, ldv=576, vc=P + 4096) == 2  # MLA needs V aliasing K
     assert call(Dqk=576, Dv=512, Nkv=1, Nh=128, ldk=576, ldv=576, rope=1e4) == 3  # decoupled RoPE: supported
     assert call() == 3                          # no workspace

@@ -46,7 +46,9 @@ GQA_CASES = [
     (3, 32, 8, 128, 1500, [1, 777, 1500], 0.0),
     (4, 8, 8, 128, 600, None, 0.0),       # MHA
     (2, 16, 2, 64, 2049, [2049, 513], 0.0),  # group of 8
-    (5, 12, 1, 128, 300, None, 0.0),      # MQA with 12 heads -> groups of 4
+    (5, 12, 1, 128, 300, None, 0.0),      # MQA with 12 heads: one group of 12
+    (2, 32, 1, 128, 700, [700, 129], 0.0),  # MQA with 32 heads: two groups of 16 per KV head
+    (2, 64, 2, 64, 520, [520, 300], 1e4),   # 32 query heads per KV head, RoPE
     (2, 32, 8, 128, 900, [900, 17], 5e5),  # q rotated at ctx-1
     (3, 6, 2, 64, 100, [1, 2, 64], 1e4),
 ]
