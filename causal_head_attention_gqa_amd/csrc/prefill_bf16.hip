@@ -23,8 +23,12 @@
 //   - online softmax per 32-key block ("Transformer 架构完全深度解析" §十三: running max and sum;
 //     the output accumulator is rescaled by the same factor, and only when some row's max
 //     moved).
+//   - K and V operands are read from LDS through small register rings (four K and two V reads in
+//     flight), so the products rarely wait on an LDS read.
 // All per-wave control values are scalar (wave-uniform branches); per-lane LDS and global
-// offsets are computed once. Grid order puts the work-groups with the most tiles first.
+// offsets are computed once. Grid order puts the work-groups with the most tiles first, head
+// groups fastest: work-group i runs on XCD i % 8, so when B * Nh / HPW is a multiple of 8 every
+// q-tile of one (sequence, KV head) runs on the same XCD and its K/V stay in that XCD's L2.
 #include <type_traits>
 
 #include "kernels.hpp"
