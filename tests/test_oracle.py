@@ -308,6 +308,11 @@ def test_prefill_flop_count():
     assert accounting.prefill_flops(4, 8192, 32, 128, causal=True) == 2_199_291_691_008
     assert accounting.prefill_flops(8, 1024, 12, 64, causal=True) == 12_897_484_800
     assert accounting.prefill_flops(1, 3, 1, 4, causal=False) == 4 * 4 * 9
+    # MLA non-absorbed prefill: 2 * (192 + 128) FLOPs per pair; the attention FLOP ratio of the absorbed
+    # form ([P4] slide 06: about 3.4x) is the ratio of these per-pair counts
+    mla = accounting.prefill_flops(1, 4096, 128, 192, causal=True, Dv=128)
+    assert mla == 2 * 320 * 128 * (4096 * 4097 // 2)
+    assert round(2 * (576 + 512) / (2 * (192 + 128)), 1) == round(accounting.mla_absorbed_flop_ratio(), 1) == 3.4
 
 
 # ------------------------------------------------------------------ prefill against a cache --
