@@ -12,7 +12,8 @@ dense bf16 matrix peak; decode in algorithmic GB/s (each needed cache row once, 
 against HBM peak. The headline value is the mean of the two fractions, in percent.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--only PART]
-Prints one JSON line.
+Prints one JSON line. `--extras` instead measures the widened rows (chunked prefill with RoPE + cache
+append, RoPE variants, sliding window with sinks) on the same prefill shape, one JSON line each.
 """
 from __future__ import annotations
 
@@ -45,6 +46,9 @@ def parse():
                    help="time a single part (profiling runs); the JSON line then reports that part")
     p.add_argument("--copy-probe", action="store_true",
                    help="run only a plain 1 GiB device-to-device copy (calibrates the HBM byte counters)")
+    p.add_argument("--extras", action="store_true",
+                   help="measure the widened rows instead (chunked prefill with cache append, sliding window "
+                        "with sinks, RoPE variants): one JSON line each")
     return p.parse_args()
 
 
@@ -171,6 +175,103 @@ def prefill_traffic():
                 + rec["write_size_kib_per_dispatch"] * rec["write_scale"]) * 1024)
 
 
+# ---------------------------------------------------------------------------------- extras ----
+def window_pairs(S: int, window: int, sinks: int) -> int:
+    """Visible (query, key) pairs of causal attention with a window of `window` keys plus `sinks`."""
+    p = np.arange(S, dtype=np.int64)
+    inside = np.minimum(p + 1, window)
+    extra = np.clip(np.minimum(sinks, p - window + 1), 0, None)
+    return int((inside + extra).sum())
+
+
+def run_extras(torch, attn, steps: int, warmup: int):
+    """The Llama-3-8B-shaped prefill (B=4, S=8192, 32/8 heads of 128, RoPE 5e5) done the other ways the
+    library offers, each priced by its own algorithmic FLOPs (or bytes for the cache append)."""
+    P = synth.LLAMA3_PREFILL
+    B, S, Nh, Nkv, Dh, theta = P.B, P.S, P.Nh, P.Nkv, P.Dh, P.rope_theta
+    C = 2048  # chunk length of the chunked prefill
+    q = device_normal(torch, (B, S, Nh, Dh), 1000 * P.wid + 0)
+    k = device_normal(torch, (B, S, Nkv, Dh), 1000 * P.wid + 1)
+    v = device_normal(torch, (B, S, Nkv, Dh), 1000 * P.wid + 2)
+    qc = [q[:, c:c + C].contiguous() for c in range(0, S, C)]
+    kc_ = [k[:, c:c + C].contiguous() for c in range(0, S, C)]
+    vc_ = [v[:, c:c + C].contiguous() for c in range(0, S, C)]
+    starts = [torch.full((B,), c, dtype=torch.int32, device="cuda") for c in range(0, S, C)]
+    zero = torch.zeros((B,), dtype=torch.int32, device="cuda")
+    kcache = torch.empty((B, S, Nkv, Dh), dtype=torch.bfloat16, device="cuda")
+    vcache = torch.empty_like(kcache)
+    out = torch.empty_like(q)
+    outc = [torch.empty_like(t) for t in qc]
+    ws = torch.empty(max(1, attn.prefill_cached_workspace_bytes(S, Dh, theta)), dtype=torch.uint8, device="cuda")
+    pws = torch.empty(max(1, attn.prefill_workspace_bytes(B, S, Nkv, Dh, theta, attn.ATTN_BF16)),
+                      dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for e0, e1 in ev:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+
+    flops_causal = acc.prefill_flops(B, S, Nh, Dh, causal=True)
+    workload = f"Llama-3-8B GQA prefill B{B} S{S} Nh{Nh} Nkv{Nkv} Dh{Dh} RoPE{theta:g}"
+    lines = []
+
+    def emit(name, ms, work, unit, peak, extra):
+        rate = work / (ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
+        lines.append({"extra": name, "workload": workload, **extra, "ms": ms, "achieved": rate, "unit": unit,
+                      "peak": peak, "frac": rate / peak})
+
+    # whole-sequence prefill, as the reference point of the rows below
+    ms_whole = timed(lambda: attn.prefill(q, k, v, rope_theta=theta, out=out, workspace=pws))
+    emit("whole_prefill", ms_whole, flops_causal, "TFLOP/s", acc.PEAK_BF16_TFLOPS, {})
+
+    # chunked prefill: per chunk, RoPE + append of its K/V to the cache, then its queries against the cache
+    def appends(rope_dims=0, inter=False):
+        for i in range(len(qc)):
+            attn.kv_append(kc_[i], vc_[i], kcache, vcache, starts[i], rope_theta=theta, rope_dims=rope_dims,
+                           interleaved=inter)
+
+    def chunked(rope_dims=0, inter=False):
+        for i in range(len(qc)):
+            attn.kv_append(kc_[i], vc_[i], kcache, vcache, starts[i], rope_theta=theta, rope_dims=rope_dims,
+                           interleaved=inter)
+            attn.prefill_cached(qc[i], kcache, vcache, starts[i], rope_theta=theta, rope_dims=rope_dims,
+                                rope_interleaved=inter, out=outc[i], workspace=ws)
+
+    ms_chunk = timed(chunked)
+    emit("chunked_prefill", ms_chunk, flops_causal, "TFLOP/s", acc.PEAK_BF16_TFLOPS,
+         {"chunks": S // C, "chunk_len": C, "includes": "RoPE + cache append of each chunk"})
+    ms_app = timed(appends)
+    app_bytes = 2 * 2 * B * S * Nkv * Dh * 2  # K and V: read the new rows, write the cache rows
+    emit("kv_append", ms_app / (S // C), app_bytes // (S // C), "GB/s", acc.PEAK_HBM_GBS,
+         {"rows_per_call": B * C * Nkv, "note": "per call of one 2048-token chunk"})
+
+    # RoPE variants on the same chunked prefill (q rotated in registers, keys at append)
+    for name, rd, inter in (("rope_adjacent_pairs", 0, True), ("rope_partial_64", 64, False)):
+        ms_v = timed(lambda rd=rd, inter=inter: chunked(rd, inter))
+        emit(name, ms_v, flops_causal, "TFLOP/s", acc.PEAK_BF16_TFLOPS,
+             {"chunks": S // C, "rope_dims": rd or Dh, "pairs": "adjacent" if inter else "half-split"})
+
+    # sliding window with attention sinks over the whole sequence (cache filled beforehand)
+    appends()
+    torch.cuda.synchronize()
+    W, sinks = 4096, 4
+    pairs = window_pairs(S, W, sinks)
+    ms_w = timed(lambda: attn.prefill_cached(q, kcache, vcache, zero, rope_theta=theta, window=W, sinks=sinks,
+                                              out=out, workspace=ws))
+    emit("sliding_window", ms_w, 4 * Dh * B * Nh * pairs, "TFLOP/s", acc.PEAK_BF16_TFLOPS,
+         {"window": W, "sinks": sinks, "visible_pairs_per_head": pairs})
+    for ln in lines:
+        print(json.dumps(ln))
+
+
 # ------------------------------------------------------------------------------------ main ----
 def main():
     args = parse()
@@ -181,6 +282,10 @@ def main():
     import torch
     if args.copy_probe:
         copy_probe(torch)
+        return
+    if args.extras:
+        import causal_head_attention_gqa_amd as attn
+        run_extras(torch, attn, args.steps, args.warmup)
         return
     import causal_head_attention_gqa_amd as attn
     P, D, M = synth.LLAMA3_PREFILL, synth.LLAMA3_DECODE, synth.MLA_DECODE

@@ -162,9 +162,12 @@ __global__ void rope_apply_kernel(T* __restrict__ x, const int* __restrict__ pos
 // KV-cache append with RoPE fused ("Transformer 架构完全深度解析" §九: new K/V are concatenated to
 // the cache; K is rotated at its absolute position first, "2.7 ..." §4, "Transformer 架构快速入门"
 // §8.2 for a rotary span of Dr <= D dims). Token s of sequence b goes to cache row
-// t = start[b] + s (clamped to max_ctx - S). One thread per (token, KV head, 8 consecutive dims):
-// copies those 8 dims of V, and of K outside the rotary span; inside it, each output element is
-// its pair's rotation (rope_cs / rope_rot, the same bits as the prefill's key pre-pass).
+// t = start[b] + s (clamped to max_ctx - S). One thread per (token, 8 consecutive dims), looping
+// over the KV heads: the (cos, sin) of its dims' pairs are computed once per token, not per head.
+// It copies those 8 dims of V, and of K outside the rotary span; inside it, each output element
+// is its pair's rotation (rope_cs / rope_rot, the same bits as the prefill's key pre-pass).
+// kVec: every pointer and row pitch allows 16-byte accesses, so the 8 dims move as one vector.
+template <bool kVec>
 __global__ void kv_append_kernel(const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
                                  uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
                                  const int* __restrict__ start, int B, int S, int Nkv, int D, int max_ctx,
@@ -172,47 +175,83 @@ __global__ void kv_append_kernel(const uint16_t* __restrict__ k_new, const uint1
                                  int interleaved) {
   const int groups = D / 8;
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (long long)B * S * Nkv * groups) return;
+  if (idx >= (long long)B * S * groups) return;
   const int d0 = (int)(idx % groups) * 8;
-  const long long row = idx / groups;  // (b * S + s) * Nkv + g
-  const int g = (int)(row % Nkv);
-  const long long tok = row / Nkv;
+  const long long tok = idx / groups;  // b * S + s
   const int s = (int)(tok % S);
   const int b = (int)(tok / S);
   const int t = min(max(start[b], 0), max_ctx - S) + s;
-  const uint16_t* kx = k_new + row * D;
-  const uint16_t* vx = v_new + row * D;
-  uint16_t* ky = kc + ((long long)b * max_ctx + t) * Nkv * ldk + (long long)g * ldk;
-  uint16_t* vy = vc + ((long long)b * max_ctx + t) * Nkv * ldv + (long long)g * ldv;
   const int half = Dr / 2;
+  // per dim: rotated or copied; the pair (da, db) holding it and whether it is the pair's first
+  float2 cs[8];
+  int partner[8];
+  bool rot[8], first[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int d = d0 + e;
-    vy[d] = vx[d];
-    if (!rope || d >= Dr) {
-      ky[d] = kx[d];
-      continue;
+    rot[e] = rope && d < Dr;
+    first[e] = interleaved ? (d & 1) == 0 : d < half;
+    const int da = first[e] ? d : (interleaved ? d - 1 : d - half);
+    partner[e] = first[e] ? (interleaved ? da + 1 : da + half) : da;
+    cs[e] = rot[e] ? rope_cs(t, interleaved ? da / 2 : da, neg2_log2theta_over_dr) : make_float2(1.f, 0.f);
+  }
+  for (int g = 0; g < Nkv; ++g) {
+    const long long row = tok * Nkv + g;
+    const uint16_t* kx = k_new + row * D;
+    const uint16_t* vx = v_new + row * D;
+    uint16_t* ky = kc + ((long long)b * max_ctx + t) * Nkv * ldk + (long long)g * ldk;
+    uint16_t* vy = vc + ((long long)b * max_ctx + t) * Nkv * ldv + (long long)g * ldv;
+    uint16_t own[8], res[8];
+    if constexpr (kVec) {
+      stg16(vy + d0, ldg16(vx + d0));
+      const U4 w = ldg16(kx + d0);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) own[e] = (uint16_t)(ws[e >> 1] >> (16 * (e & 1)));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        vy[d0 + e] = vx[d0 + e];
+        own[e] = kx[d0 + e];
+      }
     }
-    // the pair (da, db) holding d, its index i, and whether d is the pair's first element
-    const bool first = interleaved ? (d & 1) == 0 : d < half;
-    const int da = first ? d : (interleaved ? d - 1 : d - half);
-    const int db = interleaved ? da + 1 : da + half;
-    const int i = interleaved ? da / 2 : da;
-    const float2 r = rope_rot(bf16_to_f32(kx[da]), bf16_to_f32(kx[db]), rope_cs(t, i, neg2_log2theta_over_dr));
-    ky[d] = f32_to_bf16(first ? r.x : r.y);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (!rot[e]) {
+        res[e] = own[e];
+        continue;
+      }
+      const uint16_t other = kx[partner[e]];
+      const float2 r = first[e] ? rope_rot(bf16_to_f32(own[e]), bf16_to_f32(other), cs[e])
+                                : rope_rot(bf16_to_f32(other), bf16_to_f32(own[e]), cs[e]);
+      res[e] = f32_to_bf16(first[e] ? r.x : r.y);
+    }
+    if constexpr (kVec) {
+      stg16(ky + d0, U4{res[0] | (uint32_t(res[1]) << 16), res[2] | (uint32_t(res[3]) << 16),
+                        res[4] | (uint32_t(res[5]) << 16), res[6] | (uint32_t(res[7]) << 16)});
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ky[d0 + e] = res[e];
+    }
   }
 }
 
 hipError_t launch_kv_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* kc, uint16_t* vc,
                             const int* start, int B, int S, int Nkv, int D, int max_ctx, long long ldk, long long ldv,
                             double theta, int Dr, int interleaved, hipStream_t st) {
-  const long long n = (long long)B * S * Nkv * (D / 8);
+  const long long n = (long long)B * S * (D / 8);
   if (n == 0) return hipSuccess;
   const bool rope = theta > 0.0;
   const double k = rope ? -2.0 * log2(theta) / (double)Dr : 0.0;
-  kv_append_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(k_new, v_new, kc, vc, start, B, S, Nkv, D,
-                                                                           max_ctx, ldk, ldv, k, rope ? 1 : 0, Dr,
-                                                                           interleaved ? 1 : 0);
+  const auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  const bool vec = a16(k_new) && a16(v_new) && a16(kc) && a16(vc) && ldk % 8 == 0 && ldv % 8 == 0;
+  const dim3 grid((unsigned)((n + 255) / 256)), block(256);
+  if (vec)
+    kv_append_kernel<true><<<grid, block, 0, st>>>(k_new, v_new, kc, vc, start, B, S, Nkv, D, max_ctx, ldk, ldv, k,
+                                                   rope ? 1 : 0, Dr, interleaved ? 1 : 0);
+  else
+    kv_append_kernel<false><<<grid, block, 0, st>>>(k_new, v_new, kc, vc, start, B, S, Nkv, D, max_ctx, ldk, ldv, k,
+                                                    rope ? 1 : 0, Dr, interleaved ? 1 : 0);
   return hipGetLastError();
 }
 
