@@ -215,13 +215,28 @@ __global__ void kv_append_kernel(const uint16_t* __restrict__ k_new, const uint1
         own[e] = kx[d0 + e];
       }
     }
+    // partners of a fully rotated group: inside its own chunk (adjacent pairs), or one 16-byte chunk
+    // half a span away (half-split with half % 8 == 0); otherwise one element at a time
+    uint16_t pv[8];
+    const bool grp = kVec && rope && d0 + 8 <= Dr && (interleaved || half % 8 == 0);
+    if (grp) {
+      if (interleaved) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = own[e ^ 1];
+      } else {
+        const U4 w2 = ldg16(kx + (d0 < half ? d0 + half : d0 - half));
+        const uint32_t ps[4] = {w2.x, w2.y, w2.z, w2.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pv[e] = (uint16_t)(ps[e >> 1] >> (16 * (e & 1)));
+      }
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       if (!rot[e]) {
         res[e] = own[e];
         continue;
       }
-      const uint16_t other = kx[partner[e]];
+      const uint16_t other = grp ? pv[e] : kx[partner[e]];
       const float2 r = first[e] ? rope_rot(bf16_to_f32(own[e]), bf16_to_f32(other), cs[e])
                                 : rope_rot(bf16_to_f32(other), bf16_to_f32(own[e]), cs[e]);
       res[e] = f32_to_bf16(first[e] ? r.x : r.y);
