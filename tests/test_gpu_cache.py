@@ -65,6 +65,27 @@ def test_kv_append_rotates_and_places(D, interleaved, rope, rdims):
     assert np.all(kc_full[..., D:].float().cpu().numpy() == 1.0)
 
 
+@pytest.mark.parametrize("D,interleaved,rdims", [(128, False, 0), (64, True, 0), (128, False, 36)])
+def test_kv_append_scalar_path_gives_the_vector_paths_bits(D, interleaved, rdims):
+    """A row pitch of D + 2 elements rules out 16-byte accesses, so the append takes its element-wise
+    path; its rows must carry the same bits as the 16-byte path's (which the test above pins to the
+    oracle). rdims = 36 (half = 18) also makes the 16-byte path fetch partners one by one."""
+    import causal_head_attention_gqa_amd as attn
+    torch = _torch()
+    B, S, Nkv, T = 2, 21, 2, 64
+    start = torch.as_tensor(np.array([3, 40], np.int32), device="cuda")
+    kn = to_dev(synth.normal(820 + D, 0, (B, S, Nkv, D), "bf16"), "bf16")
+    vn = to_dev(synth.normal(820 + D, 1, (B, S, Nkv, D), "bf16"), "bf16")
+    caches = []
+    for ld in (D, D + 2):
+        kc, _ = _empty_cache(B, T, Nkv, D, ld=ld)
+        vc, _ = _empty_cache(B, T, Nkv, D, ld=ld)
+        attn.kv_append(kn, vn, kc, vc, start, rope_theta=1e4, rope_dims=rdims, interleaved=interleaved)
+        caches.append((_bits(kc.contiguous()), _bits(vc.contiguous())))
+    assert np.array_equal(caches[0][0], caches[1][0])
+    assert np.array_equal(caches[0][1], caches[1][1])
+
+
 CHUNK_CASES = [
     # B, S, Nh, Nkv, D, T, starts, rope, causal
     (2, 33, 8, 2, 128, 128, [0, 45], 5e5, True),
