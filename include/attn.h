@@ -22,8 +22,8 @@
  *     Arguments are validated on the host BEFORE any launch; on an error nothing is launched
  *     and no output is touched. Launch failures are reported as ATTN_ERR_HIP. Faults inside a
  *     kernel surface at the caller's next synchronisation, as for any HIP kernel.
- *   - Tensor pointers must be 16-byte aligned (ATTN_ERR_INVALID otherwise); rope_apply only
- *     needs element alignment.
+ *   - Tensor pointers must be 16-byte aligned (ATTN_ERR_INVALID otherwise); rope_apply and
+ *     attn_kv_append only need element alignment.
  *   - No C++ exception crosses this interface.
  */
 #ifndef ATTN_GFX950_H
@@ -153,7 +153,9 @@ int attn_prefill_cached(const void* q, const void* kcache, const void* vcache, c
  *          rope_theta^(-2i/rope_dims), pairs (i, i + rope_dims/2), or (2i, 2i + 1) with
  *          interleaved != 0; the other dims are copied. rope_theta <= 0 copies K unchanged.
  *          V is copied unchanged.
- * Supported: ATTN_BF16, Dh % 8 == 0 and Dh <= 1024, 1 <= S <= max_ctx.
+ * Supported: ATTN_BF16, Dh % 8 == 0 and Dh <= 1024, 1 <= S <= max_ctx. With every pointer
+ *          16-byte aligned and ldk, ldv multiples of 8 the rows move as 16-byte vectors, otherwise
+ *          element by element; both give the same bits.
  * A key appended here and a key rotated by attn_prefill's RoPE step carry identical bits.
  * ------------------------------------------------------------------------------------------ */
 int attn_kv_append(const void* k_new, const void* v_new, void* kcache, void* vcache, const int32_t* start,
