@@ -35,9 +35,9 @@ DecodePlan decode_plan(int B, int Nh, int Nkv, int Dqk, int Dv, int max_ctx) {
   p.mla = is_mla_shape(Nkv, Dqk, Dv);
   if (max_ctx <= 0 || B <= 0) return p;
   if (p.mla) {
-    // one 8/4/2/1-wave work-group per (sequence, 16*waves heads, chunk); its 108 KiB LDS ring
-    // allows one per CU, so aim for about 256 work-groups
-    const long long groups = (long long)B * (Nh / (16 * mla_waves_per_group(Nh)));
+    // one work-group per (sequence, head group, chunk); one such work-group fills a CU (64-head
+    // groups: 124 KiB of LDS, one wave per SIMD), so aim for about 256 work-groups
+    const long long groups = (long long)B * (Nh / mla_heads_per_group(Nh));
     const int tiles = (max_ctx + 31) / 32;
     long long want = (256 + groups - 1) / groups;  // about one work-group per CU
     if (want > tiles) want = tiles;

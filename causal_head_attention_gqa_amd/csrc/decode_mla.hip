@@ -258,6 +258,370 @@ __global__ __launch_bounds__(NW * 64, (NW >= 8 ? 2 : 1)) void decode_mla_kernel(
   }
 }
 
+// ---- 32 heads per wave pair (head counts that are multiples of 64) ----
+//
+// A work-group = 4 waves (one per SIMD) owns (sequence, 64 heads, one context chunk). Waves 2p and
+// 2p+1 form a pair that shares heads 32p .. 32p+31 of the group:
+//   - Q.K: wave 2p+r (r = 0, 1) contracts dims 288r .. 288r+287 of its 32 heads against a 32-token
+//     tile (S^T = K Q^T on v_mfma_f32_32x32x16_bf16, 18 k-steps), writes the 32x32 partial scores
+//     to LDS, and after a barrier adds its partner's: both waves then hold the same full scores
+//     (fp32 addition is commutative, so the two sums are bit-identical) and run the same online
+//     softmax;
+//   - P.V: wave 2p+r accumulates O^T for output dims 256r .. 256r+255 of the pair's 32 heads
+//     (16 products per tile, V^T read from the same row-major tile by the transposing LDS read).
+// Per lane this needs 72 query registers and 128 accumulator registers, so one wave per SIMD
+// keeps everything in registers. Each tile operand read from LDS feeds a 32-wide product, half the
+// LDS traffic per FLOP of the 16-heads-per-wave form above, which is bound by those reads.
+// The two head groups of a 128-head sequence chunk are dispatched 8 ids apart, i.e. to the same
+// XCD at about the same time, so the second read of each cache row is served by that XCD's L2.
+namespace pair {
+constexpr int kWaves = 4;
+constexpr int kHeads = 64;               // heads per work-group
+constexpr int kStages = 3;               // LDS ring: tiles j+1 and j+2 load while j is computed
+constexpr int kSPW = NSLOT / kWaves;     // 9 tile-load instructions per wave and tile
+constexpr int kHalfQ = DQ / 2;           // 288 reduction dims per wave
+constexpr int kKS = kHalfQ / 16;         // 18 k-steps of 16 dims
+constexpr int kDB = DV / 2 / 32;         // 8 output blocks of 32 dims per wave
+static_assert(NSLOT % kWaves == 0, "tile loads split evenly over the waves");
+
+// XOR key of the 16-byte chunk index in tile row `row` (only the low 3 bits of the chunk change,
+// so a chunk stays in its aligned group of 8): row bits 1, 2, 3 -> key bits 2, 1, 0. The 1152-byte
+// row pitch puts odd rows half a bank line (128 B) away from even rows. K operand reads (128-bit,
+// 32 consecutive rows, one chunk per half-wave): a 16-lane pass covers 16 distinct values of
+// row & 15, which the key and the row parity send to 16 distinct 16-byte bank groups.
+// Transposing V reads (64-bit, 4 consecutive rows x 64 contiguous bytes per 16-lane group):
+// row bit 1 selects the other half of the chunk group and row bit 0 the other half bank line, so
+// each 32-lane pass hits 32 distinct 8-byte bank groups.
+__device__ __forceinline__ int key(int row) {
+  return (((row >> 1) & 1) << 2) | (((row >> 2) & 1) << 1) | ((row >> 3) & 1);
+}
+
+// decoupled RoPE of one lane's q^R pairs: dims 512 + i held in `a` (i = i0 .. i0+7), their
+// half-split partners 544 + i in `b`; frequency theta^(-2i/64), position pos
+__device__ __forceinline__ void rope_qr(U4& a, U4& b, int i0, int pos, double theta) {
+  const double k2 = -2.0 * log2(theta) / (double)(DQ - DV);
+  uint32_t* pa = &a.x;
+  uint32_t* pb = &b.x;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float ra[2], rb[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      double sn, cs;
+      sincos((double)pos * exp2(k2 * (double)(i0 + 2 * e + hf)), &sn, &cs);
+      const double x = hf ? bf16hi(pa[e]) : bf16lo(pa[e]);
+      const double y = hf ? bf16hi(pb[e]) : bf16lo(pb[e]);
+      ra[hf] = (float)(x * cs - y * sn);
+      rb[hf] = (float)(x * sn + y * cs);
+    }
+    pa[e] = pack_bf16x2(ra[0], ra[1]);
+    pb[e] = pack_bf16x2(rb[0], rb[1]);
+  }
+}
+
+__global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_pair_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[kStages][TILE];
+  __shared__ __attribute__((aligned(16))) float xch[kWaves][4][64][4];  // partial scores per wave
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = w & 1;         // reduction half of Q.K / output half of P.V
+  const int hf = lane >> 5;    // half-wave: k-slot group of the MFMA operands
+  const int col = lane & 31;   // head within the pair (MFMA column)
+  // id -> (pair = (b, split), head group): the head groups of a pair sit 8 ids apart (one XCD)
+  const int n_hg = a.Nh / kHeads;
+  const int n_pairs = a.B * a.nsplit;
+  const int id = blockIdx.x;
+  const int sp_id = (id / 8 / n_hg) * 8 + id % 8;
+  const int hgrp = (id / 8) % n_hg;
+  if (sp_id >= n_pairs) return;
+  const int b = sp_id / a.nsplit;
+  const int s = sp_id % a.nsplit;
+  const int ctx = min(max(a.ctx_lens[b], 0), a.max_ctx);
+  const int t0 = s * a.chunk;
+  if (t0 >= ctx) return;
+  const int t1 = min(ctx, t0 + a.chunk);
+  const int h = hgrp * kHeads + (w >> 1) * 32 + col;
+
+  // Q^T operand of k-step kk: head h, dims 288r + 16kk + 8hf .. +7
+  bf16x8 qreg[kKS];
+  {
+    const uint16_t* qp = a.q + ((long long)b * a.Nh + h) * DQ + r * kHalfQ + hf * 8;
+    U4 raw[kKS];
+#pragma unroll
+    for (int kk = 0; kk < kKS; ++kk) raw[kk] = ldg16(qp + kk * 16);
+    if (a.rope_theta > 0 && r == 1) {
+      // q^R = dims 512..575 = k-steps 14..17 of the upper half: dims 512 + 16u + 8hf + j in
+      // raw[14 + u], their partners 544 + 16u + 8hf + j in raw[16 + u]
+      rope_qr(raw[14], raw[16], hf * 8, ctx - 1, a.rope_theta);
+      rope_qr(raw[15], raw[17], 16 + hf * 8, ctx - 1, a.rope_theta);
+    }
+#pragma unroll
+    for (int kk = 0; kk < kKS; ++kk) qreg[kk] = as_bf16x8(raw[kk]);
+    retire_vmem();  // from here on only the tile loads count in vmcnt
+  }
+
+  f32x16 o[kDB];
+#pragma unroll
+  for (int i = 0; i < kDB; ++i) o[i] = f32x16{};
+  float m = 0.f, lsum = 0.f;
+  bool ovf = false;
+  constexpr float kOvf = 64.f;
+
+  // ---- per-lane LDS offsets (elements) ----
+  // K operand of k-step kk: row col, logical chunk c0 + 2kk with c0 = 36r + hf; the key changes
+  // only the low 3 bits, so (c0 + 2(kk&3) + 8(kk>>2)) ^ key = ((c0 + 2(kk&3)) ^ key) + 8(kk>>2).
+  const int kkey = key(col);
+  int koff[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) koff[u] = col * DQ + (((36 * r + hf + 2 * u) ^ kkey) << 3);
+  // V operand (transposing read) of (ks, t, db): 16-lane group (dq, hf), lane (tj, tc) addresses
+  // row 16ks + 8t + 4hf + tj, dims 256r + 32db + 16dq + 4tc, i.e. logical chunk
+  // 32r + 4db + x with x = 2dq + (tc >> 1). The row's key is (tj>>1)<<2 | hf<<1 | t, so the physical
+  // chunk is 32r + 4(db ^ (tj>>1)) + (x ^ 2hf ^ t): one register per (db parity, t) plus an
+  // immediate (16ks + 8t) * 576 + 32 (db & ~1).
+  const int tj = (lane & 15) >> 2, tc = lane & 3, dq = (lane >> 4) & 1;
+  const int x = 2 * dq + (tc >> 1);
+  int vb[2][2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      vb[par][t] = (4 * hf + tj) * DQ + 8 * (32 * r + 4 * (par ^ (tj >> 1)) + (x ^ (2 * hf) ^ t)) + (tc & 1) * 4;
+
+  // ---- tile loads: wave w fills slots w*9 .. w*9+8; lane i of slot sl covers tile bytes
+  // sl*1024 + 16i = row*1152 + 16pc and fetches logical chunk pc ^ key(row) of that row ----
+  const long long ldk = a.ldk;  // Nkv == 1
+  const uint16_t* seq = a.kc + (long long)b * a.max_ctx * ldk;
+  int lrow[kSPW], lchk[kSPW];
+#pragma unroll
+  for (int u = 0; u < kSPW; ++u) {
+    const int ob = (w * kSPW + u) * 1024 + 16 * lane;
+    lrow[u] = ob / (DQ * 2);
+    lchk[u] = ((ob % (DQ * 2)) / 16) ^ key(ob / (DQ * 2));
+  }
+  const int n_tiles = (t1 - t0 + TT - 1) / TT;
+  auto issue_tile = [&](int j, uint16_t* dst) {
+    const int tb = t0 + j * TT;
+#pragma unroll
+    for (int u = 0; u < kSPW; ++u) {
+      const int t = min(tb + lrow[u], t1 - 1);  // rows past the chunk re-read a valid row (masked)
+      load_lds16_async<false>(seq + (long long)t * ldk + lchk[u] * 8, dst + (w * kSPW + u) * 512);
+    }
+  };
+
+  auto compute_tile = [&](int j, const uint16_t* T) {
+    // partial S^T[32 tokens x 32 heads] over this wave's 288 dims: two independent accumulation
+    // chains (even / odd k-steps) and kKR K operands in flight, since one wave per SIMD has no
+    // other wave to hide the product and LDS latencies behind
+    constexpr int kKR = 4;
+    auto kread = [&](int kk) { return *reinterpret_cast<const bf16x8*>(T + koff[kk & 3] + 64 * (kk >> 2)); };
+    bf16x8 ka[kKR];
+#pragma unroll
+    for (int u = 0; u < kKR; ++u) ka[u] = kread(u);
+    f32x16 sv2[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int kk = 0; kk < kKS; ++kk) {
+      sv2[kk & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk % kKR], qreg[kk], sv2[kk & 1], 0, 0, 0);
+      if (kk + kKR < kKS) ka[kk % kKR] = kread(kk + kKR);
+    }
+    f32x16 sv = sv2[0] + sv2[1];
+    // exchange with the partner wave (w ^ 1): same lane = same head and tokens
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<f32x4*>(&xch[w][g][lane][0]) = f32x4{sv[4 * g], sv[4 * g + 1], sv[4 * g + 2], sv[4 * g + 3]};
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 pv = *reinterpret_cast<const f32x4*>(&xch[w ^ 1][g][lane][0]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[4 * g + i] += pv[i];
+    }
+    // token of score i: tile base + 8(i>>2) + 4hf + (i&3)
+    const int tbase = t0 + j * TT;
+    if (tbase + TT > t1) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (tbase + (i >> 2) * 8 + hf * 4 + (i & 3) >= t1) sv[i] = -INFINITY;
+    }
+    float mt = sv[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mt = fmaxf(mt, sv[i]);
+    mt = pair_max32(mt);
+    // fixed reference max: the first tile's max per head; a later score may exceed it by up to
+    // 2^kOvf (p, the sums and O stay finite in fp32 and bf16); beyond that the head is flagged and
+    // recomputed exactly after the loop
+    const float mb = mt * a.scale_log2;
+    if (j == 0) m = mb;
+    ovf |= mb > m + kOvf;
+    uint32_t pk[2][4];
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      const float e0 = fast_exp2(fmaf(sv[i], a.scale_log2, -m));
+      const float e1 = fast_exp2(fmaf(sv[i + 1], a.scale_log2, -m));
+      psum += e0 + e1;
+      pk[i >> 3][(i & 7) >> 1] = pack_bf16x2(e0, e1);
+    }
+    lsum += psum;
+    // O^T[256 dims x 32 heads] += V^T P^T; two V operands in flight
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 bop = __builtin_bit_cast(bf16x8, U4{pk[ks][0], pk[ks][1], pk[ks][2], pk[ks][3]});
+      auto vread = [&](int db) {
+        const uint16_t* p = T + (16 * ks) * DQ + 32 * (db & ~1);
+        const uint2 lo = lds_read_tr16(p + vb[db & 1][0]);
+        const uint2 hi = lds_read_tr16(p + 8 * DQ + vb[db & 1][1]);
+        return __builtin_bit_cast(bf16x8, U4{lo.x, lo.y, hi.x, hi.y});
+      };
+      constexpr int kVR = 4;  // V operands in flight
+      bf16x8 va[kVR];
+#pragma unroll
+      for (int u = 0; u < kVR; ++u) va[u] = vread(u);
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db % kVR], bop, o[db], 0, 0, 0);
+        if (db + kVR < kDB) va[db % kVR] = vread(db + kVR);
+      }
+    }
+  };
+
+  // ---- ring of 3 stages; a load past the last tile re-reads the last one into a stage that is
+  // never read again, so every step keeps one fixed vmcnt. One loop body with the stage picked by
+  // a scalar index: the accumulators then keep one register assignment through the loop. ----
+  issue_tile(0, ring[0]);
+  issue_tile(min(1, n_tiles - 1), ring[1]);
+  int cur = 0;
+  for (int j = 0; j < n_tiles; ++j) {
+    wait_vmem_n<kSPW>();
+    barrier_only();
+    const int nxt = cur == 0 ? 2 : cur - 1;  // (j + 2) % 3
+    issue_tile(min(j + 2, n_tiles - 1), ring[nxt]);
+    compute_tile(j, ring[cur]);
+    cur = cur == 2 ? 0 : cur + 1;
+  }
+  wait_vmem();  // the re-reads must land before the work-group's LDS is released
+
+  // ---- result: lane holds head h, dims 256r + 32db + 8g + 4hf + i in o[db][4g + i] ----
+  const float ltot = pair_sum32(lsum);
+  const long long slot = ((long long)b * a.Nh + h) * a.nsplit + s;
+  if (!ovf) {
+    if (a.nsplit == 1) {
+      const float inv = 1.f / ltot;
+      uint16_t* op = a.out + ((long long)b * a.Nh + h) * DV + r * (DV / 2) + hf * 4;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<uint2*>(op + db * 32 + g * 8) =
+              make_uint2(pack_bf16x2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
+                         pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv));
+    } else {
+      float* po = a.part_o + slot * DV + r * (DV / 2) + hf * 4;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<float4*>(po + db * 32 + g * 8) =
+              make_float4(o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]);
+      if (r == 0 && hf == 0) {
+        a.part_ml[slot * 2 + 0] = m;
+        a.part_ml[slot * 2 + 1] = ltot;
+      }
+    }
+  }
+
+  // ---- heads whose scores outgrew the reference max by more than 2^kOvf (never for scores of
+  // ordinary size): their accumulators may have overflowed, so they are recomputed exactly by a
+  // plain two-pass loop over the chunk's rows (vector ALU, blocks of 4096 tokens merged with the
+  // same running max / sum algebra). Lanes l and l + 32 hold the same head and the same flag. ----
+  __syncthreads();  // every wave is done with the ring: its LDS holds the recompute's scratch
+  uint64_t bad = __ballot(ovf) & 0xffffffffull;
+  if (bad == 0) return;
+  float* qs = reinterpret_cast<float*>(&ring[0][0]) + w * (kStages * TILE / 2 / kWaves);  // 576 + 4096 floats
+  float* sc = qs + DQ;
+  const double k2 = a.rope_theta > 0 ? -2.0 * log2(a.rope_theta) / (double)(DQ - DV) : 0.0;
+  for (; bad; bad &= bad - 1) {
+    const int c = __builtin_ctzll(bad);
+    const int hc = hgrp * kHeads + (w >> 1) * 32 + c;
+    const uint16_t* qp = a.q + ((long long)b * a.Nh + hc) * DQ;
+    for (int d = lane; d < DQ; d += 64) {
+      float v = bf16_to_f32(qp[d]);
+      if (a.rope_theta > 0 && d >= DV) {  // the same decoupled RoPE as the main path, rounded to bf16
+        const int i = (d - DV) & 31;
+        double sn, cs;
+        sincos((double)(ctx - 1) * exp2(k2 * (double)i), &sn, &cs);
+        const double x = bf16_to_f32(qp[DV + i]), y = bf16_to_f32(qp[DV + 32 + i]);
+        v = bf16_to_f32(f32_to_bf16((float)(d < DV + 32 ? x * cs - y * sn : x * sn + y * cs)));
+      }
+      qs[d] = v;
+    }
+    float mr = -INFINITY, lr = 0.f, o4[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int tb = t0; tb < t1; tb += 4096) {
+      const int n = min(4096, t1 - tb);
+      float mx = -INFINITY;
+      for (int i = lane; i < n; i += 64) {
+        const uint16_t* kp = seq + (long long)(tb + i) * ldk;
+        float acc = 0.f;
+        for (int d = 0; d < DQ; d += 8) {
+          const U4 kv = ldg16(kp + d);
+          acc = fmaf(qs[d + 0], bf16lo(kv.x), acc);
+          acc = fmaf(qs[d + 1], bf16hi(kv.x), acc);
+          acc = fmaf(qs[d + 2], bf16lo(kv.y), acc);
+          acc = fmaf(qs[d + 3], bf16hi(kv.y), acc);
+          acc = fmaf(qs[d + 4], bf16lo(kv.z), acc);
+          acc = fmaf(qs[d + 5], bf16hi(kv.z), acc);
+          acc = fmaf(qs[d + 6], bf16lo(kv.w), acc);
+          acc = fmaf(qs[d + 7], bf16hi(kv.w), acc);
+        }
+        acc *= a.scale_log2;
+        sc[i] = acc;
+        mx = fmaxf(mx, acc);
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      const float mn = fmaxf(mr, mx);
+      const float al = mr == -INFINITY ? 0.f : fast_exp2(mr - mn);
+      lr *= al;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o4[e] *= al;
+      mr = mn;
+      for (int i = 0; i < n; ++i) {
+        const float pw = fast_exp2(sc[i] - mr);
+        lr += pw;
+        const uint2 vv = *reinterpret_cast<const uint2*>(seq + (long long)(tb + i) * ldk + r * (DV / 2) + 4 * lane);
+        o4[0] = fmaf(pw, bf16lo(vv.x), o4[0]);
+        o4[1] = fmaf(pw, bf16hi(vv.x), o4[1]);
+        o4[2] = fmaf(pw, bf16lo(vv.y), o4[2]);
+        o4[3] = fmaf(pw, bf16hi(vv.y), o4[3]);
+      }
+    }
+    if (a.nsplit == 1) {
+      const float inv = 1.f / lr;
+      *reinterpret_cast<uint2*>(a.out + ((long long)b * a.Nh + hc) * DV + r * (DV / 2) + 4 * lane) =
+          make_uint2(pack_bf16x2(o4[0] * inv, o4[1] * inv), pack_bf16x2(o4[2] * inv, o4[3] * inv));
+    } else {
+      const long long sl = ((long long)b * a.Nh + hc) * a.nsplit + s;
+      *reinterpret_cast<float4*>(a.part_o + sl * DV + r * (DV / 2) + 4 * lane) = make_float4(o4[0], o4[1], o4[2], o4[3]);
+      if (r == 0 && lane == 0) {
+        a.part_ml[sl * 2 + 0] = mr;
+        a.part_ml[sl * 2 + 1] = lr;
+      }
+    }
+  }
+}
+
+hipError_t launch(const DecodeArgs& a, hipStream_t st) {
+  const long long n_hg = a.Nh / kHeads;
+  const long long pairs = (long long)a.B * a.nsplit;
+  const long long n_wg = ((pairs + 7) / 8) * 8 * n_hg;
+  if (n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  decode_mla_pair_kernel<<<dim3((unsigned)n_wg), dim3(kWaves * 64), 0, st>>>(a);
+  return hipGetLastError();
+}
+}  // namespace pair
+
 template <int NW>
 hipError_t launch_nw(const DecodeArgs& a, hipStream_t st) {
   const long long n_hg = a.Nh / (16 * NW);
@@ -270,8 +634,10 @@ hipError_t launch_nw(const DecodeArgs& a, hipStream_t st) {
 }  // namespace
 
 int mla_waves_per_group(int Nh) { return Nh % 128 == 0 ? 8 : Nh % 64 == 0 ? 4 : Nh % 32 == 0 ? 2 : 1; }
+int mla_heads_per_group(int Nh) { return Nh % pair::kHeads == 0 ? pair::kHeads : 16 * mla_waves_per_group(Nh); }
 
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t st) {
+  if (a.Nh % pair::kHeads == 0) return pair::launch(a, st);
   switch (mla_waves_per_group(a.Nh)) {
     case 8:
       return launch_nw<8>(a, st);

@@ -79,6 +79,7 @@ struct DecodeArgs {
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t st);
 int mla_waves_per_group(int Nh);  // waves (16 heads each) per MLA work-group
+int mla_heads_per_group(int Nh);  // query heads per MLA work-group
 hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t st);
 
 }  // namespace attn

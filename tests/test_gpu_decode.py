@@ -107,6 +107,94 @@ def test_mla_decode_decoupled_rope():
     assert max_abs(got, want) <= BF16_TOL
 
 
+MLA_PAIR_CASES = [
+    # B, Nh, max_ctx, ctx list, rope: head counts that are multiples of 64 (pairs of waves sharing
+    # 32 heads); contexts of one token, ending inside a 32-token tile, and splits left empty
+    (3, 128, 1000, [1000, 45, 1], 0.0),
+    (2, 64, 333, [333, 32], 0.0),
+    (2, 64, 200, [200, 77], 1e4),      # decoupled q^R RoPE (held by the upper reduction half)
+    (2, 192, 130, [130, 96], 5e5),     # three head groups
+]
+
+
+@pytest.mark.parametrize("case", MLA_PAIR_CASES, ids=lambda c: "B%dH%dT%d" % c[:3])
+def test_mla_decode_head_pairs(case):
+    B, Nh, T, ctx, rope = case
+    wid = 480 + T
+    ctx = np.asarray(ctx, np.int32)
+    q = synth.normal(wid, 0, (B, Nh, 576), "bf16")
+    kc = synth.normal(wid, 1, (B, T, 1, 576), "bf16")
+    scale = 1.0 / math.sqrt(192)
+    got = _gpu_decode(q, kc, None, ctx, scale=scale, rope=rope, mla=True)
+    want = _oracle_decode(q, kc, None, ctx, scale=scale, rope=rope, mla=True)
+    assert max_abs(got, want) <= BF16_TOL
+
+
+def test_mla_decode_single_chunk():
+    """Enough (sequence, head group) units that each sequence is one chunk: the kernel writes the
+    normalised output itself (no split partials, no merge)."""
+    B, Nh, T = 256, 64, 64
+    rng = np.random.default_rng(490)
+    ctx = rng.integers(1, T, B, endpoint=True).astype(np.int32)
+    q = synth.normal(490, 0, (B, Nh, 576), "bf16")
+    kc = synth.normal(490, 1, (B, T, 1, 576), "bf16")
+    scale = 1.0 / math.sqrt(192)
+    got = _gpu_decode(q, kc, None, ctx, scale=scale, mla=True)
+    want = _oracle_decode(q, kc, None, ctx, scale=scale, mla=True)
+    assert max_abs(got, want) <= BF16_TOL
+
+
+@pytest.mark.parametrize("B,T,ctx,rope", [(2, 300, [300, 200], 0.0), (2, 300, [300, 260], 1e4),
+                                          (256, 160, None, 0.0)], ids=["splits", "rope", "one-chunk"])
+def test_mla_decode_score_growth_beyond_reference(B, T, ctx, rope):
+    """Scores that grow far past the first tile's max (the decoupled k^R dims of later tokens
+    scaled by 200, so V = c^KV stays of order one): such heads leave the fast path's fixed
+    reference max and are recomputed exactly; the result still matches the oracle."""
+    Nh = 64
+    ctx = np.asarray(ctx if ctx is not None else np.full(B, T), np.int32)
+    q = synth.normal(497, 0, (B, Nh, 576), "bf16")
+    kf = synth.as_f32(synth.normal(497, 1, (B, T, 1, 576), "bf16"), "bf16").copy()
+    kf[:, 40:, :, 512:] *= 200.0
+    kc = synth.f32_to_bf16_bits(kf)
+    scale = 1.0 / math.sqrt(192)
+    # the inputs do leave the fast path's range: some head's later score exceeds its first-tile max
+    # by more than 2^64 in the exponent (scale * log2(e) units), checked here without rotation
+    qf = synth.as_f32(q, "bf16").astype(np.float64)
+    kd = synth.as_f32(kc, "bf16").astype(np.float64)[:, :, 0]
+    sl = np.einsum("bhd,btd->bht", qf, kd) * scale * math.log2(math.e)
+    assert np.any(sl[:, :, 40:].max(axis=2) > sl[:, :, :32].max(axis=2) + 64)
+    got = _gpu_decode(q, kc, None, ctx, scale=scale, rope=rope, mla=True)
+    qref = q
+    if rope > 0:
+        # with scores this large the softmax is nearly one-hot, and the bf16 rounding of the rotated
+        # q^R (the kernel rotates q once and rounds it to bf16 for the products) moves near-tied
+        # weights by more than the tolerance; the reference therefore takes the oracle's rotation
+        # of q at ctx - 1, rounded to bf16 the same way, and no further RoPE
+        qr = np.empty(q.shape, np.float32)
+        for b in range(B):
+            qh = synth.as_f32(q[b], "bf16").astype(np.float64)[None, None]
+            qr[b] = oracle.rope_rotate(qh, [int(ctx[b]) - 1], rope, rot_dims=64, rot_offset=512)[0, 0]
+        qref = synth.f32_to_bf16_bits(qr)
+    want = _oracle_decode(qref, kc, None, ctx, scale=scale, mla=True)
+    assert np.all(np.isfinite(got))
+    assert max_abs(got, want) <= BF16_TOL
+
+
+def test_mla_decode_never_reads_beyond_context():
+    B, Nh, T = 3, 128, 300
+    ctx = np.array([7, 150, 300], np.int32)
+    q = synth.normal(495, 0, (B, Nh, 576), "bf16")
+    kc = synth.normal(495, 1, (B, T, 1, 576), "bf16")
+    scale = 1.0 / math.sqrt(192)
+    clean = _gpu_decode(q, kc, None, ctx, scale=scale, mla=True)
+    kn = kc.copy()
+    for b, c in enumerate(ctx):
+        kn[b, c:] = 0x7FC0  # bf16 NaN
+    dirty = _gpu_decode(q, kn, None, ctx, scale=scale, mla=True)
+    assert np.all(np.isfinite(dirty))
+    assert np.array_equal(clean, dirty)
+
+
 def test_llama3_decode_full():
     w = synth.LLAMA3_DECODE
     q, kc, vc, ctx = w.inputs()
