@@ -277,7 +277,7 @@ __global__ __launch_bounds__(NW * 64, (NW >= 8 ? 2 : 1)) void decode_mla_kernel(
 namespace pair {
 constexpr int kWaves = 4;
 constexpr int kHeads = 64;               // heads per work-group
-constexpr int kStages = 3;               // LDS ring: tiles j+1 and j+2 load while j is computed
+constexpr int kStages = 4;               // LDS ring: tiles j+1 .. j+3 load while j is computed
 constexpr int kSPW = NSLOT / kWaves;     // 9 tile-load instructions per wave and tile
 constexpr int kHalfQ = DQ / 2;           // 288 reduction dims per wave
 constexpr int kKS = kHalfQ / 16;         // 18 k-steps of 16 dims
@@ -487,19 +487,20 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_pair_kernel(DecodeA
     }
   };
 
-  // ---- ring of 3 stages; a load past the last tile re-reads the last one into a stage that is
+  // ---- ring of 4 stages (three tiles in flight while one is computed, which the cold-cache
+  // latency needs); a load past the last tile re-reads the last one into a stage that is
   // never read again, so every step keeps one fixed vmcnt. One loop body with the stage picked by
   // a scalar index: the accumulators then keep one register assignment through the loop. ----
   issue_tile(0, ring[0]);
   issue_tile(min(1, n_tiles - 1), ring[1]);
+  issue_tile(min(2, n_tiles - 1), ring[2]);
   int cur = 0;
   for (int j = 0; j < n_tiles; ++j) {
-    wait_vmem_n<kSPW>();
+    wait_vmem_n<2 * kSPW>();  // tile j has landed (tiles j+1 and j+2 may still fly)
     barrier_only();
-    const int nxt = cur == 0 ? 2 : cur - 1;  // (j + 2) % 3
-    issue_tile(min(j + 2, n_tiles - 1), ring[nxt]);
+    issue_tile(min(j + 3, n_tiles - 1), ring[(cur + 3) & 3]);
     compute_tile(j, ring[cur]);
-    cur = cur == 2 ? 0 : cur + 1;
+    cur = (cur + 1) & 3;
   }
   wait_vmem();  // the re-reads must land before the work-group's LDS is released
 
