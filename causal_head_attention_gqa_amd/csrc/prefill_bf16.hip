@@ -38,7 +38,8 @@ namespace attn {
 namespace {
 constexpr int kBC = 32;     // keys per tile (one 32x32 score block per wave)
 constexpr int kStages = 3;  // LDS ring depth: tiles j+1 and j+2 load while tile j is computed
-constexpr float kSlack = 8.f;  // log2 units: how far a row max may exceed the softmax reference max
+constexpr float kSlack = 8.f;  // log2 units: margin by which the exact path moves the reference max
+constexpr float kOvf = 1.8446744e19f;  // 2^64: sum of a block's exponentials that sends it to the exact path
 constexpr int kThreads = 256;
 
 // Physical 16-byte chunk of logical chunk c in tile row `row` (CH chunks per row). The XOR key
@@ -290,35 +291,49 @@ __global__ __launch_bounds__(kThreads, (DQK > 128 ? 2 : 3)) void prefill_bf16_ke
         if (o > hi || (o < lo && o >= sk)) sv[i] = -INFINITY;
       }
     }
-    float mt = sv[0];
+    // Reference max m per query: the max of the row's first block with a visible key (the block
+    // max is computed only while some row of the wave has none yet); later blocks exponentiate
+    // against it as is, with no per-block max. A score up to ~2^60 above m keeps p, l and O finite
+    // (bf16 and fp32 share the exponent range); a block whose exponentials sum past 2^kOvf takes
+    // the exact path: its max becomes the reference (when it exceeds m by more than kSlack), O and l
+    // are rescaled and the block is exponentiated again. Lanes l and l ^ 32 hold the same query and
+    // always agree on m.
+    auto block_max = [&]() {
+      float mt = sv[0];
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mt = fmaxf(mt, sv[i]);
-    mt = pair_max32(mt);
-    // Lazy reference max: the exponentials use m, which moves only when this block's max exceeds it
-    // by more than kSlack (p then stays below 2^kSlack; O / l is unchanged), so rescaling the
-    // accumulator is rare.
-    const float mb = mt * c;
-    const bool move = mb > m + kSlack;  // also true on the first live block (m = -inf)
-    const float m_new = move ? mb : m;
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = move ? fast_exp2(m - m_use) : 1.f;
-    m = m_new;
-    uint32_t pk[2][4];
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-      const float e0 = fast_exp2(fmaf(sv[i], c, -m_use));
-      const float e1 = fast_exp2(fmaf(sv[i + 1], c, -m_use));
-      psum += e0 + e1;
-      pk[i >> 3][(i & 7) >> 1] = pack_bf16x2(e0, e1);
+      for (int i = 1; i < 16; ++i) mt = fmaxf(mt, sv[i]);
+      return pair_max32(mt) * c;
+    };
+    if (__ballot(m == -INFINITY)) {
+      const float mb = block_max();
+      if (m == -INFINITY) m = mb;
     }
-    lsum = fmaf(lsum, alpha, psum);
-    if (__ballot(alpha != 1.f)) {
+    uint32_t pk[2][4];
+    float psum;
+    auto exps = [&](float m_use) {
+      psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const float e0 = fast_exp2(fmaf(sv[i], c, -m_use));
+        const float e1 = fast_exp2(fmaf(sv[i + 1], c, -m_use));
+        psum += e0 + e1;
+        pk[i >> 3][(i & 7) >> 1] = pack_bf16x2(e0, e1);
+      }
+    };
+    exps(m == -INFINITY ? 0.f : m);
+    if (__ballot(!(psum <= kOvf))) {  // rare: a score far above the reference (or an overflow)
+      const float mb = block_max();
+      const bool move = mb > m + kSlack;  // never for a row without a visible key (then mb = m = -inf)
+      const float alpha = move ? fast_exp2(m - mb) : 1.f;
+      m = move ? mb : m;
+      lsum *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+      exps(m == -INFINITY ? 0.f : m);
     }
+    lsum += psum;
 
     // ---- O^T += V^T P^T over this block's 32 keys ----
 #pragma unroll

@@ -172,6 +172,29 @@ def test_sliding_window_with_sinks_matches_oracle(case):
     assert max_abs(got, want) <= BF16_TOL
 
 
+def test_sliding_window_score_growth_beyond_reference():
+    """Window + sinks with keys whose scores lie far above those of each query's first visible
+    block (keys 100.. scaled after bf16 widening): the exact path of the softmax keeps the result
+    equal to the oracle's."""
+    import causal_head_attention_gqa_amd as attn
+    torch = _torch()
+    B, S, Nh, Nkv, D, T, window, sinks = 1, 256, 4, 2, 128, 256, 64, 4
+    k_all = synth.as_f32(synth.normal(880, 1, (B, T, Nkv, D), "bf16"), "bf16").copy()
+    k_all[:, 100:] *= 20.0
+    k_all = synth.f32_to_bf16_bits(k_all)
+    v_all = synth.normal(880, 2, (B, T, Nkv, D), "bf16")
+    q = synth.normal(880, 0, (B, S, Nh, D), "bf16")
+    kc, _ = _empty_cache(B, T, Nkv, D)
+    vc, _ = _empty_cache(B, T, Nkv, D)
+    zeros = torch.zeros(B, dtype=torch.int32, device="cuda")
+    attn.kv_append(to_dev(k_all, "bf16"), to_dev(v_all, "bf16"), kc, vc, zeros)
+    got = attn.prefill_cached(to_dev(q, "bf16"), kc, vc, zeros, window=window, sinks=sinks).float().cpu().numpy()
+    want = oracle.prefill_chunk(values(q, "bf16"), values(k_all, "bf16"), values(v_all, "bf16"), np.zeros(B, np.int32),
+                                window=window, sinks=sinks)
+    assert np.all(np.isfinite(got))
+    assert max_abs(got, want) <= BF16_TOL
+
+
 ROPE_CASES = [
     # D, rope_dims, interleaved, theta
     (128, 64, False, 1e4),

@@ -49,6 +49,41 @@ def test_prefill_bf16_small(case):
     assert max_abs(got, want) <= BF16_TOL
 
 
+GROWTH_CASES = [
+    # B, S, Nh, Nkv, D, causal, scaled keys, factor: keys scaled after bf16 widening so that the
+    # scores of those keys lie far above (or far below) those of the row's first 32-key block
+    (1, 300, 8, 2, 128, True, (40, None), 20.0),   # later keys dominate: exact path, new reference
+    (1, 300, 8, 2, 128, True, (0, 32), 20.0),      # the first block dominates: later p underflow
+    (2, 200, 4, 4, 64, False, (100, None), 20.0),  # full attention
+]
+
+
+@pytest.mark.parametrize("case", GROWTH_CASES, ids=["later", "first", "full"])
+def test_prefill_score_growth_beyond_reference(case):
+    """The softmax reference max of a query is its first visible block's max; scores far above it
+    send a block through the exact path (new reference, rescaled output). Compared with the oracle
+    on inputs that do leave the fast path's range."""
+    import causal_head_attention_gqa_amd as attn
+    B, S, Nh, Nkv, D, causal, (k0, k1), factor = case
+    wid = 180 + S
+    q = synth.normal(wid, 0, (B, S, Nh, D), "bf16")
+    kf = synth.as_f32(synth.normal(wid, 1, (B, S, Nkv, D), "bf16"), "bf16").copy()
+    kf[:, k0:k1] *= factor
+    k = synth.f32_to_bf16_bits(kf)
+    v = synth.normal(wid, 2, (B, S, Nkv, D), "bf16")
+    qv, kv, vv = values(q, "bf16"), values(k, "bf16"), values(v, "bf16")
+    if k0 > 0:  # some query's later score exceeds its first block's max by more than 2^64
+        G = Nh // Nkv
+        sl = np.einsum("bshd,bthd->bhst", qv[:, :, ::G].astype(np.float64), kv.astype(np.float64))
+        sl *= np.log2(np.e) / np.sqrt(D)
+        assert np.any(sl[..., k0:].max(-1) > sl[..., :32].max(-1) + 64)
+    out = attn.prefill(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), causal=causal)
+    got = to_host_f64(out)
+    want = oracle.prefill(qv, kv, vv, causal=causal)
+    assert np.all(np.isfinite(got))
+    assert max_abs(got, want) <= BF16_TOL
+
+
 SMALL_F32 = [
     (1, 128, 4, 4, 16, 1e4, True),
     (2, 150, 4, 2, 32, 1e4, True),
