@@ -6,7 +6,9 @@
 // (the first 512 dims of the same row), and the scale is given by the caller (1/sqrt(192) for
 // DeepSeek-V3's 128 + 64 per-head query dims).
 //
-// With 128 heads per row the work is ~242 FLOP per cached byte, so the matrix cores are used:
+// With 128 heads per row the work is ~242 FLOP per cached byte, so the matrix cores are used. Two
+// kernels: head counts that are multiples of 64 use the pair kernel further below (32 heads per
+// pair of waves on 32x32x16 products); other head counts use this one, 16 heads per wave:
 //   - a work-group = NW waves x 16 heads owns (sequence, 16*NW heads, one context chunk); with
 //     NW = 8 all 128 heads share the work-group, so every cached row crosses HBM once per chunk;
 //   - 32-token tiles (36 KiB) go from HBM straight into an LDS ring of NB stages
