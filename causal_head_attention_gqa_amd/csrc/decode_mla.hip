@@ -1,4 +1,4 @@
-// MLA-absorbed decode on gfx950 matrix cores (v_mfma_f32_16x16x32_bf16).
+// MLA-absorbed decode on gfx950 matrix cores (v_mfma_f32_32x32x16_bf16 and v_mfma_f32_16x16x32_bf16).
 //
 // What is computed ("Transformer 与 LLM：结构、实现与算量" slide 06): after W_UK and W_UV are
 // absorbed, decode is multi-query attention in which all query heads share ONE cached row per
