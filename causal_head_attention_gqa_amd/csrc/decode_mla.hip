@@ -369,7 +369,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_pair_kernel(DecodeA
   for (int i = 0; i < kDB; ++i) o[i] = f32x16{};
   float m = 0.f, lsum = 0.f;
   bool ovf = false;
-  constexpr float kOvf = 64.f;
+  constexpr float kOvf = 1.8446744e19f;  // 2^64
 
   // ---- per-lane LDS offsets (elements) ----
   // K operand of k-step kk: row col, logical chunk c0 + 2kk with c0 = 36r + hf; the key changes
@@ -447,16 +447,16 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_pair_kernel(DecodeA
       for (int i = 0; i < 16; ++i)
         if (tbase + (i >> 2) * 8 + hf * 4 + (i & 3) >= t1) sv[i] = -INFINITY;
     }
-    float mt = sv[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mt = fmaxf(mt, sv[i]);
-    mt = pair_max32(mt);
-    // fixed reference max: the first tile's max per head; a later score may exceed it by up to
-    // 2^kOvf (p, the sums and O stay finite in fp32 and bf16); beyond that the head is flagged and
+    // fixed reference max: the first tile's max per head, the only tile whose max is computed; a
+    // later score may exceed it by up to ~2^60 (p, the sums and O stay finite in fp32 and bf16). A
+    // tile whose exponentials sum past 2^64 in either half of a head flags the head, which is then
     // recomputed exactly after the loop
-    const float mb = mt * a.scale_log2;
-    if (j == 0) m = mb;
-    ovf |= mb > m + kOvf;
+    if (j == 0) {
+      float mt = sv[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mt = fmaxf(mt, sv[i]);
+      m = pair_max32(mt) * a.scale_log2;
+    }
     uint32_t pk[2][4];
     float psum = 0.f;
 #pragma unroll
@@ -467,6 +467,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_pair_kernel(DecodeA
       pk[i >> 3][(i & 7) >> 1] = pack_bf16x2(e0, e1);
     }
     lsum += psum;
+    ovf |= !(psum <= kOvf);
     // O^T[256 dims x 32 heads] += V^T P^T; two V operands in flight
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -509,7 +510,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_pair_kernel(DecodeA
   // ---- result: lane holds head h, dims 256r + 32db + 8g + 4hf + i in o[db][4g + i] ----
   const float ltot = pair_sum32(lsum);
   const long long slot = ((long long)b * a.Nh + h) * a.nsplit + s;
-  if (!ovf) {
+  const uint64_t bal = __ballot(ovf);
+  uint64_t bad = (bal | (bal >> 32)) & 0xffffffffull;  // heads flagged by either of their lanes
+  if (!((bad >> col) & 1)) {
     if (a.nsplit == 1) {
       const float inv = 1.f / ltot;
       uint16_t* op = a.out + ((long long)b * a.Nh + h) * DV + r * (DV / 2) + hf * 4;
@@ -535,12 +538,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_pair_kernel(DecodeA
     }
   }
 
-  // ---- heads whose scores outgrew the reference max by more than 2^kOvf (never for scores of
+  // ---- heads whose scores outgrew the reference max by ~2^60 or more (never for scores of
   // ordinary size): their accumulators may have overflowed, so they are recomputed exactly by a
   // plain two-pass loop over the chunk's rows (vector ALU, blocks of 4096 tokens merged with the
-  // same running max / sum algebra). Lanes l and l + 32 hold the same head and the same flag. ----
+  // same running max / sum algebra). Both waves of a pair see the same scores and flags. ----
   __syncthreads();  // every wave is done with the ring: its LDS holds the recompute's scratch
-  uint64_t bad = __ballot(ovf) & 0xffffffffull;
   if (bad == 0) return;
   float* qs = reinterpret_cast<float*>(&ring[0][0]) + w * (kStages * TILE / 2 / kWaves);  // 576 + 4096 floats
   float* sc = qs + DQ;
