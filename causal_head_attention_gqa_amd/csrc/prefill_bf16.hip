@@ -304,7 +304,7 @@ __global__ __launch_bounds__(kThreads, (DQK > 128 ? 2 : 3)) void prefill_bf16_ke
       for (int i = 1; i < 16; ++i) mt = fmaxf(mt, sv[i]);
       return pair_max32(mt) * c;
     };
-    if (__ballot(m == -INFINITY)) {
+    if (__builtin_expect(__ballot(m == -INFINITY) != 0, 0)) {
       const float mb = block_max();
       if (m == -INFINITY) m = mb;
     }
@@ -321,7 +321,7 @@ __global__ __launch_bounds__(kThreads, (DQK > 128 ? 2 : 3)) void prefill_bf16_ke
       }
     };
     exps(m == -INFINITY ? 0.f : m);
-    if (__ballot(!(psum <= kOvf))) {  // rare: a score far above the reference (or an overflow)
+    if (__builtin_expect(__ballot(!(psum <= kOvf)) != 0, 0)) {  // rare: a score far above the reference
       const float mb = block_max();
       const bool move = mb > m + kSlack;  // never for a row without a visible key (then mb = m = -inf)
       const float alpha = move ? fast_exp2(m - mb) : 1.f;
