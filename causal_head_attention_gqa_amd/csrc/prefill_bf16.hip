@@ -162,7 +162,8 @@ __global__ __launch_bounds__(kThreads, (DQK > 128 ? 2 : 3)) void prefill_bf16_ke
   f32x16 o[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) o[i] = f32x16{};
-  float m = -INFINITY;  // running max of scale*log2(e)*score for this lane's query
+  float m = -INFINITY;  // softmax reference max (scale*log2(e) units) of this lane's query
+  float mneg = -0.f;     // -m, or 0 while m = -inf: the exponent offset, updated only when m moves
   float lsum = 0.f;     // running sum over the keys this lane holds
 
   // ---- per-lane global source offsets of the tile loads (row r of a tile, swizzled chunk) ----
@@ -304,34 +305,37 @@ __global__ __launch_bounds__(kThreads, (DQK > 128 ? 2 : 3)) void prefill_bf16_ke
       for (int i = 1; i < 16; ++i) mt = fmaxf(mt, sv[i]);
       return pair_max32(mt) * c;
     };
+    auto set_ref = [&](float mr) {
+      m = mr;
+      mneg = mr == -INFINITY ? -0.f : -mr;
+    };
     if (__builtin_expect(__ballot(m == -INFINITY) != 0, 0)) {
       const float mb = block_max();
-      if (m == -INFINITY) m = mb;
+      if (m == -INFINITY) set_ref(mb);
     }
     uint32_t pk[2][4];
     float psum;
-    auto exps = [&](float m_use) {
-      psum = 0.f;
+    auto exps = [&]() {
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
-        const float e0 = fast_exp2(fmaf(sv[i], c, -m_use));
-        const float e1 = fast_exp2(fmaf(sv[i + 1], c, -m_use));
-        psum += e0 + e1;
+        const float e0 = fast_exp2(fmaf(sv[i], c, mneg));
+        const float e1 = fast_exp2(fmaf(sv[i + 1], c, mneg));
+        psum = i == 0 ? e0 + e1 : psum + (e0 + e1);
         pk[i >> 3][(i & 7) >> 1] = pack_bf16x2(e0, e1);
       }
     };
-    exps(m == -INFINITY ? 0.f : m);
+    exps();
     if (__builtin_expect(__ballot(!(psum <= kOvf)) != 0, 0)) {  // rare: a score far above the reference
       const float mb = block_max();
       const bool move = mb > m + kSlack;  // never for a row without a visible key (then mb = m = -inf)
       const float alpha = move ? fast_exp2(m - mb) : 1.f;
-      m = move ? mb : m;
+      if (move) set_ref(mb);
       lsum *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-      exps(m == -INFINITY ? 0.f : m);
+      exps();
     }
     lsum += psum;
 
