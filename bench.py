@@ -276,7 +276,7 @@ def run_extras(torch, attn, steps: int, warmup: int):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU: every workload is one GPU's share; "
+        print(json.dumps({"error": "this library runs on one GPU: every workload is one GPU's share; "
                                    "--gpus above 1 is not supported"}))
         sys.exit(2)
     import torch
