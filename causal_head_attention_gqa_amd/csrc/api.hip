@@ -45,11 +45,11 @@ DecodePlan decode_plan(int B, int Nh, int Nkv, int Dqk, int Dv, int max_ctx) {
     const int per = (int)((max_ctx + want - 1) / want);
     p.chunk = (per + 31) / 32 * 32;
   } else {
-    // work-groups of (sequence, KV head, up to 16 query heads, chunk); 512-token chunks unless
+    // work-groups of (sequence, KV head, up to 16 query heads, chunk); 1024-token chunks unless
     // that leaves fewer than ~1024 work-groups
     const int G = Nh / Nkv;
     const long long groups = (long long)B * Nkv * (G < 16 ? 1 : G / 16);
-    p.chunk = 512;
+    p.chunk = 1024;
     while (p.chunk > 64 && groups * ((max_ctx + p.chunk - 1) / p.chunk) < 1024) p.chunk /= 2;
   }
   p.nsplit = (max_ctx + p.chunk - 1) / p.chunk;
