@@ -20,9 +20,10 @@
 //   - tiles past the work-group's last query are never visited and 32-key blocks above a wave's
 //     diagonal are skipped ("2.7 Transformer Decoder Block完整解析" §3.3); the element mask is
 //     applied only on blocks that cross the diagonal or the sequence end;
-//   - online softmax per 32-key block ("Transformer 架构完全深度解析" §十三: running max and sum;
-//     the output accumulator is rescaled by the same factor, and only when some row's max
-//     moved).
+//   - online softmax per 32-key block ("Transformer 架构完全深度解析" §十三: running max and sum), with the
+//     reference max of each query fixed at its first block with a visible key; a block whose
+//     exponentials would overflow that reference takes an exact path (new reference, output and sum
+//     rescaled), so ordinary blocks compute no row max at all.
 //   - K and V operands are read from LDS through small register rings (four K and two V reads in
 //     flight), so the products rarely wait on an LDS read.
 // All per-wave control values are scalar (wave-uniform branches); per-lane LDS and global
