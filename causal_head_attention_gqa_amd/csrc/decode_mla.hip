@@ -78,10 +78,18 @@ __global__ __launch_bounds__(NW * 64, (NW >= 8 ? 2 : 1)) void decode_mla_kernel(
   const int s = pair % a.nsplit;
   const int ctx = min(max(a.ctx_lens[b], 0), a.max_ctx);
   const int t0 = s * a.chunk;
-  if (t0 >= ctx) return;
-  const int t1 = min(ctx, t0 + a.chunk);
   const int hc = lane & 15, rg = lane >> 4;  // head column, row group
   const int h = hgrp * 16 * NW + w * 16 + hc;
+  if (t0 >= ctx) {
+    // an empty split; with a single chunk (no merge follows) an empty context gives a zero row
+    if (a.nsplit == 1) {
+      uint16_t* op = a.out + ((long long)b * a.Nh + h) * DV + rg * 4;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) *reinterpret_cast<uint2*>(op + db * 16) = make_uint2(0u, 0u);
+    }
+    return;
+  }
+  const int t1 = min(ctx, t0 + a.chunk);
 
   // Q^T operand: head h, dims kk*32 + rg*8 .. +7
   bf16x8 qreg[NKK];
@@ -342,9 +350,19 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_pair_kernel(DecodeA
   const int s = sp_id % a.nsplit;
   const int ctx = min(max(a.ctx_lens[b], 0), a.max_ctx);
   const int t0 = s * a.chunk;
-  if (t0 >= ctx) return;
-  const int t1 = min(ctx, t0 + a.chunk);
   const int h = hgrp * kHeads + (w >> 1) * 32 + col;
+  if (t0 >= ctx) {
+    // an empty split; with a single chunk (no merge follows) an empty context gives a zero row
+    if (a.nsplit == 1) {
+      uint16_t* op = a.out + ((long long)b * a.Nh + h) * DV + r * (DV / 2) + hf * 4;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) *reinterpret_cast<uint2*>(op + db * 32 + g * 8) = make_uint2(0u, 0u);
+    }
+    return;
+  }
+  const int t1 = min(ctx, t0 + a.chunk);
 
   // Q^T operand of k-step kk: head h, dims 288r + 16kk + 8hf .. +7
   bf16x8 qreg[kKS];

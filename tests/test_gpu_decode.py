@@ -180,6 +180,33 @@ def test_mla_decode_score_growth_beyond_reference(B, T, ctx, rope):
     assert max_abs(got, want) <= BF16_TOL
 
 
+@pytest.mark.parametrize("mla,B,Nh", [(False, 3, 8), (True, 3, 64), (True, 256, 64), (True, 3, 32), (True, 256, 32)],
+                         ids=["gqa", "mla64-split", "mla64-one-chunk", "mla32-split", "mla32-one-chunk"])
+def test_decode_empty_context_gives_zero_row(mla, B, Nh):
+    """A context of 0 keys (a precondition violation the kernels clamp) gives an all-zero output row,
+    whether or not the call splits the context (single chunk: no merge follows); the other rows are
+    unaffected."""
+    T = 96
+    ctx = np.full(B, 70, np.int32)
+    ctx[0] = 0
+    ctx[B // 2] = 0
+    wid = 530 + B + Nh
+    if mla:
+        q = synth.normal(wid, 0, (B, Nh, 576), "bf16")
+        kc = synth.normal(wid, 1, (B, T, 1, 576), "bf16")
+        vc, kw = None, dict(scale=1.0 / math.sqrt(192), mla=True)
+    else:
+        q = synth.normal(wid, 0, (B, Nh, 128), "bf16")
+        kc = synth.normal(wid, 1, (B, T, 2, 128), "bf16")
+        vc, kw = synth.normal(wid, 2, (B, T, 2, 128), "bf16"), {}
+    got = _gpu_decode(q, kc, vc, ctx, **kw)
+    empty = ctx == 0
+    assert np.all(got[empty] == 0.0)
+    keep = np.flatnonzero(~empty)[:4]
+    want = _oracle_decode(q[keep], kc[keep], None if vc is None else vc[keep], ctx[keep], **kw)
+    assert max_abs(got[keep], want) <= BF16_TOL
+
+
 def test_mla_decode_never_reads_beyond_context():
     B, Nh, T = 3, 128, 300
     ctx = np.array([7, 150, 300], np.int32)
