@@ -91,8 +91,20 @@ __global__ __launch_bounds__(kThreads, (DQK > 128 ? 2 : 3)) void prefill_bf16_ke
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int HGn = Nh / HPW;
   const int id = blockIdx.x;
-  const int bh = id % (B * HGn);
-  const int pt = n_ptiles - 1 - id / (B * HGn);
+  // block order: work-group id runs on XCD id % 8. When the (sequence, head group) pairs split evenly
+  // over the 8 XCDs, XCD x takes its pairs x, x + 8, ... one after the other, each pair's q-tiles
+  // heaviest first, so the work-groups resident on an XCD share one pair's K/V in its L2; otherwise
+  // the heaviest q-tiles of all pairs go first.
+  const int npairs = B * HGn;
+  int bh, pt;
+  if (npairs % 8 == 0) {
+    const int li = id / 8;
+    bh = id % 8 + 8 * (li / n_ptiles);
+    pt = n_ptiles - 1 - li % n_ptiles;
+  } else {
+    bh = id % npairs;
+    pt = n_ptiles - 1 - id / npairs;
+  }
   const int b = bh / HGn;
   const int h0 = (bh % HGn) * HPW;
   const int g = h0 / (Nh / Nkv);
