@@ -27,9 +27,11 @@
 //   - K and V operands are read from LDS through small register rings (four K and two V reads in
 //     flight), so the products rarely wait on an LDS read.
 // All per-wave control values are scalar (wave-uniform branches); per-lane LDS and global
-// offsets are computed once. Grid order puts the work-groups with the most tiles first, head
-// groups fastest: work-group i runs on XCD i % 8, so when B * Nh / HPW is a multiple of 8 every
-// q-tile of one (sequence, KV head) runs on the same XCD and its K/V stay in that XCD's L2.
+// offsets are computed once. Grid order: work-group i runs on XCD i % 8; when B * Nh / HPW is a
+// multiple of 8, each XCD runs its (sequence, head group) pairs one after the other, q-tiles with
+// the most key tiles first, so the work-groups resident on an XCD share one pair's K/V in its L2
+// (HBM-side reads 1.8x the algorithmic bytes instead of 6x); otherwise the heaviest q-tiles of all
+// pairs go first.
 #include <type_traits>
 
 #include "kernels.hpp"
