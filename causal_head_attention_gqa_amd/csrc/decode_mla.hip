@@ -432,21 +432,20 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_pair_kernel(DecodeA
   };
 
   auto compute_tile = [&](int j, const uint16_t* T) {
-    // partial S^T[32 tokens x 32 heads] over this wave's 288 dims: two independent accumulation
-    // chains (even / odd k-steps) and kKR K operands in flight, since one wave per SIMD has no
-    // other wave to hide the product and LDS latencies behind
+    // partial S^T[32 tokens x 32 heads] over this wave's 288 dims: one accumulation chain (a wave
+    // issues dependent 32x32x16 products at the full rate, and a second chain would cost 32 AGPR
+    // reads and 16 adds per tile to combine) and kKR K operands in flight
     constexpr int kKR = 4;
     auto kread = [&](int kk) { return *reinterpret_cast<const bf16x8*>(T + koff[kk & 3] + 64 * (kk >> 2)); };
     bf16x8 ka[kKR];
 #pragma unroll
     for (int u = 0; u < kKR; ++u) ka[u] = kread(u);
-    f32x16 sv2[2] = {f32x16{}, f32x16{}};
+    f32x16 sv = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < kKS; ++kk) {
-      sv2[kk & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk % kKR], qreg[kk], sv2[kk & 1], 0, 0, 0);
+      sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk % kKR], qreg[kk], sv, 0, 0, 0);
       if (kk + kKR < kKS) ka[kk % kKR] = kread(kk + kKR);
     }
-    f32x16 sv = sv2[0] + sv2[1];
     // exchange with the partner wave (w ^ 1): same lane = same head and tokens
 #pragma unroll
     for (int g = 0; g < 4; ++g)
