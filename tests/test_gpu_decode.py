@@ -207,6 +207,34 @@ def test_decode_empty_context_gives_zero_row(mla, B, Nh):
     assert max_abs(got[keep], want) <= BF16_TOL
 
 
+@pytest.mark.parametrize("mla", [False, True], ids=["gqa", "mla"])
+def test_decode_padded_cache_rows(mla):
+    """Cache rows with a pitch larger than the head dim (the binding passes the stride as the row
+    pitch); the padding holds NaN, so reading it would show in the output."""
+    import causal_head_attention_gqa_amd as attn
+    torch = __import__("torch")
+    B, T = 3, 200
+    ctx = np.array([200, 37, 129], np.int32)
+    Nh, Nkv, D, pitch = (64, 1, 576, 640) if mla else (16, 4, 128, 136)
+    q = synth.normal(540 + D, 0, (B, Nh, D), "bf16")
+    kc = synth.normal(540 + D, 1, (B, T, Nkv, D), "bf16")
+    vc = None if mla else synth.normal(540 + D, 2, (B, T, Nkv, D), "bf16")
+
+    def padded(x):
+        buf = torch.full((B, T, Nkv, pitch), float("nan"), dtype=torch.bfloat16, device="cuda")
+        buf[..., :D] = to_dev(x, "bf16")
+        return buf
+
+    kpad = padded(kc)
+    vd = kpad[..., :512] if mla else padded(vc)[..., :D]
+    scale = 1.0 / math.sqrt(192) if mla else None
+    out = attn.decode(to_dev(q, "bf16"), kpad[..., :D], vd, torch.as_tensor(ctx, device="cuda"), scale=scale)
+    got = out.float().cpu().numpy()
+    want = _oracle_decode(q, kc, vc, ctx, scale=scale, mla=mla)
+    assert np.all(np.isfinite(got))
+    assert max_abs(got, want) <= BF16_TOL
+
+
 def test_mla_decode_never_reads_beyond_context():
     B, Nh, T = 3, 128, 300
     ctx = np.array([7, 150, 300], np.int32)
