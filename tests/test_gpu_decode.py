@@ -68,6 +68,21 @@ def test_decode_gqa_small(case):
     assert max_abs(got, want) <= BF16_TOL
 
 
+def test_decode_contexts_at_chunk_edges():
+    """64 sequences x 8 KV heads: the plan splits contexts into 1024-token chunks; contexts of 1, at,
+    just below and just above the chunk edges (one key into a new chunk) against the oracle."""
+    B, Nh, Nkv, D, T = 64, 8, 8, 64, 2049
+    edges = [1, 2, 1023, 1024, 1025, 2047, 2048, 2049]
+    ctx = np.array([edges[i % len(edges)] for i in range(B)], np.int32)
+    q = synth.normal(560, 0, (B, Nh, D), "bf16")
+    kc = synth.normal(560, 1, (B, T, Nkv, D), "bf16")
+    vc = synth.normal(560, 2, (B, T, Nkv, D), "bf16")
+    got = _gpu_decode(q, kc, vc, ctx)
+    pick = np.arange(len(edges))  # one sequence per context length
+    want = _oracle_decode(q[pick], kc[pick], vc[pick], ctx[pick])
+    assert max_abs(got[pick], want) <= BF16_TOL
+
+
 def test_decode_never_reads_beyond_context():
     B, Nh, Nkv, D, T = 3, 8, 2, 128, 700
     ctx = np.array([5, 333, 700], np.int32)
