@@ -40,6 +40,54 @@ __device__ __forceinline__ float rows_max4(float x) {
   return pair_max32(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
 }
 
+// Work item `item` of the split kernel, in the order the work-groups are dispatched: first every
+// sequence's full chunks (sequence-major), then the shorter last chunks of the sequences whose
+// context is not a multiple of the chunk, also sequence-major. Putting the short items last leaves
+// fewer compute units idle while the last items drain: -3.5 to -5 % decode time against the plain
+// sequence-major order of all chunks. Ordering the short chunks by length as well (longest or
+// shortest band first) measured slower than keeping them in sequence order. Returns false past the
+// last item. Called by every lane of a wave with the same `item`; the result is uniform over it.
+__device__ __forceinline__ bool decode_item(const DecodeArgs& a, int item, int& b_out, int& s_out) {
+  const int lane = threadIdx.x & 63;
+  int before = 0;  // full chunks of the sequences before this block of 64
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const int b = b0 + lane;
+    const int ctx = b < a.B ? min(max(a.ctx_lens[b], 0), a.max_ctx) : 0;
+    const int f = ctx / a.chunk;
+    int incl = f;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    const int total = __shfl(incl, 63);
+    if (item < before + total) {
+      const int l = __builtin_ctzll(__ballot(before + incl > item));
+      b_out = b0 + l;
+      s_out = item - before - (__shfl(incl, l) - __shfl(f, l));
+      return true;
+    }
+    before += total;
+  }
+  int j = item - before;  // index among the short last chunks
+  for (int b0 = 0; b0 < a.B; b0 += 64) {
+    const int b = b0 + lane;
+    const int ctx = b < a.B ? min(max(a.ctx_lens[b], 0), a.max_ctx) : 0;
+    const bool part = ctx % a.chunk != 0;
+    const unsigned long long m = __ballot(part);
+    const int cnt = __popcll(m);
+    if (j < cnt) {
+      const bool hit = part && __popcll(m & ((1ull << lane) - 1)) == j;
+      const int l = __builtin_ctzll(__ballot(hit));
+      b_out = b0 + l;
+      s_out = __shfl(ctx, l) / a.chunk;
+      return true;
+    }
+    j -= cnt;
+  }
+  return false;
+}
+
 // One work-group = 4 waves for (sequence b, KV head g, up to 16 of its query heads, one chunk).
 // Each wave streams its own 16-token stages (stage k of the chunk goes to wave k % 4) through a
 // private NB-deep LDS ring filled by direct-to-LDS loads, so no barrier is needed while streaming:
@@ -65,15 +113,15 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   const int G = a.Nh / a.Nkv;
   const int HG = G < 16 ? G : 16;
   const int n_hg = G / HG;  // head groups per KV head
-  // block order: head group fastest, then chunk, then sequence. The KV heads of one token sit side
-  // by side in a cache row, so consecutive work-groups (dispatched to different XCDs at the same
-  // time) read the neighbouring segments of the same rows together: +12 % bandwidth over a
-  // chunk-fastest order, which fetched each head's 256-byte segments of a row at different times.
+  // block order: head group fastest, then the work item (full chunks first, short last chunks
+  // after them). The KV heads of one token sit side by side in a cache row, so consecutive
+  // work-groups (dispatched to different XCDs at the same time) read the neighbouring segments of
+  // the same rows together: +12 % bandwidth over a chunk-fastest order, which fetched each head's
+  // 256-byte segments of a row at different times.
   const int nhg = a.Nkv * n_hg;
   const int hgi = blockIdx.x % nhg;
-  const int rest = blockIdx.x / nhg;
-  const int s = rest % a.nsplit;
-  const int b = rest / a.nsplit;
+  int b, s;
+  if (!decode_item(a, blockIdx.x / nhg, b, s)) return;  // past the last item
   const int g = hgi / n_hg;
   const int h0 = g * G + (hgi % n_hg) * HG;
   const int ctx = min(max(a.ctx_lens[b], 0), a.max_ctx);
