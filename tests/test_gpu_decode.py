@@ -83,6 +83,31 @@ def test_decode_contexts_at_chunk_edges():
     assert max_abs(got[pick], want) <= BF16_TOL
 
 
+def test_decode_workspace_needs_no_clearing():
+    """The split partials live in the caller's workspace: a workspace holding arbitrary bytes, and the
+    same workspace reused by consecutive calls with other contexts (and so other chunk counts), give
+    the oracle's result every time."""
+    import causal_head_attention_gqa_amd as attn
+    torch = __import__("torch")
+    B, Nh, Nkv, D, T = 6, 16, 4, 128, 3000
+    q = synth.normal(570, 0, (B, Nh, D), "bf16")
+    kc = synth.normal(570, 1, (B, T, Nkv, D), "bf16")
+    vc = synth.normal(570, 2, (B, T, Nkv, D), "bf16")
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(kc, "bf16"), to_dev(vc, "bf16")
+    need = attn.decode_workspace_bytes(B, Nh, Nkv, D, D, T, attn.ATTN_BF16)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(570)
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device="cuda", generator=gen)
+    contexts = [[3000, 1, 2048, 1025, 999, 2500], [17, 3000, 3000, 2049, 64, 1], [3000, 1, 2048, 1025, 999, 2500]]
+    for i, ctx in enumerate(contexts):
+        if i == 2:
+            ws.fill_(0xFF)
+        ctx = np.asarray(ctx, np.int32)
+        out = attn.decode(qd, kd, vd, torch.as_tensor(ctx, device="cuda"), workspace=ws)
+        got = out.float().cpu().numpy()
+        assert max_abs(got, _oracle_decode(q, kc, vc, ctx)) <= BF16_TOL, f"call {i}"
+
+
 def test_decode_never_reads_beyond_context():
     B, Nh, Nkv, D, T = 3, 8, 2, 128, 700
     ctx = np.array([5, 333, 700], np.int32)
@@ -195,8 +220,10 @@ def test_mla_decode_score_growth_beyond_reference(B, T, ctx, rope):
     assert max_abs(got, want) <= BF16_TOL
 
 
-@pytest.mark.parametrize("mla,B,Nh", [(False, 3, 8), (True, 3, 64), (True, 256, 64), (True, 3, 32), (True, 256, 32)],
-                         ids=["gqa", "mla64-split", "mla64-one-chunk", "mla32-split", "mla32-one-chunk"])
+@pytest.mark.parametrize("mla,B,Nh", [(False, 3, 8), (False, 600, 8), (True, 3, 64), (True, 256, 64), (True, 3, 32),
+                                     (True, 256, 32)],
+                         ids=["gqa-split", "gqa-one-chunk", "mla64-split", "mla64-one-chunk", "mla32-split",
+                              "mla32-one-chunk"])
 def test_decode_empty_context_gives_zero_row(mla, B, Nh):
     """A context of 0 keys (a precondition violation the kernels clamp) gives an all-zero output row,
     whether or not the call splits the context (single chunk: no merge follows); the other rows are
