@@ -142,15 +142,16 @@ int attn_prefill(const void* q, const void* k, const void* v, void* out, int B, 
   if (rope) {
     float2* table = static_cast<float2*>(workspace);
     void* krot = static_cast<char*>(workspace) + align_up((size_t)S * (size_t)(Dh / 2) * sizeof(float2));
-    hipError_t e = launch_rope_table(table, S, Dh, (double)rope_theta, st);
-    if (e != hipSuccess) return hip_status(e);
-    const long long rows = (long long)B * S * Nkv;
-    if (dtype == ATTN_BF16)
-      e = launch_rope_rotate_table<bf16_t>(static_cast<const bf16_t*>(k), static_cast<bf16_t*>(krot), table, rows,
-                                           S, Nkv, Dh, st);
-    else
-      e = launch_rope_rotate_table<float>(static_cast<const float*>(k), static_cast<float*>(krot), table, rows, S,
-                                          Nkv, Dh, st);
+    hipError_t e;
+    if (dtype == ATTN_BF16) {
+      e = launch_rope_table_rotate_bf16(static_cast<const bf16_t*>(k), static_cast<bf16_t*>(krot), table, B, S, Nkv,
+                                        Dh, (double)rope_theta, st);
+    } else {
+      e = launch_rope_table(table, S, Dh, (double)rope_theta, st);
+      if (e == hipSuccess)
+        e = launch_rope_rotate_table<float>(static_cast<const float*>(k), static_cast<float*>(krot), table,
+                                            (long long)B * S * Nkv, S, Nkv, Dh, st);
+    }
     if (e != hipSuccess) return hip_status(e);
     a.table = table;
     a.k = krot;

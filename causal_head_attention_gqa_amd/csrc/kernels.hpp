@@ -22,6 +22,9 @@ __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return bf16_t{f32_
 
 // ---- RoPE (rope.hip) ----
 hipError_t launch_rope_table(float2* table, int S, int D, double theta, hipStream_t st);
+// The table and the bf16 rotation of K [B, S, N, D] (positions 0 .. S-1) in one launch.
+hipError_t launch_rope_table_rotate_bf16(const bf16_t* src, bf16_t* dst, float2* table, int B, int S, int N, int D,
+                                         double theta, hipStream_t st);
 template <typename T>
 hipError_t launch_rope_rotate_table(const T* src, T* dst, const float2* table, long long rows, int S, int N,
                                     int D, hipStream_t st);

@@ -95,6 +95,58 @@ __global__ void rope_rotate_table_bf16_kernel(const uint16_t* __restrict__ src, 
   }
 }
 
+// The same rotation with the angle table made on the way (one launch instead of two): the threads
+// of a work-group cover the (s, g, 8-pair group) items first .. first+255, i.e. positions p0 .. p1;
+// they evaluate those positions' (cos, sin) once each (rope_cs, the table kernel's formula, so the
+// bits are the same), keep them in LDS for their own rotations and write them to `table` for the
+// prefill's q rotation. Entries of a position shared by two work-groups are written by both with
+// the same value. LDS: (p1 - p0 + 1) * D/2 <= (255 / (N * D/16) + 2) * D/2 <= 2040 + D entries.
+constexpr int kTableRotMaxD = 512;
+constexpr int kTableRotLds = 2040 + kTableRotMaxD;
+__global__ __launch_bounds__(256) void rope_table_rotate_bf16_kernel(const uint16_t* __restrict__ src,
+                                                                     uint16_t* __restrict__ dst,
+                                                                     float2* __restrict__ table, int B, int S,
+                                                                     int N, int D, double neg2_log2theta_over_d) {
+  __shared__ float2 cs_lds[kTableRotLds];
+  const int half = D / 2, groups = D / 16;
+  const long long total = (long long)S * N * groups;
+  const long long first = (long long)blockIdx.x * 256;
+  const long long last = min(first + 255, total - 1);
+  const int p0 = (int)(first / groups / N), p1 = (int)(last / groups / N);
+  const int nent = (p1 - p0 + 1) * half;
+  for (int e = threadIdx.x; e < nent; e += 256) {
+    const int pos = p0 + e / half, i = e % half;
+    const float2 c = rope_cs(pos, i, neg2_log2theta_over_d);
+    cs_lds[e] = c;
+    table[(long long)pos * half + i] = c;
+  }
+  __syncthreads();
+  const long long idx = first + threadIdx.x;
+  if (idx >= total) return;
+  const int i0 = (int)(idx % groups) * 8;
+  const long long sg = idx / groups;  // s * N + g
+  const int pos = (int)(sg / N);
+  const float2* tb = cs_lds + (pos - p0) * half + i0;
+  float2 cs[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) cs[e] = tb[e];
+  for (int b = 0; b < B; ++b) {
+    const long long off = ((long long)b * S * N + sg) * D + i0;
+    const U4 xa = ldg16(src + off), xb = ldg16(src + off + D / 2);
+    const uint32_t wa[4] = {xa.x, xa.y, xa.z, xa.w}, wb[4] = {xb.x, xb.y, xb.z, xb.w};
+    uint32_t ya[4], yb[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float2 r0 = rope_rot(bf16lo(wa[q]), bf16lo(wb[q]), cs[2 * q]);
+      const float2 r1 = rope_rot(bf16hi(wa[q]), bf16hi(wb[q]), cs[2 * q + 1]);
+      ya[q] = pack_bf16x2(r0.x, r1.x);
+      yb[q] = pack_bf16x2(r0.y, r1.y);
+    }
+    stg16(dst + off, U4{ya[0], ya[1], ya[2], ya[3]});
+    stg16(dst + off + D / 2, U4{yb[0], yb[1], yb[2], yb[3]});
+  }
+}
+
 // Copy of src [rows, D] into dst with the half-split pairs of the span [roff, roff + Dr) rotated by
 // the table [S][Dr/2] (row r has position (r / N) % S); dims outside the span are copied. One
 // thread per (row, 8 consecutive dims). Used for MLA's decoupled RoPE block ("Transformer 与 LLM"
@@ -313,6 +365,20 @@ template hipError_t launch_rope_rotate_table<float>(const float*, float*, const 
                                                     hipStream_t);
 template hipError_t launch_rope_rotate_table<bf16_t>(const bf16_t*, bf16_t*, const float2*, long long, int, int,
                                                      int, hipStream_t);
+
+hipError_t launch_rope_table_rotate_bf16(const bf16_t* src, bf16_t* dst, float2* table, int B, int S, int N, int D,
+                                         double theta, hipStream_t st) {
+  if (D % 16 != 0 || D > kTableRotMaxD || D <= 0 || B <= 0 || S <= 0 || N <= 0) {  // the two-launch form
+    hipError_t e = launch_rope_table(table, S, D, theta, st);
+    if (e != hipSuccess) return e;
+    return launch_rope_rotate_table<bf16_t>(src, dst, table, (long long)B * S * N, S, N, D, st);
+  }
+  const long long n = (long long)S * N * (D / 16);
+  const double k = -2.0 * log2(theta) / (double)D;
+  rope_table_rotate_bf16_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(
+      reinterpret_cast<const uint16_t*>(src), reinterpret_cast<uint16_t*>(dst), table, B, S, N, D, k);
+  return hipGetLastError();
+}
 template hipError_t launch_rope_apply<float>(float*, const int*, long long, int, int, int, double, int,
                                              hipStream_t);
 template hipError_t launch_rope_apply<bf16_t>(bf16_t*, const int*, long long, int, int, int, double, int,
