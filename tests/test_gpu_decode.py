@@ -83,6 +83,23 @@ def test_decode_contexts_at_chunk_edges():
     assert max_abs(got[pick], want) <= BF16_TOL
 
 
+def test_decode_more_than_64_sequences():
+    """130 sequences x 8 KV heads with contexts up to 1100: 1024-token chunks, so the kernel's work-item
+    order (every full chunk, then the short last chunks) spans three blocks of 64 sequences in both
+    parts; sequences from each block against the oracle."""
+    B, Nh, Nkv, D, T = 130, 8, 8, 64, 1100
+    rng = np.random.default_rng(575)
+    ctx = rng.integers(1, T, B, endpoint=True).astype(np.int32)
+    ctx[[5, 70, 129]] = [1024, 1100, 1025]
+    q = synth.normal(575, 0, (B, Nh, D), "bf16")
+    kc = synth.normal(575, 1, (B, T, Nkv, D), "bf16")
+    vc = synth.normal(575, 2, (B, T, Nkv, D), "bf16")
+    got = _gpu_decode(q, kc, vc, ctx)
+    pick = np.array([0, 5, 63, 64, 70, 100, 127, 128, 129])
+    want = _oracle_decode(q[pick], kc[pick], vc[pick], ctx[pick])
+    assert max_abs(got[pick], want) <= BF16_TOL
+
+
 def test_decode_workspace_needs_no_clearing():
     """The split partials live in the caller's workspace: a workspace holding arbitrary bytes, and the
     same workspace reused by consecutive calls with other contexts (and so other chunk counts), give
