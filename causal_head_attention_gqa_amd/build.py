@@ -128,11 +128,13 @@ def valu_sgpr_lds_hazards(asm: str, wait_states: int = 5) -> list[str]:
         open_regs = set(range(lo, hi + 1))
         ws = 0
         for u in reversed(lines[:i]):
-            if not u or u.startswith((";", ".")):
+            if not u or u.startswith(";"):  # comments, including "; %bb.N:" of fall-through blocks
                 continue
-            if u.endswith(":"):
+            if u.endswith(":"):  # a branch target (compiler labels start with "." too)
                 bad.append("label " + u + " within the wait window of " + t)
                 break
+            if u.startswith("."):  # directives
+                continue
             parts = u.split(None, 1)
             d = _sgprs(parts[1].split(",")[0]) if len(parts) > 1 and not u.startswith(no_dest) else None
             if d:
@@ -150,6 +152,60 @@ def valu_sgpr_lds_hazards(asm: str, wait_states: int = 5) -> list[str]:
     return bad
 
 
+_LDS_DMA = re.compile(r"^global_load_lds_dword")
+
+
+def m0_lds_dma_hazards(asm: str) -> list[str]:
+    """Direct-to-LDS loads that come too soon after an instruction that writes M0.
+
+    The load takes its LDS address from M0. A scalar instruction that writes M0 needs 1 wait
+    state before such a load, and a vector instruction that writes it (v_readfirstlane_b32 m0,
+    ...) needs 5. The compiler inserts these only in front of the loads it emits itself, not in
+    front of inline assembly, which is how the kernels issue these loads. Walking back from each
+    load, each instruction counts one wait state and s_nop N counts N + 1. The walk ends when a
+    scalar write of M0 is found at a safe distance, or after 5 wait states. A write found closer
+    than its hazard needs is reported, and so is a label reached before the walk ends (another
+    predecessor may have written M0).
+    """
+    lines = [ln.strip() for ln in asm.splitlines()]
+    bad = []
+    for i, t in enumerate(lines):
+        if not _LDS_DMA.match(t):
+            continue
+        ws = 0
+        for u in reversed(lines[:i]):
+            if not u or u.startswith(";"):  # comments, including "; %bb.N:" of fall-through blocks
+                continue
+            if u.endswith(":"):  # a branch target (compiler labels start with "." too)
+                bad.append("label " + u + " within the M0 wait window of " + t)
+                break
+            if u.startswith("."):  # directives
+                continue
+            parts = u.split(None, 1)
+            dest = parts[1].split(",")[0].strip() if len(parts) > 1 else ""
+            if dest == "m0":
+                if u.startswith("v_"):
+                    bad.append(u + " -> " + t)  # any vector write within 5 wait states
+                elif ws < 1:
+                    bad.append(u + " -> " + t)
+                break
+            m = re.match(r"s_nop\s+(\d+)", u)
+            ws += int(m.group(1)) + 1 if m else 1
+            if ws >= 5:
+                break
+    return bad
+
+
+def scan(text: str) -> list[tuple[str, list[str]]]:
+    """Every check of the generated assembly, as (what is wrong, offending lines) pairs."""
+    return [
+        ("MFMA destination overlaps a source operand", mfma_overlaps(text)),
+        ("sign-extended base address of a direct-to-LDS load", sign_extended_lds_bases(text)),
+        ("direct-to-LDS load reads an SGPR a VALU wrote < 5 wait states earlier", valu_sgpr_lds_hazards(text)),
+        ("direct-to-LDS load too soon after an M0 write", m0_lds_dma_hazards(text)),
+    ]
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
     asm = os.path.join(BUILD, os.path.basename(src)[:-4] + ".s")
@@ -164,18 +220,10 @@ def _compile(src: str) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"hipcc -S failed for {src}:\n{r.stderr}")
     with open(asm) as f:
-        bad = mfma_overlaps(f.read())
-    if bad:
-        raise RuntimeError(f"{src}: MFMA destination overlaps a source operand:\n" + "\n".join(bad[:5]))
-    with open(asm) as f:
         text = f.read()
-    bad = sign_extended_lds_bases(text)
-    if bad:
-        raise RuntimeError(f"{src}: sign-extended base address of a direct-to-LDS load:\n" + "\n".join(bad[:5]))
-    bad = valu_sgpr_lds_hazards(text)
-    if bad:
-        raise RuntimeError(f"{src}: direct-to-LDS load reads an SGPR a VALU wrote < 5 wait states earlier:\n"
-                           + "\n".join(bad[:5]))
+    for what, bad in scan(text):
+        if bad:
+            raise RuntimeError(f"{src}: {what}:\n" + "\n".join(bad[:5]))
     return obj
 
 

@@ -102,6 +102,8 @@ int attn_prefill(const void* q, const void* k, const void* v, void* out, int B, 
   if (!std::isfinite(rope_theta) || !std::isfinite(scale)) return ATTN_ERR_INVALID;
   if (!prefill_supported(dtype, Dh)) return ATTN_ERR_UNSUPPORTED;
   if ((long long)B * S * Nh > (1LL << 40)) return ATTN_ERR_INVALID;
+  // the bf16 kernel addresses a 32-key tile with 32-bit per-lane byte offsets (32 rows of Nkv*Dh)
+  if ((long long)Nkv * Dh * 32 * (long long)esize(dtype) > 0x7fffffffLL) return ATTN_ERR_INVALID;
   if (B == 0 || S == 0) return ATTN_OK;
   if (!q || !k || !v || !out) return ATTN_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_ERR_INVALID;

@@ -99,13 +99,17 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 // the wave (byte address) goes through M0. kStream adds the non-temporal hint, for rows that are
 // read once (the decode caches; it measurably raises the achieved HBM bandwidth there); tiles that
 // other work-groups read again (prefill K/V) keep the default policy.
+// A global load with the LDS bit must come at least one wait state after a scalar instruction
+// that writes M0. The compiler writes M0 for the "{m0}" operand directly in front of the asm and
+// does not insert hazard wait states in front of inline assembly, so the s_nop 0 is part of the
+// asm itself (the build scans the generated code for any M0 write closer to such a load).
 template <bool kStream = true>
 __device__ __forceinline__ void load_lds16_async(const void* gptr, const void* lds_base) {
   const uint32_t lds_addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
   if constexpr (kStream)
-    asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(gptr), "{m0}"(lds_addr) : "memory");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(gptr), "{m0}"(lds_addr) : "memory");
   else
-    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(lds_addr) : "memory");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"(lds_addr) : "memory");
 }
 
 // The same load with a wave-uniform base in SGPRs and a 32-bit per-lane byte offset: the
@@ -116,7 +120,7 @@ __device__ __forceinline__ void load_lds16_async(const void* gptr, const void* l
 // insert in front of inline assembly (the build rejects such sequences in the generated code).
 __device__ __forceinline__ void load_lds16_async_sv(const void* sbase, uint32_t voff, const void* lds_base) {
   const uint32_t lds_addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
 }
 
 // Work-group barrier without the memory fences of __syncthreads(): for tiles filled by

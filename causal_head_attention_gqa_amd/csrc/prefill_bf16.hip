@@ -160,9 +160,16 @@ __global__ __launch_bounds__(kThreads, (DQK > 128 ? 2 : 3)) void prefill_bf16_ke
               }
             }
           };
+          // one branch per span: rope_dims / 32 register pairs (the host accepts multiples of 32
+          // up to the rotated block's width, so every accepted span has its branch)
           if (rope_dims == 32) half(std::integral_constant<int, 1>{});
           else if (rope_dims == 64) half(std::integral_constant<int, 2>{});
-          else if constexpr (DQK - kRopeOff >= 128) half(std::integral_constant<int, 4>{});
+          else if constexpr (DQK - kRopeOff >= 96) {
+            if (rope_dims == 96) half(std::integral_constant<int, 3>{});
+            else if constexpr (DQK - kRopeOff >= 128) {
+              if (rope_dims == 128) half(std::integral_constant<int, 4>{});
+            }
+          }
         }
       }
     } else {

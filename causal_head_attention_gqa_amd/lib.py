@@ -116,6 +116,34 @@ def _need_cuda(*ts):
             raise ValueError("tensors must be contiguous")
 
 
+def _check_out(out, shape, dtype, device):
+    """A caller-supplied output must be exactly what the kernel writes: shape, dtype, device, dense."""
+    if not out.is_cuda or out.device != device:
+        raise ValueError(f"out must live on {device}")
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"out must have shape {tuple(shape)}, got {tuple(out.shape)}")
+    if out.dtype != dtype:
+        raise TypeError(f"out must be {dtype}, got {out.dtype}")
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    return out
+
+
+def _workspace(ws, need: int, device):
+    """(pointer, bytes) of a workspace: torch allocates it when the caller gives none; a given one
+    must be a dense buffer on the same device (its size is checked by the library)."""
+    torch = _torch()
+    if ws is None:
+        if need <= 0:
+            return None, 0
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    if not ws.is_cuda or ws.device != device:
+        raise ValueError(f"workspace must live on {device}")
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
 def prefill_workspace_bytes(B: int, S: int, Nkv: int, Dh: int, rope_theta: float, dtype: int) -> int:
     return int(load().attn_prefill_workspace_bytes(B, S, Nkv, Dh, float(rope_theta), dtype))
 
@@ -136,14 +164,8 @@ def prefill(q, k, v, *, rope_theta: float = 0.0, causal: bool = True, scale: flo
     dt = _dtype_code(q)
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share one dtype")
-    if out is None:
-        out = torch.empty_like(q)
-    _need_cuda(out)
-    need = prefill_workspace_bytes(B, S, Nkv, Dh, rope_theta, dt)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    out = torch.empty_like(q) if out is None else _check_out(out, q.shape, q.dtype, q.device)
+    ws_ptr, ws_len = _workspace(workspace, prefill_workspace_bytes(B, S, Nkv, Dh, rope_theta, dt), q.device)
     st = load().attn_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, S, Nh, Nkv, Dh,
                              float(rope_theta), 1 if causal else 0, float(scale or 0.0), dt, ws_ptr, ws_len,
                              _stream_ptr(q.device))
@@ -169,14 +191,8 @@ def prefill_mla(q, k, v, *, rope_theta: float = 0.0, causal: bool = True, scale:
         raise TypeError("MLA prefill takes bf16 q, k, v")
     if out is None:
         out = torch.empty((B, S, Nh, 128), dtype=q.dtype, device=q.device)
-    _need_cuda(out)
-    if out.shape != (B, S, Nh, 128) or out.dtype != q.dtype:
-        raise ValueError("out must be [B, S, Nh, 128] bf16")
-    need = prefill_mla_workspace_bytes(B, S, Nkv, rope_theta)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check_out(out, (B, S, Nh, 128), q.dtype, q.device)
+    ws_ptr, ws_len = _workspace(workspace, prefill_mla_workspace_bytes(B, S, Nkv, rope_theta), q.device)
     st = load().attn_prefill_mla(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, S, Nh, Nkv,
                                  float(rope_theta), 1 if causal else 0, float(scale or 0.0), ws_ptr, ws_len,
                                  _stream_ptr(q.device))
@@ -209,15 +225,16 @@ def decode(q, kcache, vcache, ctx_lens, *, scale: float | None = None, rope_thet
     if ctx_lens.dtype != torch.int32 or ctx_lens.shape != (B,):
         raise ValueError("ctx_lens must be int32 [B]")
     dt = _dtype_code(q)
+    if kcache.dtype != q.dtype or vcache.dtype != q.dtype:
+        raise TypeError("q and the caches must share one dtype")
     if out is None:
         out = torch.empty((B, Nh, Dv), dtype=q.dtype, device=q.device)
-    need = decode_workspace_bytes(B, Nh, Nkv, Dqk, Dv, max_ctx, dt)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_out(out, (B, Nh, Dv), q.dtype, q.device)
+    ws_ptr, ws_len = _workspace(workspace, max(decode_workspace_bytes(B, Nh, Nkv, Dqk, Dv, max_ctx, dt), 1),
+                                q.device)
     st = load().attn_decode(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), ctx_lens.data_ptr(), out.data_ptr(),
                             B, Nh, Nkv, Dqk, Dv, max_ctx, kcache.stride(2), vcache.stride(2), float(rope_theta),
-                            float(scale or 0.0), dt, workspace.data_ptr(),
-                            workspace.numel() * workspace.element_size(), _stream_ptr(q.device))
+                            float(scale or 0.0), dt, ws_ptr, ws_len, _stream_ptr(q.device))
     _check(st, "attn_decode")
     return out
 
@@ -269,13 +286,10 @@ def prefill_cached(q, kcache, vcache, q_start, *, rope_theta: float = 0.0, rope_
         raise ValueError("cache rows shorter than the head dim")
     if q_start.dtype != torch.int32 or q_start.shape != (B,):
         raise ValueError("q_start must be int32 [B]")
-    if out is None:
-        out = torch.empty_like(q)
-    need = prefill_cached_workspace_bytes(max_ctx, Dh, rope_theta)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = workspace.data_ptr() if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if kcache.dtype != q.dtype or vcache.dtype != q.dtype:
+        raise TypeError("q and the caches must share one dtype")
+    out = torch.empty_like(q) if out is None else _check_out(out, q.shape, q.dtype, q.device)
+    ws_ptr, ws_bytes = _workspace(workspace, prefill_cached_workspace_bytes(max_ctx, Dh, rope_theta), q.device)
     st = load().attn_prefill_cached(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), q_start.data_ptr(),
                                     out.data_ptr(), B, S, Nh, Nkv, Dh, max_ctx, ld, float(rope_theta), int(rope_dims),
                                     1 if rope_interleaved else 0, 1 if causal else 0, int(window), int(sinks),
@@ -302,6 +316,8 @@ def kv_append(k_new, v_new, kcache, vcache, start, *, rope_theta: float = 0.0, r
         raise ValueError("cache shapes disagree with k_new")
     if start.dtype != torch.int32 or start.shape != (B,):
         raise ValueError("start must be int32 [B]")
+    if v_new.dtype != k_new.dtype or kcache.dtype != k_new.dtype or vcache.dtype != k_new.dtype:
+        raise TypeError("new rows and caches must share one dtype")
     st = load().attn_kv_append(k_new.data_ptr(), v_new.data_ptr(), kcache.data_ptr(), vcache.data_ptr(),
                                start.data_ptr(), B, S, Nkv, Dh, max_ctx, ldk, ldv, float(rope_theta), int(rope_dims),
                                1 if interleaved else 0, _dtype_code(k_new), _stream_ptr(k_new.device))

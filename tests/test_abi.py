@@ -66,6 +66,8 @@ def test_prefill_argument_errors():
     assert call(rope=1e4, ws=P, wsb=16) == 3    # too small
     assert call(rope=float("nan")) == 1
     assert call(B=0) == 0 and call(S=0) == 0    # empty: nothing to do
+    # a 32-key tile of Nkv * Dh elements per row must stay addressable with 32-bit byte offsets
+    assert call(Nh=1 << 20, Nkv=1 << 20) == 1
 
 
 def test_decode_argument_errors():
@@ -180,3 +182,50 @@ def test_prefill_mla_workspace_query():
     assert lib.prefill_mla_workspace_bytes(1, 4096, 128, 0.0) == 0
     # fp32 (cos, sin) table [S, 32] plus keys with the rotated k^R block
     assert lib.prefill_mla_workspace_bytes(1, 4096, 128, 1e4) == 4096 * 32 * 8 + 4096 * 128 * 192 * 2
+
+
+class _FakeTensor:
+    """Just enough of a device tensor for the binding's checks of caller-supplied buffers."""
+
+    def __init__(self, shape, dtype, device="cuda:0", contiguous=True, cuda=True):
+        import torch
+        self.shape = tuple(shape)
+        self.dtype = dtype
+        self.device = torch.device(device)
+        self.is_cuda = cuda
+        self._c = contiguous
+
+    def is_contiguous(self):
+        return self._c
+
+
+def test_binding_rejects_mismatched_out_buffers():
+    import torch
+    from causal_head_attention_gqa_amd import lib
+    dev = torch.device("cuda:0")
+    good = _FakeTensor((2, 8, 4, 64), torch.bfloat16)
+    assert lib._check_out(good, (2, 8, 4, 64), torch.bfloat16, dev) is good
+    with pytest.raises(ValueError):
+        lib._check_out(_FakeTensor((2, 8, 4, 32), torch.bfloat16), (2, 8, 4, 64), torch.bfloat16, dev)  # too small
+    with pytest.raises(TypeError):
+        lib._check_out(_FakeTensor((2, 8, 4, 64), torch.float32), (2, 8, 4, 64), torch.bfloat16, dev)
+    with pytest.raises(ValueError):
+        lib._check_out(_FakeTensor((2, 8, 4, 64), torch.bfloat16, contiguous=False), (2, 8, 4, 64),
+                       torch.bfloat16, dev)
+    with pytest.raises(ValueError):
+        lib._check_out(_FakeTensor((2, 8, 4, 64), torch.bfloat16, device="cpu", cuda=False), (2, 8, 4, 64),
+                       torch.bfloat16, dev)
+    with pytest.raises(ValueError):
+        lib._check_out(_FakeTensor((2, 8, 4, 64), torch.bfloat16, device="cuda:1"), (2, 8, 4, 64),
+                       torch.bfloat16, dev)
+
+
+def test_binding_rejects_foreign_workspaces():
+    import torch
+    from causal_head_attention_gqa_amd import lib
+    dev = torch.device("cuda:0")
+    with pytest.raises(ValueError):
+        lib._workspace(_FakeTensor((64,), torch.uint8, device="cpu", cuda=False), 64, dev)
+    with pytest.raises(ValueError):
+        lib._workspace(_FakeTensor((64,), torch.uint8, contiguous=False), 64, dev)
+    assert lib._workspace(None, 0, dev) == (None, 0)

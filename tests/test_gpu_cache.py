@@ -201,6 +201,8 @@ ROPE_CASES = [
     (128, 128, True, 5e5),
     (64, 32, True, 1e4),
     (128, 32, False, 5e5),
+    (128, 96, False, 1e4),  # three register pairs of the half-split q rotation
+    (128, 96, True, 1e4),
 ]
 
 

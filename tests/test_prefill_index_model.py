@@ -105,3 +105,95 @@ def test_swizzle_is_a_permutation_per_row():
     for ch in (8, 16, 24):
         for row in range(KBC):
             assert sorted(swz(ch, c, row) for c in range(ch)) == list(range(ch))
+
+
+# ---- the whole grid: block id -> (sequence, head group, q-tile), then every access's extent ----
+def grid_map(B, S, Nh, HPW, n_ptiles):
+    """(b, h0, pt) of every work-group id, as the kernel computes them."""
+    HGn = Nh // HPW
+    npairs = B * HGn
+    ids = np.arange(n_ptiles * npairs, dtype=np.int64)
+    if npairs % 8 == 0:
+        li = ids // 8
+        bh = ids % 8 + 8 * (li // n_ptiles)
+        pt = n_ptiles - 1 - li % n_ptiles
+    else:
+        bh = ids % npairs
+        pt = n_ptiles - 1 - ids // npairs
+    return bh // HGn, (bh % HGn) * HPW, pt
+
+
+def lane_offsets(d, tok):
+    """Per-lane element offsets (row * tok + physical chunk * 8) of one tile's loads, all waves."""
+    lp = KBC * (d // 8) // 64 // 4
+    offs, rows = [], []
+    for w in range(4):
+        for r in range(lp):
+            sl = w * lp + r
+            for lane in range(64):
+                b = sl * 1024 + 16 * lane
+                row, pc = b // (d * 2), (b % (d * 2)) // 16
+                assert row * tok < 2 ** 31  # the kernel forms row * (int)tok in 32 bits
+                offs.append(row * tok + swz(d // 8, pc, row) * 8)
+                rows.append(row)
+    return np.array(offs, np.int64), np.array(rows, np.int64)
+
+
+GRID_CASES = [
+    # B, S, Nh, Nkv, DQK, DV, causal
+    (1, 4096, 128, 128, 192, 128, True),   # DeepSeek-V3-shaped MLA non-absorbed prefill
+    (4, 8192, 32, 8, 128, 128, True),      # Llama-3-8B-shaped GQA prefill
+    (8, 1024, 12, 12, 64, 64, True),       # GPT-2-small-shaped prefill
+    (1, 200, 4, 4, 192, 128, True),
+    (2, 97, 4, 4, 192, 128, True),
+    (1, 130, 8, 2, 192, 128, True),
+    (1, 150, 4, 2, 192, 128, False),
+    (3, 1, 4, 4, 192, 128, True),
+    (1, 256, 2, 2, 192, 128, True),
+]
+
+
+@pytest.mark.parametrize("case", GRID_CASES, ids=lambda c: "B%dS%dH%dK%d_%d_%d_c%d" % c)
+def test_grid_covers_every_tile_once_and_stays_in_bounds(case):
+    B, S, Nh, Nkv, dqk, dv, causal = case
+    G = Nh // Nkv
+    HPW = 4 if G % 4 == 0 else 2 if G % 2 == 0 else 1
+    BP = 32 * (4 // HPW)
+    n_ptiles = (S + BP - 1) // BP
+    b, h0, pt = grid_map(B, S, Nh, HPW, n_ptiles)
+    # every (sequence, head group, q-tile) exactly once: nothing skipped, nothing written twice
+    keys = (b * (Nh // HPW) + h0 // HPW) * n_ptiles + pt
+    assert np.array_equal(np.sort(keys), np.arange(B * (Nh // HPW) * n_ptiles))
+    assert b.min() >= 0 and b.max() < B and h0.max() + HPW <= Nh and pt.min() >= 0
+    g = h0 // G
+    p0 = pt * BP
+    # K (the rotated copy in the workspace when RoPE is on, same layout) and V: [B, S, Nkv, d]
+    for d in (dqk, dv):
+        tok, batch, head = Nkv * d, S * Nkv * d, d
+        size = B * S * Nkv * d
+        loff, lrow = lane_offsets(d, tok)
+        last = np.minimum(S, p0 + BP) if causal else np.full_like(p0, S)
+        n_tiles = (last + KBC - 1) // KBC
+        base = b * batch + g * head
+        # full tiles (jt * 32 + 32 <= S): base + jt * 32 * tok + loff, increasing in jt and loff
+        n_full = np.minimum(n_tiles, S // KBC)
+        has_full = n_full > 0
+        lo = base + loff.min()
+        hi = base + (n_full - 1) * KBC * tok + loff.max() + 8
+        if has_full.any():
+            assert lo[has_full].min() >= 0 and hi[has_full].max() <= size
+            assert ((n_full - 1) * KBC + lrow.max())[has_full].max() <= S - 1  # keys inside the sequence
+        # a partial last tile: key = min(jt * 32 + row, S - 1), chunk inside the row
+        part = n_tiles > n_full
+        if part.any():
+            key_hi = np.minimum((n_tiles - 1) * KBC + lrow.max(), S - 1)
+            hi_p = base + key_hi * tok + d
+            assert hi_p[part].max() <= size and ((n_tiles - 1) * KBC)[part].min() >= 0
+    # q reads and out writes of the rows p < S: [B, S, Nh, dqk] / [B, S, Nh, dv]
+    for w in range(4):
+        h = h0 + w % HPW
+        pw = p0 + (w // HPW) * 32 + 31  # the wave's last row
+        pw = np.minimum(pw, S - 1)
+        q_hi = ((b * S + pw) * Nh + h) * dqk + 8 + (dqk // 16 - 1) * 16 + 8
+        o_hi = ((b * S + pw) * Nh + h) * dv + 4 + (dv // 32 - 1) * 32 + 3 * 8 + 4
+        assert q_hi.max() <= B * S * Nh * dqk and o_hi.max() <= B * S * Nh * dv
