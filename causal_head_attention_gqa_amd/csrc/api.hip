@@ -162,8 +162,6 @@ int attn_prefill(const void* q, const void* k, const void* v, void* out, int B, 
   return hip_status(e);
 }
 
-constexpr bool kMlaPrefillEnabled = false;
-
 size_t attn_prefill_mla_workspace_bytes(int B, int S, int Nkv, float rope_theta) {
   if (!(rope_theta > 0.f) || B <= 0 || S <= 0 || Nkv <= 0) return 0;
   return align_up((size_t)S * 32 * sizeof(float2)) + align_up((size_t)B * S * Nkv * 192 * 2);
@@ -181,11 +179,6 @@ int attn_prefill_mla(const void* q, const void* k, const void* v, void* out, int
   const size_t need = attn_prefill_mla_workspace_bytes(B, S, Nkv, rope_theta);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
     return ATTN_ERR_WORKSPACE;
-
-  // The 192/128 kernel variant is compiled but not enabled: it has not yet passed its device tests
-  // (its first device runs faulted; the causes found in the generated code are fixed, see the
-  // build's assembly scans), so the call stops here after validating its arguments.
-  if (!kMlaPrefillEnabled) return ATTN_ERR_UNSUPPORTED;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const double sc = scale > 0.f ? (double)scale : 1.0 / std::sqrt(192.0);

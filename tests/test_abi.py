@@ -173,7 +173,7 @@ def test_prefill_mla_argument_errors():
     assert call(rope=float("nan")) == 1
     assert call(scale=float("inf")) == 1
     assert call(B=0) == 0 and call(S=0) == 0
-    assert call() == 2                          # valid arguments: the variant is not enabled yet
+    # (valid arguments would launch: never with these stand-in addresses)
 
 
 def test_prefill_mla_workspace_query():

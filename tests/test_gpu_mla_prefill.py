@@ -12,12 +12,7 @@ import oracle
 import synth
 from gpu_util import BF16_TOL, max_abs, to_dev, to_host_f64, values
 
-pytestmark = [
-    pytest.mark.gpu,
-    pytest.mark.skip(reason="attn_prefill_mla is disabled (returns ATTN_ERR_UNSUPPORTED): its first device runs "
-                            "faulted on a sign-extended and then a hazard-read SGPR base in the tile loads; both "
-                            "causes are fixed and rejected by the build scans, the fixed kernel awaits its device run"),
-]
+pytestmark = pytest.mark.gpu
 
 
 def _inputs(wid, B, S, Nh, Nkv):
@@ -62,17 +57,22 @@ def test_mla_prefill_row0_is_v0_exactly():
 
 
 def test_mla_prefill_scale_and_workspace_reuse():
-    """An explicit scale equal to the default gives the same bits; a caller-owned workspace of the
-    queried size gives the same bits as one the binding allocates."""
+    """A caller-owned workspace of the queried size gives the same bits as one the binding
+    allocates. An explicit scale of 1/sqrt(192) matches the default within the tolerance (the
+    explicit value is an fp32 number, the default is formed in fp64, so the two can differ in the
+    last bit of the exponent scale and hence in a few output bits)."""
     import causal_head_attention_gqa_amd as attn
     torch = __import__("torch")
     q, k, v = _inputs(651, 1, 160, 4, 4)
     qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
     a = attn.prefill_mla(qd, kd, vd, rope_theta=1e4)
-    b = attn.prefill_mla(qd, kd, vd, rope_theta=1e4, scale=1.0 / np.sqrt(192.0))
     ws = torch.empty(attn.prefill_mla_workspace_bytes(1, 160, 4, 1e4), dtype=torch.uint8, device=qd.device)
     c = attn.prefill_mla(qd, kd, vd, rope_theta=1e4, workspace=ws)
-    assert torch.equal(a, b) and torch.equal(a, c)
+    assert torch.equal(a, c), "caller workspace changed the result"
+    b = attn.prefill_mla(qd, kd, vd, rope_theta=1e4, scale=1.0 / np.sqrt(192.0))
+    want = oracle.prefill(values(q, "bf16"), values(k, "bf16"), values(v, "bf16"), causal=True, rope_theta=1e4)
+    assert max_abs(to_host_f64(b), want) <= BF16_TOL
+    assert max_abs(to_host_f64(a), to_host_f64(b)) <= 2 ** -6
     k_before = kd.clone()
     attn.prefill_mla(qd, kd, vd, rope_theta=1e4)
     assert torch.equal(kd, k_before)  # keys are rotated into the workspace, never in place
