@@ -57,7 +57,38 @@ __device__ __forceinline__ float rows_sum(float x) {
   return pair_sum32(__uint_as_float(r[0]) + __uint_as_float(r[1]));
 }
 
-template <int NW>
+// decoupled RoPE of one lane's q^R pairs: dims 512 + i held in `a` (i = i0 .. i0+7), their
+// half-split partners 544 + i in `b`; frequency theta^(-2i/64), position pos. The rotated fp32
+// value x is kept as two bf16 numbers, hi = bf16(x) in a / b and lo = bf16(x - hi) in alo / blo
+// (x - hi is exact in fp32): the products then see q^R to ~2^-17 instead of bf16's 2^-9, which
+// matters when k^R is large and the softmax is nearly one-hot.
+__device__ __forceinline__ void rope_qr_hilo(U4& a, U4& b, U4& alo, U4& blo, int i0, int pos, double theta) {
+  const double k2 = -2.0 * log2(theta) / (double)(DQ - DV);
+  uint32_t* pa = &a.x;
+  uint32_t* pb = &b.x;
+  uint32_t* la = &alo.x;
+  uint32_t* lb = &blo.x;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float ra[2], rb[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      double sn, cs;
+      sincos((double)pos * exp2(k2 * (double)(i0 + 2 * e + hf)), &sn, &cs);
+      const double x = hf ? bf16hi(pa[e]) : bf16lo(pa[e]);
+      const double y = hf ? bf16hi(pb[e]) : bf16lo(pb[e]);
+      ra[hf] = (float)(x * cs - y * sn);
+      rb[hf] = (float)(x * sn + y * cs);
+    }
+    pa[e] = pack_bf16x2(ra[0], ra[1]);
+    pb[e] = pack_bf16x2(rb[0], rb[1]);
+    la[e] = pack_bf16x2(ra[0] - bf16lo(pa[e]), ra[1] - bf16hi(pa[e]));
+    lb[e] = pack_bf16x2(rb[0] - bf16lo(pb[e]), rb[1] - bf16hi(pb[e]));
+  }
+}
+
+// kRope: rotate q^R in-kernel (a.rope_theta > 0) and add the products of its bf16 residuals.
+template <int NW, bool kRope>
 __global__ __launch_bounds__(NW * 64, (NW >= 8 ? 2 : 1)) void decode_mla_kernel(DecodeArgs a) {
   constexpr int NT = NW * 64;
   constexpr int SPW = (NSLOT + NW - 1) / NW;  // load slots per wave (some waves one fewer)
@@ -93,37 +124,23 @@ __global__ __launch_bounds__(NW * 64, (NW >= 8 ? 2 : 1)) void decode_mla_kernel(
 
   // Q^T operand: head h, dims kk*32 + rg*8 .. +7
   bf16x8 qreg[NKK];
+  bf16x8 qlo[2];  // kRope: bf16 residuals of the rotated q^R (k-steps 16, 17)
   {
     const uint16_t* qp = a.q + ((long long)b * a.Nh + h) * DQ + rg * 8;
     U4 raw[NKK];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) raw[kk] = ldg16(qp + kk * 32);
-    if (a.rope_theta > 0) {
+    U4 lo[2] = {U4{0, 0, 0, 0}, U4{0, 0, 0, 0}};
+    if (kRope) {
       // decoupled RoPE on the q^R block (dims 512..575, slide 06 of "Transformer 与 LLM"): half-split
       // pairs (512 + i, 544 + i), frequency theta^(-2i/64), position ctx-1; the cache holds rotated
       // k^R. Dims 512 + rg*8 + j sit in raw[16], their partners in raw[17] of the same lane.
-      const double k2 = -2.0 * log2(a.rope_theta) / (double)(DQ - DV);
-      uint32_t* pa = &raw[DV / 32].x;
-      uint32_t* pb = &raw[DV / 32 + 1].x;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float ra[2], rb[2];
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int i = rg * 8 + 2 * e + hf;
-          double sn, cs;
-          sincos((double)(ctx - 1) * exp2(k2 * (double)i), &sn, &cs);
-          const double x = hf ? bf16hi(pa[e]) : bf16lo(pa[e]);
-          const double y = hf ? bf16hi(pb[e]) : bf16lo(pb[e]);
-          ra[hf] = (float)(x * cs - y * sn);
-          rb[hf] = (float)(x * sn + y * cs);
-        }
-        pa[e] = pack_bf16x2(ra[0], ra[1]);
-        pb[e] = pack_bf16x2(rb[0], rb[1]);
-      }
+      rope_qr_hilo(raw[DV / 32], raw[DV / 32 + 1], lo[0], lo[1], rg * 8, ctx - 1, a.rope_theta);
     }
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) qreg[kk] = as_bf16x8(raw[kk]);
+    qlo[0] = as_bf16x8(lo[0]);
+    qlo[1] = as_bf16x8(lo[1]);
     retire_vmem();
   }
 
@@ -176,6 +193,17 @@ __global__ __launch_bounds__(NW * 64, (NW >= 8 ? 2 : 1)) void decode_mla_kernel(
         sacc[tg] = mfma16x16x32(ka, qreg[kk], sacc[tg]);
       }
       if (kk % 3 == 2) __builtin_amdgcn_sched_barrier(0);  // bound how far LDS reads are hoisted
+    }
+    if constexpr (kRope) {  // the q^R residuals against k-steps 16 and 17
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int kk = NKK - 2 + u;
+#pragma unroll
+        for (int tg = 0; tg < 2; ++tg) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Tt + tg * 16 * DQ + koff[kk & 3] + 32 * (kk & ~3));
+          sacc[tg] = mfma16x16x32(ka, qlo[u], sacc[tg]);
+        }
+      }
     }
     const int tbase = t0 + j * TT;
     if (tbase + TT > t1) {
@@ -306,29 +334,8 @@ __device__ __forceinline__ int key(int row) {
   return (((row >> 1) & 1) << 2) | (((row >> 2) & 1) << 1) | ((row >> 3) & 1);
 }
 
-// decoupled RoPE of one lane's q^R pairs: dims 512 + i held in `a` (i = i0 .. i0+7), their
-// half-split partners 544 + i in `b`; frequency theta^(-2i/64), position pos
-__device__ __forceinline__ void rope_qr(U4& a, U4& b, int i0, int pos, double theta) {
-  const double k2 = -2.0 * log2(theta) / (double)(DQ - DV);
-  uint32_t* pa = &a.x;
-  uint32_t* pb = &b.x;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    float ra[2], rb[2];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      double sn, cs;
-      sincos((double)pos * exp2(k2 * (double)(i0 + 2 * e + hf)), &sn, &cs);
-      const double x = hf ? bf16hi(pa[e]) : bf16lo(pa[e]);
-      const double y = hf ? bf16hi(pb[e]) : bf16lo(pb[e]);
-      ra[hf] = (float)(x * cs - y * sn);
-      rb[hf] = (float)(x * sn + y * cs);
-    }
-    pa[e] = pack_bf16x2(ra[0], ra[1]);
-    pb[e] = pack_bf16x2(rb[0], rb[1]);
-  }
-}
-
+// kRope: rotate q^R in-kernel (a.rope_theta > 0) and add the products of its bf16 residuals.
+template <bool kRope>
 __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_pair_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t ring[kStages][TILE];
   __shared__ __attribute__((aligned(16))) float xch[kWaves][4][64][4];  // partial scores per wave
@@ -366,19 +373,23 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_pair_kernel(DecodeA
 
   // Q^T operand of k-step kk: head h, dims 288r + 16kk + 8hf .. +7
   bf16x8 qreg[kKS];
+  bf16x8 qlo[4];  // kRope, upper half: bf16 residuals of the rotated q^R (k-steps 14..17)
   {
     const uint16_t* qp = a.q + ((long long)b * a.Nh + h) * DQ + r * kHalfQ + hf * 8;
     U4 raw[kKS];
 #pragma unroll
     for (int kk = 0; kk < kKS; ++kk) raw[kk] = ldg16(qp + kk * 16);
-    if (a.rope_theta > 0 && r == 1) {
+    U4 lo[4] = {U4{0, 0, 0, 0}, U4{0, 0, 0, 0}, U4{0, 0, 0, 0}, U4{0, 0, 0, 0}};
+    if (kRope && r == 1) {
       // q^R = dims 512..575 = k-steps 14..17 of the upper half: dims 512 + 16u + 8hf + j in
       // raw[14 + u], their partners 544 + 16u + 8hf + j in raw[16 + u]
-      rope_qr(raw[14], raw[16], hf * 8, ctx - 1, a.rope_theta);
-      rope_qr(raw[15], raw[17], 16 + hf * 8, ctx - 1, a.rope_theta);
+      rope_qr_hilo(raw[14], raw[16], lo[0], lo[2], hf * 8, ctx - 1, a.rope_theta);
+      rope_qr_hilo(raw[15], raw[17], lo[1], lo[3], 16 + hf * 8, ctx - 1, a.rope_theta);
     }
 #pragma unroll
     for (int kk = 0; kk < kKS; ++kk) qreg[kk] = as_bf16x8(raw[kk]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) qlo[u] = as_bf16x8(lo[u]);
     retire_vmem();  // from here on only the tile loads count in vmcnt
   }
 
@@ -445,6 +456,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_pair_kernel(DecodeA
     for (int kk = 0; kk < kKS; ++kk) {
       sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk % kKR], qreg[kk], sv, 0, 0, 0);
       if (kk + kKR < kKS) ka[kk % kKR] = kread(kk + kKR);
+    }
+    if constexpr (kRope) {
+      // the q^R residuals against the same K operands, still in the ring (k-steps 14..17)
+      if (r == 1) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[(kKS - 4 + u) % kKR], qlo[u], sv, 0, 0, 0);
+      }
     }
     // exchange with the partner wave (w ^ 1): same lane = same head and tokens
 #pragma unroll
@@ -570,12 +589,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_pair_kernel(DecodeA
     const uint16_t* qp = a.q + ((long long)b * a.Nh + hc) * DQ;
     for (int d = lane; d < DQ; d += 64) {
       float v = bf16_to_f32(qp[d]);
-      if (a.rope_theta > 0 && d >= DV) {  // the same decoupled RoPE as the main path, rounded to bf16
+      if (a.rope_theta > 0 && d >= DV) {  // the decoupled RoPE of the main path, kept in fp32 here
         const int i = (d - DV) & 31;
         double sn, cs;
         sincos((double)(ctx - 1) * exp2(k2 * (double)i), &sn, &cs);
         const double x = bf16_to_f32(qp[DV + i]), y = bf16_to_f32(qp[DV + 32 + i]);
-        v = bf16_to_f32(f32_to_bf16((float)(d < DV + 32 ? x * cs - y * sn : x * sn + y * cs)));
+        v = (float)(d < DV + 32 ? x * cs - y * sn : x * sn + y * cs);
       }
       qs[d] = v;
     }
@@ -639,7 +658,10 @@ hipError_t launch(const DecodeArgs& a, hipStream_t st) {
   const long long pairs = (long long)a.B * a.nsplit;
   const long long n_wg = ((pairs + 7) / 8) * 8 * n_hg;
   if (n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  decode_mla_pair_kernel<<<dim3((unsigned)n_wg), dim3(kWaves * 64), 0, st>>>(a);
+  if (a.rope_theta > 0)
+    decode_mla_pair_kernel<true><<<dim3((unsigned)n_wg), dim3(kWaves * 64), 0, st>>>(a);
+  else
+    decode_mla_pair_kernel<false><<<dim3((unsigned)n_wg), dim3(kWaves * 64), 0, st>>>(a);
   return hipGetLastError();
 }
 }  // namespace pair
@@ -650,7 +672,10 @@ hipError_t launch_nw(const DecodeArgs& a, hipStream_t st) {
   const long long pairs = (long long)a.B * a.nsplit;
   const long long n_wg = ((pairs + 7) / 8) * 8 * n_hg;
   if (n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  decode_mla_kernel<NW><<<dim3((unsigned)n_wg), dim3(NW * 64), 0, st>>>(a);
+  if (a.rope_theta > 0)
+    decode_mla_kernel<NW, true><<<dim3((unsigned)n_wg), dim3(NW * 64), 0, st>>>(a);
+  else
+    decode_mla_kernel<NW, false><<<dim3((unsigned)n_wg), dim3(NW * 64), 0, st>>>(a);
   return hipGetLastError();
 }
 }  // namespace

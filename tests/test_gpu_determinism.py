@@ -56,3 +56,26 @@ def test_mla_decode_repeatable():
     kc = to_dev(synth.normal(720, 1, (B, T, 1, 576), "bf16"), "bf16")
     outs = [_bits(attn.decode(q, kc, kc[..., :512], ctx, scale=192 ** -0.5)) for _ in range(REPEATS)]
     assert _same_bits(outs)
+
+
+def test_mla_prefill_repeatable():
+    import causal_head_attention_gqa_amd as attn
+    B, S, Nh, Nkv = 2, 300, 8, 4
+    q = to_dev(synth.normal(730, 0, (B, S, Nh, 192), "bf16"), "bf16")
+    k = to_dev(synth.normal(730, 1, (B, S, Nkv, 192), "bf16"), "bf16")
+    v = to_dev(synth.normal(730, 2, (B, S, Nkv, 128), "bf16"), "bf16")
+    outs = [_bits(attn.prefill_mla(q, k, v, rope_theta=1e4)) for _ in range(REPEATS)]
+    assert _same_bits(outs)
+
+
+def test_chunked_prefill_repeatable():
+    import causal_head_attention_gqa_amd as attn
+    torch = __import__("torch")
+    B, S, Nh, Nkv, D, T = 2, 96, 8, 2, 128, 400
+    starts = torch.as_tensor(np.array([0, 250], np.int32), device="cuda")
+    q = to_dev(synth.normal(740, 0, (B, S, Nh, D), "bf16"), "bf16")
+    kc = to_dev(synth.normal(740, 1, (B, T, Nkv, D), "bf16"), "bf16")
+    vc = to_dev(synth.normal(740, 2, (B, T, Nkv, D), "bf16"), "bf16")
+    outs = [_bits(attn.prefill_cached(q, kc, vc, starts, rope_theta=5e5, window=120, sinks=4))
+            for _ in range(REPEATS)]
+    assert _same_bits(outs)

@@ -82,6 +82,18 @@ def test_softmax_closed_form_two_entries():
                                    rtol=1e-14, atol=1e-300)
 
 
+def test_softmax_survives_large_scores():
+    """The softmax of "Transformer 架构快速入门" §4.4 is exp(s_j) / sum_k exp(s_k) for any scores; it
+    is invariant to a common shift, so two keys whose scores differ by ln 2 get weights 2/3 and
+    1/3 whether the scores sit near +1000 or -1000 (where exp alone overflows or underflows)."""
+    for base in (1000.0, -1000.0, 0.0):
+        s = np.array([[base, base - math.log(2.0)]])
+        np.testing.assert_allclose(oracle.softmax_rows(s), [[2.0 / 3.0, 1.0 / 3.0]], rtol=1e-12)
+    q = np.array([[40.0]])
+    k = np.array([[50.0], [50.0 - math.log(2.0) / 40.0]])
+    np.testing.assert_allclose(oracle.attention_weights(q, k, 1.0), [[2.0 / 3.0, 1.0 / 3.0]], rtol=1e-9)
+
+
 def test_scale_divides_by_head_dim():
     """"Transformer 架构快速入门" §4.3: scores are divided by sqrt(D_h), per head dim.
 
