@@ -9,6 +9,8 @@ from .lib import (  # noqa: F401
     ATTN_F32,
     AttnError,
     decode,
+    decode_noalloc,
+    decode_noalloc_max_bytes,
     decode_workspace_bytes,
     kv_append,
     load,

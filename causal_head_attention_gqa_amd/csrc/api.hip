@@ -3,6 +3,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "attn.h"
 #include "kernels.hpp"
@@ -57,6 +58,35 @@ DecodePlan decode_plan(int B, int Nh, int Nkv, int Dqk, int Dv, int max_ctx) {
 }
 
 hipError_t g_last_hip = hipSuccess;
+
+// Scratch of attn_decode_noalloc: the split-KV partials live in this file-scope device array
+// instead of a caller workspace. Every GPU the library runs on holds its own copy from the
+// first use until the process ends. On the host, `scratch` names a host-side stand-in, not device
+// memory: host code uses only the per-device address that hipGetSymbolAddress returns.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+__device__ __align__(256) static unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per device.
+hipError_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 int hip_status(hipError_t e) {
   if (e == hipSuccess) return ATTN_OK;
@@ -366,6 +396,25 @@ int attn_decode(const void* q, const void* kcache, const void* vcache, const int
   if (e != hipSuccess) return hip_status(e);
   if (mla && p.nsplit == 1) return ATTN_OK;  // a single chunk already wrote the output
   return hip_status(launch_decode_reduce(a, st));
+}
+
+size_t attn_decode_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int attn_decode_noalloc(const void* q, const void* kcache, const void* vcache, const int32_t* ctx_lens, void* out,
+                        int B, int Nh, int Nkv, int Dqk, int Dv, int max_ctx, long long ldk, long long ldv,
+                        float rope_theta, float scale, int dtype, void* stream) {
+  // the split partials must fit the static scratch; anything else is validated by attn_decode
+  const size_t need = attn_decode_workspace_bytes(B, Nh, Nkv, Dqk, Dv, max_ctx, dtype);
+  if (need > kScratchBytes) return ATTN_ERR_WORKSPACE;
+  if (B <= 0) {  // nothing to launch: attn_decode validates and returns without touching the scratch
+    return attn_decode(q, kcache, vcache, ctx_lens, out, B, Nh, Nkv, Dqk, Dv, max_ctx, ldk, ldv, rope_theta, scale,
+                       dtype, nullptr, 0, stream);
+  }
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return hip_status(e);
+  return attn_decode(q, kcache, vcache, ctx_lens, out, B, Nh, Nkv, Dqk, Dv, max_ctx, ldk, ldv, rope_theta, scale,
+                     dtype, ws, kScratchBytes, stream);
 }
 
 int rope_apply(void* x, const int32_t* positions, int B, int S, int N, int Dh, float theta, int interleaved,

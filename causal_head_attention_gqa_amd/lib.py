@@ -28,6 +28,8 @@ EXPORTS = (
     "attn_kv_append",
     "attn_prefill_mla_workspace_bytes",
     "attn_prefill_mla",
+    "attn_decode_noalloc_max_bytes",
+    "attn_decode_noalloc",
 )
 
 _lib = None
@@ -76,6 +78,11 @@ def load() -> ctypes.CDLL:
     lib.attn_prefill_mla.restype = c_int
     lib.attn_prefill_mla.argtypes = [c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_float, c_int, c_float,
                                      c_vp, c_size, c_vp]
+    lib.attn_decode_noalloc_max_bytes.restype = c_size
+    lib.attn_decode_noalloc_max_bytes.argtypes = []
+    lib.attn_decode_noalloc.restype = c_int
+    lib.attn_decode_noalloc.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_int, c_ll,
+                                        c_ll, c_float, c_float, c_int, c_vp]
     _lib = lib
     return lib
 
@@ -237,6 +244,39 @@ def decode(q, kcache, vcache, ctx_lens, *, scale: float | None = None, rope_thet
                             float(scale or 0.0), dt, ws_ptr, ws_len, _stream_ptr(q.device))
     _check(st, "attn_decode")
     return out
+
+
+def decode_noalloc(q, kcache, vcache, ctx_lens, *, scale: float | None = None, rope_theta: float = 0.0, out):
+    """attn_decode without a workspace (the library's static per-GPU scratch holds the split
+    partials): for callers that cannot allocate, such as code under graph capture. `out` must be
+    given ([B, Nh, Dv], the dtype of q); arguments are those of decode(). Calls that overlap in
+    time on one GPU race on the scratch."""
+    _need_cuda(q, ctx_lens)
+    for t in (kcache, vcache):
+        if not t.is_cuda:
+            raise ValueError("caches must live on the GPU")
+        B_, T_, N_, D_ = t.shape
+        if t.stride(3) != 1 or t.stride(1) != N_ * t.stride(2) or t.stride(0) != T_ * t.stride(1):
+            raise ValueError("cache must be [B, max_ctx, Nkv, row] with a dense row pitch")
+    B, Nh, Dqk = q.shape
+    _, max_ctx, Nkv, Dk = kcache.shape
+    Dv = vcache.shape[3]
+    if Dk != Dqk or vcache.shape[:3] != kcache.shape[:3]:
+        raise ValueError("cache shapes disagree with q")
+    if ctx_lens.dtype != _torch().int32 or ctx_lens.shape != (B,):
+        raise ValueError("ctx_lens must be int32 [B]")
+    if kcache.dtype != q.dtype or vcache.dtype != q.dtype:
+        raise TypeError("q and the caches must share one dtype")
+    _check_out(out, (B, Nh, Dv), q.dtype, q.device)
+    st = load().attn_decode_noalloc(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), ctx_lens.data_ptr(),
+                                    out.data_ptr(), B, Nh, Nkv, Dqk, Dv, max_ctx, kcache.stride(2), vcache.stride(2),
+                                    float(rope_theta), float(scale or 0.0), _dtype_code(q), _stream_ptr(q.device))
+    _check(st, "attn_decode_noalloc")
+    return out
+
+
+def decode_noalloc_max_bytes() -> int:
+    return int(load().attn_decode_noalloc_max_bytes())
 
 
 def rope_apply_(x, *, theta: float, positions=None, interleaved: bool = False):

@@ -193,6 +193,29 @@ int attn_decode(const void* q, const void* kcache, const void* vcache, const int
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------
+ * KV-cache decode that allocates nothing, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Arguments, layouts, supported shapes and results are those of attn_decode, which it calls
+ * (same kernels, same bits); only the workspace is gone. The split-KV partials go to a static
+ * device buffer of attn_decode_noalloc_max_bytes() bytes (64 MiB) inside the library, one per GPU,
+ * held from its first use on that GPU until the process ends. No hipMalloc, hipFree or other
+ * allocating call is made.
+ * Errors: ATTN_ERR_WORKSPACE when attn_decode_workspace_bytes(...) of the call exceeds that size
+ *          (nothing is launched); otherwise as attn_decode.
+ * Concurrency: every call on one GPU uses that GPU's one buffer. Calls that overlap in time on
+ *          one GPU (different streams, or host threads without ordering) race and give wrong
+ *          results; calls ordered on one stream are safe. The buffer keeps the last call's
+ *          partials; nothing in it needs clearing (each call writes every partial it reads).
+ * ------------------------------------------------------------------------------------------ */
+size_t attn_decode_noalloc_max_bytes(void);
+
+int attn_decode_noalloc(const void* q, const void* kcache, const void* vcache, const int32_t* ctx_lens,
+                        void* out, int B, int Nh, int Nkv, int Dqk, int Dv, int max_ctx,
+                        long long ldk, long long ldv, float rope_theta, float scale, int dtype,
+                        void* stream);
+
+/* ------------------------------------------------------------------------------------------
  * RoPE, in place: rotate every head vector of x [B, S, N, Dh] by its position.
  *   "2.7 ..." §4 (half-split pairs), "Transformer 架构快速入门" §8.2-8.3 (frequencies, adjacent
  *   pairs), "Transformer 架构完全深度解析" §七.
