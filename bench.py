@@ -10,6 +10,10 @@ One step = one pass of every kernel of the path over synthetic inputs:
 Prefill is priced in algorithmic TFLOP/s (4*Dh FLOPs per unmasked (query, key) pair) against the
 dense bf16 matrix peak; decode in algorithmic GB/s (each needed cache row once, plus q and out)
 against HBM peak. The headline value is the mean of the two fractions, in percent.
+The decode parts rotate over replicas of their caches (2 for the GQA decode, 4 for the MLA decode),
+so each call reads rows that are not in the 256 MiB Infinity Cache. The roofline object prices the
+prefill's attention kernel alone, timed by HIP events the library records around its launch on
+the call's stream. The GPT-2-small-shaped prefill (Dh=64) is timed after the step as a component.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--only PART]
 Prints one JSON line. `--extras` instead measures the widened rows (chunked prefill with RoPE + cache
@@ -75,6 +79,10 @@ def device_normal(torch, shape, seed):
     return torch.randn(shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
 
 
+GQA_REPLICAS = 2  # 2 x 1.2 GB of touched cache rows per rotation
+MLA_REPLICAS = 4  # 4 x 151 MB = 604 MB, over twice the 256 MiB Infinity Cache
+
+
 def make_inputs(torch, attn):
     P, D, M = synth.LLAMA3_PREFILL, synth.LLAMA3_DECODE, synth.MLA_DECODE
     x = {}
@@ -85,15 +93,18 @@ def make_inputs(torch, attn):
     x["pws"] = torch.empty(max(1, attn.prefill_workspace_bytes(P.B, P.S, P.Nkv, P.Dh, P.rope_theta, attn.ATTN_BF16)),
                            dtype=torch.uint8, device="cuda")
     x["dq"] = device_normal(torch, (D.B, D.Nh, D.Dqk), 1000 * D.wid + 0)
-    x["dk"] = device_normal(torch, (D.B, D.max_ctx, D.Nkv, D.Dqk), 1000 * D.wid + 1)
-    x["dv"] = device_normal(torch, (D.B, D.max_ctx, D.Nkv, D.Dv), 1000 * D.wid + 2)
+    x["dk"] = [device_normal(torch, (D.B, D.max_ctx, D.Nkv, D.Dqk), 1000 * D.wid + 1 + 10 * r)
+               for r in range(GQA_REPLICAS)]
+    x["dv"] = [device_normal(torch, (D.B, D.max_ctx, D.Nkv, D.Dv), 1000 * D.wid + 2 + 10 * r)
+               for r in range(GQA_REPLICAS)]
     x["dctx_np"] = D.ctx_lens()
     x["dctx"] = torch.as_tensor(x["dctx_np"], device="cuda")
     x["dout"] = torch.empty((D.B, D.Nh, D.Dv), dtype=torch.bfloat16, device="cuda")
     x["dws"] = torch.empty(attn.decode_workspace_bytes(D.B, D.Nh, D.Nkv, D.Dqk, D.Dv, D.max_ctx, attn.ATTN_BF16),
                            dtype=torch.uint8, device="cuda")
     x["mq"] = device_normal(torch, (M.B, M.Nh, M.Dqk), 1000 * M.wid + 0)
-    x["mkv"] = device_normal(torch, (M.B, M.max_ctx, 1, M.Dqk), 1000 * M.wid + 1)
+    x["mkv"] = [device_normal(torch, (M.B, M.max_ctx, 1, M.Dqk), 1000 * M.wid + 1 + 10 * r)
+                for r in range(MLA_REPLICAS)]
     x["mctx_np"] = M.ctx_lens()
     x["mctx"] = torch.as_tensor(x["mctx_np"], device="cuda")
     x["mout"] = torch.empty((M.B, M.Nh, M.Dv), dtype=torch.bfloat16, device="cuda")
@@ -151,7 +162,9 @@ def cpu_baseline():
     return {
         "value": 100.0 * frac, "unit": "% of peak", "cores": int(threads), "kind": "oracle",
         "sample": (f"fp64 numpy oracle on the host: every row of query heads 0-7 of sequence 0 of the Llama-3-8B "
-                   f"prefill ({tp:.1f} s, {p_tflops * 1e3:.2f} GFLOP/s algorithmic); all 64 sequences of the "
+                   f"prefill ({tp:.1f} s, {p_tflops * 1e3:.2f} GFLOP/s algorithmic; the oracle materialises the "
+                   f"full 8192x8192 score matrix, i.e. does twice the causal FLOPs it is credited with); all 64 "
+                   f"sequences of the "
                    f"GQA decode ({td:.1f} s) and all 32 of the MLA decode ({tm:.1f} s): {d_gbs:.3f} GB/s "
                    f"algorithmic; {threads} BLAS threads; host {platform.machine()}, {os.cpu_count()} logical CPUs"),
         "prefill_tflops": p_tflops, "decode_gbs": d_gbs,
@@ -223,9 +236,9 @@ def run_extras(torch, attn, steps: int, warmup: int):
     workload = f"Llama-3-8B GQA prefill B{B} S{S} Nh{Nh} Nkv{Nkv} Dh{Dh} RoPE{theta:g}"
     lines = []
 
-    def emit(name, ms, work, unit, peak, extra):
+    def emit(name, ms, work, unit, peak, extra, wl=None):
         rate = work / (ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
-        lines.append({"extra": name, "workload": workload, **extra, "ms": ms, "achieved": rate, "unit": unit,
+        lines.append({"extra": name, "workload": wl or workload, **extra, "ms": ms, "achieved": rate, "unit": unit,
                       "peak": peak, "frac": rate / peak})
 
     # whole-sequence prefill, as the reference point of the rows below
@@ -268,6 +281,20 @@ def run_extras(torch, attn, steps: int, warmup: int):
                                               out=out, workspace=ws))
     emit("sliding_window", ms_w, 4 * Dh * B * Nh * pairs, "TFLOP/s", acc.PEAK_BF16_TFLOPS,
          {"window": W, "sinks": sinks, "visible_pairs_per_head": pairs})
+    del q, k, v, qc, kc_, vc_, kcache, vcache, out, outc, pws
+
+    # MLA's non-absorbed prefill, DeepSeek-V3 shape: 128 heads, q/k 192 = 128 + 64 decoupled RoPE dims, v 128
+    Mp = synth.MLA_PREFILL
+    mq = device_normal(torch, (Mp.B, Mp.S, Mp.Nh, Mp.Dh), 1000 * Mp.wid + 0)
+    mk = device_normal(torch, (Mp.B, Mp.S, Mp.Nkv, Mp.Dh), 1000 * Mp.wid + 1)
+    mv = device_normal(torch, (Mp.B, Mp.S, Mp.Nkv, Mp.dv), 1000 * Mp.wid + 2)
+    mo = torch.empty((Mp.B, Mp.S, Mp.Nh, Mp.dv), dtype=torch.bfloat16, device="cuda")
+    mws = torch.empty(max(1, attn.prefill_mla_workspace_bytes(Mp.B, Mp.S, Mp.Nkv, Mp.rope_theta)), dtype=torch.uint8,
+                      device="cuda")
+    ms_m = timed(lambda: attn.prefill_mla(mq, mk, mv, rope_theta=Mp.rope_theta, out=mo, workspace=mws))
+    emit("mla_prefill", ms_m, acc.prefill_flops(Mp.B, Mp.S, Mp.Nh, Mp.Dh, causal=True, Dv=Mp.dv), "TFLOP/s",
+         acc.PEAK_BF16_TFLOPS, {"flop_per_pair": 2 * (Mp.Dh + Mp.dv), "includes": "k^R rotation pass"},
+         wl=f"DeepSeek-V3 MLA non-absorbed prefill B{Mp.B} S{Mp.S} Nh{Mp.Nh} q/k {Mp.Dh} v {Mp.dv} RoPE{Mp.rope_theta:g}")
     for ln in lines:
         print(json.dumps(ln))
 
@@ -290,15 +317,20 @@ def main():
     import causal_head_attention_gqa_amd as attn
     P, D, M = synth.LLAMA3_PREFILL, synth.LLAMA3_DECODE, synth.MLA_DECODE
     x = make_inputs(torch, attn)
+    calls = {"decode": 0, "mla": 0}
 
     def run_prefill():
         attn.prefill(x["pq"], x["pk"], x["pv"], rope_theta=P.rope_theta, out=x["pout"], workspace=x["pws"])
 
     def run_decode():
-        attn.decode(x["dq"], x["dk"], x["dv"], x["dctx"], out=x["dout"], workspace=x["dws"])
+        r = calls["decode"] % GQA_REPLICAS
+        calls["decode"] += 1
+        attn.decode(x["dq"], x["dk"][r], x["dv"][r], x["dctx"], out=x["dout"], workspace=x["dws"])
 
     def run_mla():
-        attn.decode(x["mq"], x["mkv"], x["mkv"][..., :M.Dv], x["mctx"], scale=M.scale, out=x["mout"],
+        r = calls["mla"] % MLA_REPLICAS
+        calls["mla"] += 1
+        attn.decode(x["mq"], x["mkv"][r], x["mkv"][r][..., :M.Dv], x["mctx"], scale=M.scale, out=x["mout"],
                     workspace=x["mws"])
 
     parts = [("prefill", run_prefill), ("decode", run_decode), ("mla", run_mla)]
@@ -306,17 +338,27 @@ def main():
         parts = [p for p in parts if p[0] == args.only]
     stream = torch.cuda.current_stream()
 
+    def new_events():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(4)]  # call start/end, kernel start/end
+
     def step(evs=None):
         for i, (_, fn) in enumerate(parts):
-            if evs is not None:
-                evs[i][0].record(stream)
-            fn()
-            if evs is not None:
-                evs[i][1].record(stream)
+            if evs is None:
+                fn()
+                continue
+            c0, c1, k0, k1 = evs[i]
+            c0.record(stream)
+            with attn.kernel_events(k0, k1):
+                fn()
+            c1.record(stream)
 
     for _ in range(args.warmup):
         step()
-    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in parts] for _ in range(args.steps)]
+    events = [[new_events() for _ in parts] for _ in range(args.steps)]
+    for per_step in events:  # create the HIP events before the timed region
+        for evs in per_step:
+            for e in evs:
+                e.record(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -325,6 +367,8 @@ def main():
     wall = time.perf_counter() - t0
     ms = {name: float(np.mean([events[s][i][0].elapsed_time(events[s][i][1]) for s in range(args.steps)]))
           for i, (name, _) in enumerate(parts)}
+    kms = {name: float(np.mean([events[s][i][2].elapsed_time(events[s][i][3]) for s in range(args.steps)]))
+           for i, (name, _) in enumerate(parts)}
 
     p_flops = acc.prefill_flops(P.B, P.S, P.Nh, P.Dh, causal=True)
     d_bytes = acc.decode_bytes(x["dctx_np"], D.B, D.Nh, D.Nkv, D.Dqk, D.Dv, 2)
@@ -333,13 +377,17 @@ def main():
     if "prefill" in ms:
         comp["prefill_tflops"] = p_flops / (ms["prefill"] * 1e-3) / 1e12
         comp["prefill_ms"] = ms["prefill"]
+        comp["prefill_kernel_ms"] = kms["prefill"]
+        comp["prefill_kernel_tflops"] = p_flops / (kms["prefill"] * 1e-3) / 1e12
     if "decode" in ms:
         comp["gqa_decode_gbs"] = d_bytes / (ms["decode"] * 1e-3) / 1e9
         comp["gqa_decode_ms"] = ms["decode"]
+        comp["gqa_split_kernel_ms"] = kms["decode"]
     if "mla" in ms:
         comp["mla_decode_gbs"] = m_bytes / (ms["mla"] * 1e-3) / 1e9
         comp["mla_decode_tflops"] = acc.decode_flops(x["mctx_np"], M.Nh, M.Dqk, M.Dv) / (ms["mla"] * 1e-3) / 1e12
         comp["mla_decode_ms"] = ms["mla"]
+        comp["mla_split_kernel_ms"] = kms["mla"]
     dec_ms = ms.get("decode", 0.0) + ms.get("mla", 0.0)
     dec_bytes = (d_bytes if "decode" in ms else 0) + (m_bytes if "mla" in ms else 0)
     fracs = []
@@ -349,17 +397,46 @@ def main():
         comp["decode_gbs"] = dec_bytes / (dec_ms * 1e-3) / 1e9
         fracs.append(comp["decode_gbs"] / acc.PEAK_HBM_GBS)
     value = 100.0 * float(np.mean(fracs))
+    comp["decode_cache_replicas"] = {"gqa": GQA_REPLICAS, "mla": MLA_REPLICAS}
 
     if "prefill" in ms:
-        roofline = {"kernel": "prefill_bf16_kernel (Llama-3-8B GQA prefill, one call incl. RoPE pre-pass)",
-                    "bound": "mfma", "achieved": comp["prefill_tflops"], "peak": acc.PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": comp["prefill_tflops"] / acc.PEAK_BF16_TFLOPS,
-                    "traffic": prefill_traffic()}
+        # GPT-2-small-shaped prefill (B=8, S=1024, 12 heads of 64, no RoPE): 200 back-to-back calls,
+        # kernel events around each, after the step's timed region
+        G = synth.GPT2_PREFILL
+        gq = device_normal(torch, (G.B, G.S, G.Nh, G.Dh), 1000 * G.wid + 0)
+        gk = device_normal(torch, (G.B, G.S, G.Nkv, G.Dh), 1000 * G.wid + 1)
+        gv = device_normal(torch, (G.B, G.S, G.Nkv, G.Dh), 1000 * G.wid + 2)
+        gout = torch.empty_like(gq)
+        for _ in range(5):
+            attn.prefill(gq, gk, gv, out=gout)
+        gev = [new_events()[:2] for _ in range(200)]
+        for a_, b_ in gev:
+            a_.record(stream)
+            b_.record(stream)
+        torch.cuda.synchronize()
+        for k0, k1 in gev:
+            with attn.kernel_events(k0, k1):
+                attn.prefill(gq, gk, gv, out=gout)
+        torch.cuda.synchronize()
+        g_ms = float(np.median([a_.elapsed_time(b_) for a_, b_ in gev]))
+        g_flops = acc.prefill_flops(G.B, G.S, G.Nh, G.Dh, causal=True)
+        comp["gpt2_prefill_kernel_ms"] = g_ms
+        comp["gpt2_prefill_tflops"] = g_flops / (g_ms * 1e-3) / 1e12
+        comp["gpt2_prefill_frac"] = comp["gpt2_prefill_tflops"] / acc.PEAK_BF16_TFLOPS
+
+    if "prefill" in ms:
+        roofline = {"kernel": "prefill_bf16_kernel<128,128,4,false,false> (Llama-3-8B GQA prefill; kernel alone, "
+                              "HIP events around its launch)",
+                    "bound": "mfma", "achieved": comp["prefill_kernel_tflops"], "peak": acc.PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": comp["prefill_kernel_tflops"] / acc.PEAK_BF16_TFLOPS,
+                    "flops_per_launch": p_flops, "kernel_ms": kms["prefill"], "traffic": prefill_traffic()}
     else:
         name = args.only
-        gbs = comp["gqa_decode_gbs"] if name == "decode" else comp["mla_decode_gbs"]
-        roofline = {"kernel": f"{name} decode", "bound": "hbm", "achieved": gbs, "peak": acc.PEAK_HBM_GBS,
-                    "unit": "GB/s", "frac": gbs / acc.PEAK_HBM_GBS, "traffic": None}
+        b = d_bytes if name == "decode" else m_bytes
+        gbs = b / (kms[name] * 1e-3) / 1e9
+        roofline = {"kernel": f"{name} decode split kernel (HIP events around its launch)", "bound": "hbm",
+                    "achieved": gbs, "peak": acc.PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / acc.PEAK_HBM_GBS,
+                    "kernel_ms": kms[name], "traffic": None}
 
     line = {
         "metric": METRIC, "value": value, "unit": "% of peak", "n_gpus": 1, "steps": args.steps,

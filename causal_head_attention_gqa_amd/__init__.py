@@ -12,6 +12,7 @@ from .lib import (  # noqa: F401
     decode_noalloc,
     decode_noalloc_max_bytes,
     decode_workspace_bytes,
+    kernel_events,
     kv_append,
     load,
     prefill,

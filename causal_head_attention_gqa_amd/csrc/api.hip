@@ -94,6 +94,23 @@ int hip_status(hipError_t e) {
   return ATTN_ERR_HIP;
 }
 
+// Profiling hook (attn_set_kernel_events): events recorded right before and right after the main
+// attention kernel of each call made by this host thread.
+thread_local hipEvent_t t_ev_before = nullptr;
+thread_local hipEvent_t t_ev_after = nullptr;
+
+// Launches `fn` on st between the caller's profiling events, when set.
+template <typename F>
+hipError_t timed_launch(hipStream_t st, F&& fn) {
+  if (t_ev_before) {
+    const hipError_t e = hipEventRecord(t_ev_before, st);
+    if (e != hipSuccess) return e;
+  }
+  const hipError_t e = fn();
+  if (e != hipSuccess || !t_ev_after) return e;
+  return hipEventRecord(t_ev_after, st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -188,8 +205,8 @@ int attn_prefill(const void* q, const void* k, const void* v, void* out, int B, 
     a.table = table;
     a.k = krot;
   }
-  const hipError_t e = dtype == ATTN_BF16 ? launch_prefill_bf16(a, st) : launch_prefill_f32(a, st);
-  return hip_status(e);
+  return hip_status(timed_launch(st, [&] { return dtype == ATTN_BF16 ? launch_prefill_bf16(a, st)
+                                                                     : launch_prefill_f32(a, st); }));
 }
 
 size_t attn_prefill_mla_workspace_bytes(int B, int S, int Nkv, float rope_theta) {
@@ -249,7 +266,7 @@ int attn_prefill_mla(const void* q, const void* k, const void* v, void* out, int
     a.table = table;
     a.k = krot;
   }
-  return hip_status(launch_prefill_bf16(a, st));
+  return hip_status(timed_launch(st, [&] { return launch_prefill_bf16(a, st); }));
 }
 
 size_t attn_prefill_cached_workspace_bytes(int max_ctx, int Dh, float rope_theta) {
@@ -313,7 +330,7 @@ int attn_prefill_cached(const void* q, const void* kcache, const void* vcache, c
     if (e != hipSuccess) return hip_status(e);
     a.table = table;
   }
-  return hip_status(launch_prefill_bf16(a, st));
+  return hip_status(timed_launch(st, [&] { return launch_prefill_bf16(a, st); }));
 }
 
 int attn_kv_append(const void* k_new, const void* v_new, void* kcache, void* vcache, const int32_t* start, int B,
@@ -392,13 +409,20 @@ int attn_decode(const void* q, const void* kcache, const void* vcache, const int
   a.nsplit = p.nsplit;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = mla ? launch_decode_mla(a, st) : launch_decode_gqa(a, st);
+  hipError_t e = timed_launch(st, [&] { return mla ? launch_decode_mla(a, st) : launch_decode_gqa(a, st); });
   if (e != hipSuccess) return hip_status(e);
   if (mla && p.nsplit == 1) return ATTN_OK;  // a single chunk already wrote the output
   return hip_status(launch_decode_reduce(a, st));
 }
 
 size_t attn_decode_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int attn_set_kernel_events(void* before, void* after) {
+  if ((before == nullptr) != (after == nullptr)) return ATTN_ERR_INVALID;
+  t_ev_before = static_cast<hipEvent_t>(before);
+  t_ev_after = static_cast<hipEvent_t>(after);
+  return ATTN_OK;
+}
 
 int attn_decode_noalloc(const void* q, const void* kcache, const void* vcache, const int32_t* ctx_lens, void* out,
                         int B, int Nh, int Nkv, int Dqk, int Dv, int max_ctx, long long ldk, long long ldv,

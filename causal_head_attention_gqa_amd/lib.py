@@ -30,6 +30,7 @@ EXPORTS = (
     "attn_prefill_mla",
     "attn_decode_noalloc_max_bytes",
     "attn_decode_noalloc",
+    "attn_set_kernel_events",
 )
 
 _lib = None
@@ -83,6 +84,8 @@ def load() -> ctypes.CDLL:
     lib.attn_decode_noalloc.restype = c_int
     lib.attn_decode_noalloc.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_int, c_int, c_int, c_int, c_int, c_int, c_ll,
                                         c_ll, c_float, c_float, c_int, c_vp]
+    lib.attn_set_kernel_events.restype = c_int
+    lib.attn_set_kernel_events.argtypes = [c_vp, c_vp]
     _lib = lib
     return lib
 
@@ -277,6 +280,28 @@ def decode_noalloc(q, kcache, vcache, ctx_lens, *, scale: float | None = None, r
 
 def decode_noalloc_max_bytes() -> int:
     return int(load().attn_decode_noalloc_max_bytes())
+
+
+class kernel_events:
+    """Context manager: calls made inside it by this thread record (before, after) - two
+    torch.cuda.Event(enable_timing=True) - around their main attention kernel, so that
+    before.elapsed_time(after) is that kernel's duration alone."""
+
+    def __init__(self, before, after):
+        self.before, self.after = before, after
+
+    def __enter__(self):
+        torch = _torch()
+        for ev in (self.before, self.after):
+            if not ev.cuda_event:  # torch creates the HIP event at its first record
+                ev.record(torch.cuda.current_stream())
+        _check(load().attn_set_kernel_events(self.before.cuda_event, self.after.cuda_event),
+               "attn_set_kernel_events")
+        return self
+
+    def __exit__(self, *exc):
+        load().attn_set_kernel_events(None, None)
+        return False
 
 
 def rope_apply_(x, *, theta: float, positions=None, interleaved: bool = False):

@@ -227,6 +227,20 @@ int attn_decode_noalloc(const void* q, const void* kcache, const void* vcache, c
 int rope_apply(void* x, const int32_t* positions, int B, int S, int N, int Dh,
                float theta, int interleaved, int dtype, void* stream);
 
+/* ------------------------------------------------------------------------------------------
+ * Profiling: time the main kernel of a call apart from its helper launches (the RoPE table and
+ * key rotation of attn_prefill, the span pass of attn_prefill_mla, the split reduction of
+ * attn_decode). After attn_set_kernel_events(before, after), every attn_prefill,
+ * attn_prefill_cached, attn_prefill_mla and attn_decode call made by the SAME host thread records
+ * the HIP event `before` on its stream right before the attention kernel's launch and `after`
+ * right after it (the decode's split kernel); hipEventElapsedTime(before, after) is then that
+ * kernel's duration. The events are owned by the caller (hipEvent_t, created with timing
+ * enabled). attn_set_kernel_events(NULL, NULL) stops the recording.
+ * Errors: ATTN_ERR_INVALID if exactly one of the two is NULL; a failed record makes the call
+ *          return ATTN_ERR_HIP.
+ * ------------------------------------------------------------------------------------------ */
+int attn_set_kernel_events(void* before, void* after);
+
 #ifdef __cplusplus
 }
 #endif
