@@ -338,27 +338,30 @@ def main():
         parts = [p for p in parts if p[0] == args.only]
     stream = torch.cuda.current_stream()
 
-    def new_events():
-        return [torch.cuda.Event(enable_timing=True) for _ in range(4)]  # call start/end, kernel start/end
+    def new_events(n=2):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in evs:  # create the HIP events before any timed region
+            e.record(stream)
+        return evs
 
-    def step(evs=None):
+    def step(evs=None, kernel=False):
+        """One pass of every part. evs[i] = (start, end): around part i's whole call, or with
+        kernel=True around its main kernel alone (recorded by the library at the launch)."""
         for i, (_, fn) in enumerate(parts):
             if evs is None:
                 fn()
-                continue
-            c0, c1, k0, k1 = evs[i]
-            c0.record(stream)
-            with attn.kernel_events(k0, k1):
+            elif kernel:
+                with attn.kernel_events(*evs[i]):
+                    fn()
+            else:
+                evs[i][0].record(stream)
                 fn()
-            c1.record(stream)
+                evs[i][1].record(stream)
 
     for _ in range(args.warmup):
         step()
+    # the timed steps: one event pair around each part's call, nothing else added to the stream
     events = [[new_events() for _ in parts] for _ in range(args.steps)]
-    for per_step in events:  # create the HIP events before the timed region
-        for evs in per_step:
-            for e in evs:
-                e.record(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -367,7 +370,13 @@ def main():
     wall = time.perf_counter() - t0
     ms = {name: float(np.mean([events[s][i][0].elapsed_time(events[s][i][1]) for s in range(args.steps)]))
           for i, (name, _) in enumerate(parts)}
-    kms = {name: float(np.mean([events[s][i][2].elapsed_time(events[s][i][3]) for s in range(args.steps)]))
+    # the same steps again, with the event pairs around each part's main kernel alone (roofline)
+    kevents = [[new_events() for _ in parts] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for s in range(args.steps):
+        step(kevents[s], kernel=True)
+    torch.cuda.synchronize()
+    kms = {name: float(np.mean([kevents[s][i][0].elapsed_time(kevents[s][i][1]) for s in range(args.steps)]))
            for i, (name, _) in enumerate(parts)}
 
     p_flops = acc.prefill_flops(P.B, P.S, P.Nh, P.Dh, causal=True)
@@ -409,10 +418,7 @@ def main():
         gout = torch.empty_like(gq)
         for _ in range(5):
             attn.prefill(gq, gk, gv, out=gout)
-        gev = [new_events()[:2] for _ in range(200)]
-        for a_, b_ in gev:
-            a_.record(stream)
-            b_.record(stream)
+        gev = [new_events() for _ in range(200)]
         torch.cuda.synchronize()
         for k0, k1 in gev:
             with attn.kernel_events(k0, k1):

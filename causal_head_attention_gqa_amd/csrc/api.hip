@@ -357,7 +357,7 @@ size_t attn_decode_workspace_bytes(int B, int Nh, int Nkv, int Dqk, int Dv, int 
   if (Nh % Nkv != 0) return 0;
   const DecodePlan p = decode_plan(B, Nh, Nkv, Dqk, Dv, max_ctx);
   const size_t slots = (size_t)B * (size_t)Nh * (size_t)p.nsplit;
-  return align_up(slots * (size_t)Dv * sizeof(float)) + align_up(slots * 2 * sizeof(float));
+  return align_up(slots * (size_t)Dv * sizeof(uint16_t)) + align_up(slots * 2 * sizeof(float));
 }
 
 int attn_decode(const void* q, const void* kcache, const void* vcache, const int32_t* ctx_lens, void* out, int B,
@@ -392,8 +392,8 @@ int attn_decode(const void* q, const void* kcache, const void* vcache, const int
   a.vc = static_cast<const uint16_t*>(vcache);
   a.ctx_lens = ctx_lens;
   a.out = static_cast<uint16_t*>(out);
-  a.part_o = static_cast<float*>(workspace);
-  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(slots * (size_t)Dv * sizeof(float)));
+  a.part_o = static_cast<uint16_t*>(workspace);
+  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(slots * (size_t)Dv * sizeof(uint16_t)));
   a.B = B;
   a.Nh = Nh;
   a.Nkv = Nkv;

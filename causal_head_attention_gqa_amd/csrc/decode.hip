@@ -13,7 +13,8 @@
 //     direct-to-LDS loads (several stages in flight per wave, no barrier while streaming);
 //   - the tiny contractions run on the matrix cores with the heads padded to 16 (q.k as
 //     16x16x32, p.v as 16x16x16 whose p operand is the score block's own register layout);
-//   - each chunk writes (max, sum, unnormalised output) in fp32; the reduction kernel merges
+//   - each chunk writes its (max, sum) in fp32 and its output normalised by that sum in bf16;
+//     the reduction kernel merges
 //     the chunks with the online-softmax algebra ("Transformer 架构完全深度解析" §十三: the
 //     running max / sum recurrences, applied to whole chunks).
 #include "kernels.hpp"
@@ -286,7 +287,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
       l = fmaf(wgt, mm(v)[hl * 2 + 1], l);
     }
     const long long slot = ((long long)b * a.Nh + h0 + hl) * a.nsplit + s;
-    a.part_o[slot * D + d] = acc;
+    a.part_o[slot * D + d] = f32_to_bf16(acc / l);  // every written chunk holds a key: l > 0
     if (d == 0) {
       a.part_ml[slot * 2 + 0] = mx;
       a.part_ml[slot * 2 + 1] = l;
@@ -295,8 +296,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 }
 
 // Merge the chunks of each (b, h): m* = max m_s, l* = sum 2^(m_s - m*) l_s,
-// out = sum 2^(m_s - m*) o_s / l*. One wave per (b, h); each lane owns float4 columns and keeps
-// the loads of several chunks in flight.
+// out = sum 2^(m_s - m*) l_s (o_s / l_s) / l* ("Transformer 架构完全深度解析" §十三: the running max
+// and sum recurrences applied to whole chunks). Each chunk left its output normalised by its own
+// sum, o_s / l_s, in bf16 (half the bytes of fp32; the merge is a convex combination of them, so
+// their rounding stays within one bf16 step of the output). One wave per (b, h); each lane owns
+// 4-column groups and keeps the loads of several chunks in flight.
 __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(DecodeArgs a) {
   const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -318,31 +322,24 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(DecodeArgs a) {
   float l = 0.f;
   for (int s = 0; s < ns; ++s) l += fast_exp2(ml[2 * s] - mx) * ml[2 * s + 1];
   const float inv = 1.f / l;
-  const float4* po = reinterpret_cast<const float4*>(a.part_o + slot0 * Dv);
+  const uint2* po = reinterpret_cast<const uint2*>(a.part_o + slot0 * Dv);
+  auto fma4 = [](float w, uint2 v, float4& acc) {
+    acc.x = fmaf(w, bf16lo(v.x), acc.x);
+    acc.y = fmaf(w, bf16hi(v.x), acc.y);
+    acc.z = fmaf(w, bf16lo(v.y), acc.z);
+    acc.w = fmaf(w, bf16hi(v.y), acc.w);
+  };
   for (int c = lane; c < nvec; c += 64) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     int s = 0;
     for (; s + 4 <= ns; s += 4) {
-      float4 v[4];
+      uint2 v[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) v[u] = po[(long long)(s + u) * nvec + c];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float wgt = fast_exp2(ml[2 * (s + u)] - mx);
-        acc.x = fmaf(wgt, v[u].x, acc.x);
-        acc.y = fmaf(wgt, v[u].y, acc.y);
-        acc.z = fmaf(wgt, v[u].z, acc.z);
-        acc.w = fmaf(wgt, v[u].w, acc.w);
-      }
+      for (int u = 0; u < 4; ++u) fma4(fast_exp2(ml[2 * (s + u)] - mx) * ml[2 * (s + u) + 1], v[u], acc);
     }
-    for (; s < ns; ++s) {
-      const float4 v = po[(long long)s * nvec + c];
-      const float wgt = fast_exp2(ml[2 * s] - mx);
-      acc.x = fmaf(wgt, v.x, acc.x);
-      acc.y = fmaf(wgt, v.y, acc.y);
-      acc.z = fmaf(wgt, v.z, acc.z);
-      acc.w = fmaf(wgt, v.w, acc.w);
-    }
+    for (; s < ns; ++s) fma4(fast_exp2(ml[2 * s] - mx) * ml[2 * s + 1], po[(long long)s * nvec + c], acc);
     *reinterpret_cast<uint2*>(op + 4 * c) =
         make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
   }

@@ -20,7 +20,8 @@
 //     read row-major), online softmax per head, then O^T[512 x 16] += V^T P^T (32 MFMAs) with the
 //     V operand read from the SAME row-major tile by the transposing LDS read (4 consecutive
 //     tokens of one dim per lane) - the row serves as K and as V without a second copy;
-//   - each chunk writes (max, sum, unnormalised output) in fp32 for the split reduction; a single
+//   - each chunk writes (max, sum) in fp32 and its output normalised by that sum in bf16 for the
+//     split reduction; a single
 //     chunk writes the normalised bf16 output directly.
 // Work-group ids are mapped so that the head groups of one (sequence, chunk) run on one XCD and
 // share its L2 when the heads do not fit one work-group.
@@ -286,10 +287,12 @@ __global__ __launch_bounds__(NW * 64, (NW >= 8 ? 2 : 1)) void decode_mla_kernel(
     return;
   }
   const long long slot = ((long long)b * a.Nh + h) * a.nsplit + s;
-  float* po = a.part_o + slot * DV + rg * 4;
+  uint16_t* po = a.part_o + slot * DV + rg * 4;
+  const float inv = 1.f / ltot;  // the chunk's output, normalised by its own sum, in bf16
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
-    *reinterpret_cast<float4*>(po + db * 16) = make_float4(o[db][0], o[db][1], o[db][2], o[db][3]);
+    *reinterpret_cast<uint2*>(po + db * 16) =
+        make_uint2(pack_bf16x2(o[db][0] * inv, o[db][1] * inv), pack_bf16x2(o[db][2] * inv, o[db][3] * inv));
   if (rg == 0) {
     a.part_ml[slot * 2 + 0] = m;
     a.part_ml[slot * 2 + 1] = ltot;
@@ -560,13 +563,15 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_pair_kernel(DecodeA
               make_uint2(pack_bf16x2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
                          pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv));
     } else {
-      float* po = a.part_o + slot * DV + r * (DV / 2) + hf * 4;
+      uint16_t* po = a.part_o + slot * DV + r * (DV / 2) + hf * 4;
+      const float inv = 1.f / ltot;  // the chunk's output, normalised by its own sum, in bf16
 #pragma unroll
       for (int db = 0; db < kDB; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g)
-          *reinterpret_cast<float4*>(po + db * 32 + g * 8) =
-              make_float4(o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]);
+          *reinterpret_cast<uint2*>(po + db * 32 + g * 8) =
+              make_uint2(pack_bf16x2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
+                         pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv));
       if (r == 0 && hf == 0) {
         a.part_ml[slot * 2 + 0] = m;
         a.part_ml[slot * 2 + 1] = ltot;
@@ -644,7 +649,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_pair_kernel(DecodeA
           make_uint2(pack_bf16x2(o4[0] * inv, o4[1] * inv), pack_bf16x2(o4[2] * inv, o4[3] * inv));
     } else {
       const long long sl = ((long long)b * a.Nh + hc) * a.nsplit + s;
-      *reinterpret_cast<float4*>(a.part_o + sl * DV + r * (DV / 2) + 4 * lane) = make_float4(o4[0], o4[1], o4[2], o4[3]);
+      const float inv = 1.f / lr;
+      *reinterpret_cast<uint2*>(a.part_o + sl * DV + r * (DV / 2) + 4 * lane) =
+          make_uint2(pack_bf16x2(o4[0] * inv, o4[1] * inv), pack_bf16x2(o4[2] * inv, o4[3] * inv));
       if (r == 0 && lane == 0) {
         a.part_ml[sl * 2 + 0] = mr;
         a.part_ml[sl * 2 + 1] = lr;

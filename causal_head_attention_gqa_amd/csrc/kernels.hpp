@@ -71,8 +71,8 @@ struct DecodeArgs {
   const uint16_t* vc;
   const int* ctx_lens;
   uint16_t* out;
-  float* part_o;   // [B][Nh][nsplit][Dv] fp32
-  float* part_ml;  // [B][Nh][nsplit][2]  fp32 (running max in log2 units, sum)
+  uint16_t* part_o;  // [B][Nh][nsplit][Dv] bf16: the chunk's output normalised by its own sum
+  float* part_ml;    // [B][Nh][nsplit][2]  fp32 (reference max in log2 units, sum)
   int B, Nh, Nkv, Dqk, Dv, max_ctx;
   long long ldk, ldv;
   float scale_log2;
