@@ -230,3 +230,55 @@ def test_prefill_cached_rope_variants_match_oracle(case):
     want = oracle.prefill_chunk(values(q, "bf16"), values(k_all, "bf16"), values(v_all, "bf16"), starts,
                                 rope_theta=theta, rope_interleaved=inter, rope_dims=rdims)
     assert max_abs(got, want) <= BF16_TOL
+
+
+def _llama3_full_size_rows(window, sinks):
+    """The Llama-3-8B-shaped prefill (B=4, S=8192, 32/8 heads of 128, RoPE 5e5) run the way the
+    benchmark's widened rows run it: the cache filled by four 2048-token appends (RoPE fused), then
+    either each chunk's queries against the cache (window 0) or all 8192 queries at once with a
+    sliding window. Returns (output rows [4, R, 32, 128], the oracle's, the rows)."""
+    import causal_head_attention_gqa_amd as attn
+    torch = _torch()
+    w = synth.LLAMA3_PREFILL
+    B, S, Nh, Nkv, D, theta, C = w.B, w.S, w.Nh, w.Nkv, w.Dh, w.rope_theta, 2048
+    q, k, v = w.inputs()
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    kcache = torch.empty((B, S, Nkv, D), dtype=torch.bfloat16, device="cuda")
+    vcache = torch.empty_like(kcache)
+    out = torch.empty_like(qd)
+    for c in range(0, S, C):
+        start = torch.full((B,), c, dtype=torch.int32, device="cuda")
+        attn.kv_append(kd[:, c:c + C].contiguous(), vd[:, c:c + C].contiguous(), kcache, vcache, start,
+                       rope_theta=theta)
+        if window == 0:
+            out[:, c:c + C] = attn.prefill_cached(qd[:, c:c + C].contiguous(), kcache, vcache, start, rope_theta=theta)
+    if window > 0:
+        zero = torch.zeros((B,), dtype=torch.int32, device="cuda")
+        attn.prefill_cached(qd, kcache, vcache, zero, rope_theta=theta, window=window, sinks=sinks, out=out)
+    # chunk and tile edges, window edges, the last row, and rows drawn at random
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, 2047, 2048, 2049, 4095, 4096, 4099, 4100, 6143, 6144, 8191],
+                                     np.random.default_rng(11).integers(0, S, 26)]))
+    got = out[:, torch.as_tensor(rows, device=out.device)].float().cpu().numpy()
+    # oracle: each row is a one-token chunk at its position; q and k rotated once by the oracle's RoPE
+    # (the same rotation prefill_chunk applies, so rope_theta=0 there)
+    kv_, vv = values(k, "bf16"), values(v, "bf16")
+    want = np.empty(got.shape)
+    for b in range(B):
+        kr = oracle.rope_rotate(kv_[b:b + 1], np.arange(S), theta)
+        qr = oracle.rope_rotate(values(q[b:b + 1, rows], "bf16"), rows, theta)
+        for i, r in enumerate(rows):
+            want[b, i] = oracle.prefill_chunk(qr[:, i:i + 1], kr[:, :r + 1], vv[b:b + 1, :r + 1], [int(r)],
+                                              window=window, sinks=sinks)[0, 0]
+    return got, want, rows
+
+
+def test_llama3_chunked_prefill_full_size_sampled_rows():
+    """Four 2048-token chunks with fused RoPE append, at the Llama-3-8B size the benchmark times."""
+    got, want, rows = _llama3_full_size_rows(0, 0)
+    assert max_abs(got, want) <= BF16_TOL
+
+
+def test_llama3_sliding_window_full_size_sampled_rows():
+    """Window 4096 + 4 sinks over the whole 8192-token sequence, the size the benchmark times."""
+    got, want, rows = _llama3_full_size_rows(4096, 4)
+    assert max_abs(got, want) <= BF16_TOL
