@@ -148,39 +148,50 @@ __global__ __launch_bounds__(256) void rope_table_rotate_bf16_kernel(const uint1
 }
 
 // Copy of src [rows, D] into dst with the half-split pairs of the span [roff, roff + Dr) rotated by
-// the table [S][Dr/2] (row r has position (r / N) % S); dims outside the span are copied. One
-// thread per (row, 8 consecutive dims). Used for MLA's decoupled RoPE block ("Transformer 与 LLM"
-// slide 06: only the 64-dim k^R / q^R part carries position).
+// the table [S][Dr/2] (row r has position (r / N) % S); the dims before the span are copied (the
+// span ends the row, roff + Dr = D). Used for MLA's decoupled RoPE block ("Transformer 与 LLM" slide 06: only the 64-dim k^R / q^R part carries
+// position). 16-byte vectors throughout: per row, roff/8 threads copy 8 dims each and Dr/16 threads
+// each rotate 8 pairs (i, i + Dr/2), reading both halves and writing both (rows of 16-byte-aligned
+// pitch; D, roff multiples of 8 and Dr of 16, checked by the launcher).
 __global__ void rope_span_table_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
                                        const float2* __restrict__ table, long long rows, int S, int N, int D,
                                        int roff, int Dr) {
-  const int groups = D / 8;
+  const int ncopy = roff / 8, nrot = Dr / 16, half = Dr / 2;
+  const int groups = ncopy + nrot;
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= rows * groups) return;
   const long long row = idx / groups;
-  const int d0 = (int)(idx % groups) * 8;
-  const int pos = (int)((row / N) % S);
+  const int gi = (int)(idx % groups);
   const uint16_t* x = src + row * D;
   uint16_t* y = dst + row * D;
-  const int half = Dr / 2;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int d = d0 + e;
-    const int j = d - roff;  // position inside the span
-    if (j < 0 || j >= Dr) {
-      y[d] = x[d];
-      continue;
-    }
-    const int i = j < half ? j : j - half;
-    const float2 r = rope_rot(bf16_to_f32(x[roff + i]), bf16_to_f32(x[roff + i + half]),
-                              table[(long long)pos * half + i]);
-    y[d] = f32_to_bf16(j < half ? r.x : r.y);
+  if (gi < ncopy) {
+    stg16(y + 8 * gi, ldg16(x + 8 * gi));
+    return;
   }
+  const int i0 = 8 * (gi - ncopy);  // pairs i0 .. i0+7 of the span
+  const int pos = (int)((row / N) % S);
+  const float2* tb = table + (long long)pos * half + i0;
+  const U4 xa = ldg16(x + roff + i0), xb = ldg16(x + roff + half + i0);
+  const uint32_t wa[4] = {xa.x, xa.y, xa.z, xa.w}, wb[4] = {xb.x, xb.y, xb.z, xb.w};
+  uint32_t ya[4], yb[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float2 r0 = rope_rot(bf16lo(wa[q]), bf16lo(wb[q]), tb[2 * q]);
+    const float2 r1 = rope_rot(bf16hi(wa[q]), bf16hi(wb[q]), tb[2 * q + 1]);
+    ya[q] = pack_bf16x2(r0.x, r1.x);
+    yb[q] = pack_bf16x2(r0.y, r1.y);
+  }
+  stg16(y + roff + i0, U4{ya[0], ya[1], ya[2], ya[3]});
+  stg16(y + roff + half + i0, U4{yb[0], yb[1], yb[2], yb[3]});
 }
 
 hipError_t launch_rope_span_table(const uint16_t* src, uint16_t* dst, const float2* table, long long rows, int S,
                                   int N, int D, int roff, int Dr, hipStream_t st) {
-  const long long n = rows * (D / 8);
+  // the span is the row's trailing block (MLA: 128 + 64 = 192): nothing after it to copy
+  if (D % 8 != 0 || roff % 8 != 0 || Dr % 16 != 0 || roff + Dr != D || (reinterpret_cast<uintptr_t>(src) & 15) ||
+      (reinterpret_cast<uintptr_t>(dst) & 15))
+    return hipErrorInvalidValue;
+  const long long n = rows * (roff / 8 + Dr / 16);
   if (n == 0) return hipSuccess;
   rope_span_table_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(src, dst, table, rows, S, N, D,
                                                                                    roff, Dr);

@@ -47,3 +47,21 @@ def test_lds_bound_is_tight_for_the_largest_head_dim():
         for N in (1, 2, 3, 7, 8):
             worst = max(worst, (255 // (N * (D // 16)) + 2) * (D // 2))
     assert worst <= LDS_ENTRIES
+
+
+@pytest.mark.parametrize("D,roff,Dr", [(192, 128, 64), (576, 512, 64), (128, 0, 128), (64, 32, 32)])
+def test_span_pass_writes_every_element_once(D, roff, Dr):
+    """The k^R span pass: per row, roff/8 threads copy 8 dims, Dr/16 threads rotate 8 pairs (i, i + Dr/2)
+    each; together they write every element of the row once, and a rotating thread reads exactly the
+    two 8-element halves it writes."""
+    ncopy, nrot, half = roff // 8, Dr // 16, Dr // 2
+    written = []
+    for gi in range(ncopy + nrot):
+        if gi < ncopy:
+            written += list(range(8 * gi, 8 * gi + 8))
+        else:
+            i0 = 8 * (gi - ncopy)
+            assert i0 + 8 <= half
+            written += list(range(roff + i0, roff + i0 + 8)) + list(range(roff + half + i0, roff + half + i0 + 8))
+    assert roff + Dr == D  # the launcher's precondition: the span ends the row
+    assert sorted(written) == list(range(D))
