@@ -420,6 +420,292 @@ __global__ __launch_bounds__(kThreads, (DQK > 128 ? 2 : 3)) void prefill_bf16_ke
   }
 }
 
+// ---- split-key prefill, for grids too small to fill the chip ----
+//
+// With few (sequence, head) pairs and a short sequence (GPT-2-small: 96 pairs of 1024 tokens), the
+// kernel above has too few work-groups, and its critical path is the wave that holds a sequence's
+// last 32 rows: one dependent chain over every key tile. Here the 4 waves of a work-group split
+// the key tiles of their query rows KS ways: the work-group holds 4/KS blocks of 32 query rows of
+// one head, and wave w takes block w / KS and the key tiles w % KS, w % KS + KS, ... (a KS-th of the
+// chain). Each wave streams its tiles through its own 2-stage LDS ring (direct-to-LDS loads, no
+// barrier while streaming) and runs the online softmax of the kernel above on them (fixed
+// reference max, exact path for a block that overflows it); at the end the KS partial (max, sum,
+// output) of each block are merged through LDS with the same recurrences ("Transformer 架构完全
+// 深度解析" §十三: running max and sum, applied to the waves' partial results). Plain prefill only
+// (positions 0 .. S-1, no cache, no window), equal q/k/v head dims, half-split RoPE over the whole
+// head when a table is given.
+template <int D, int KS>
+__global__ __launch_bounds__(kThreads, (D <= 64 ? 2 : 1)) void prefill_splitk_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ out, const float2* __restrict__ table, int B, int S, int Nh, int Nkv, float c, int causal,
+    int n_qb) {
+  constexpr int NB = 2;                 // stages per wave
+  constexpr int CH = D / 8;             // 16-byte chunks per row
+  constexpr int TE = kBC * D;           // elements of one K (or V) tile
+  constexpr int LT = kBC * CH / 64;     // load instructions per K (or V) tile, one wave
+  constexpr int NQ = D / 16;            // MFMA k-steps over the head dim
+  constexpr int NDB = D / 32;           // 32-row blocks of the output's head dim
+  constexpr int MP = D + 4;             // row pitch (floats) of the merge area
+  constexpr int QB = 4 / KS;            // 32-row query blocks per work-group
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[4][NB][2][TE];
+  static_assert(NB * 2 * TE * 2 >= (32 * MP + 64) * 4, "merge area must fit in a wave's ring");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // heaviest blocks first, (sequence, head) fastest; n_qb counts groups of QB blocks
+  const int nbh = B * Nh;
+  const int id = blockIdx.x;
+  const int bh = id % nbh;
+  const int qg = n_qb - 1 - id / nbh;
+  const int b = bh / Nh, h = bh % Nh;
+  const int g = h / (Nh / Nkv);
+  const int qsub = w / KS, ks = w % KS;  // the wave's query block within the group, its key split
+  const int p0 = (qg * QB + qsub) * 32;
+  const int col = lane & 31, hh = lane >> 5;
+  const int p = p0 + col;  // this lane's query position
+
+  // ---- Q^T operand (RoPE at position p when a table is given) ----
+  bf16x8 qreg[NQ];
+  {
+    U4 raw[NQ];
+    if (p < S) {
+      const uint16_t* qp = q + (((long long)b * S + p) * Nh + h) * D + hh * 8;
+#pragma unroll
+      for (int kk = 0; kk < NQ; ++kk) raw[kk] = ldg16(qp + kk * 16);
+      if (table) {  // half-split pairs (i, i + D/2): registers kk and kk + NQ/2
+        const float2* tb = table + (long long)p * (D / 2);
+#pragma unroll
+        for (int kk = 0; kk < NQ / 2; ++kk) {
+          uint32_t* pa = &raw[kk].x;
+          uint32_t* pb = &raw[kk + NQ / 2].x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float2 c0 = tb[kk * 16 + hh * 8 + 2 * e], c1 = tb[kk * 16 + hh * 8 + 2 * e + 1];
+            const float a0 = bf16lo(pa[e]), a1 = bf16hi(pa[e]);
+            const float b0 = bf16lo(pb[e]), b1 = bf16hi(pb[e]);
+            pa[e] = pack_bf16x2(fmaf(a0, c0.x, -(b0 * c0.y)), fmaf(a1, c1.x, -(b1 * c1.y)));
+            pb[e] = pack_bf16x2(fmaf(a0, c0.y, b0 * c0.x), fmaf(a1, c1.y, b1 * c1.x));
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < NQ; ++kk) raw[kk] = U4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int kk = 0; kk < NQ; ++kk) qreg[kk] = as_bf16x8(raw[kk]);
+    retire_vmem();  // from here on only the tile loads count in vmcnt
+  }
+
+  f32x16 o[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) o[i] = f32x16{};
+  float m = -INFINITY, mneg = -0.f, lsum = 0.f;
+
+  // ---- this wave's tiles: ks, ks + KS, ... up to its block's last row (none past the sequence) ----
+  const int last = p0 >= S ? 0 : causal ? min(S, p0 + 32) : S;
+  const int n_tiles = (last + kBC - 1) / kBC;
+  const int my_n = n_tiles > ks ? (n_tiles - ks + KS - 1) / KS : 0;
+  const long long kv_tok = (long long)Nkv * D;
+  const uint16_t* kbase = k + (long long)b * S * kv_tok + (long long)g * D;
+  const uint16_t* vbase = v + (long long)b * S * kv_tok + (long long)g * D;
+  // lane i of load sl covers tile bytes sl*1024 + 16i = row * 2D + 16 * chunk
+  auto trow = [&](int sl) { return (sl * 1024 + 16 * lane) / (D * 2); };
+  auto tchk = [&](int sl) { return ((sl * 1024 + 16 * lane) % (D * 2)) / 16; };
+  uint32_t loff[LT];
+#pragma unroll
+  for (int sl = 0; sl < LT; ++sl) loff[sl] = 2u * (uint32_t)(trow(sl) * (int)kv_tok + swz<CH>(tchk(sl), trow(sl)) * 8);
+  auto issue_tile = [&](int jt, uint16_t* kdst, uint16_t* vdst) {
+    if (jt * kBC + kBC <= S) {
+#pragma unroll
+      for (int sl = 0; sl < LT; ++sl)
+        load_lds16_async_sv(kbase + (long long)jt * kBC * kv_tok, loff[sl], kdst + sl * 512);
+#pragma unroll
+      for (int sl = 0; sl < LT; ++sl)
+        load_lds16_async_sv(vbase + (long long)jt * kBC * kv_tok, loff[sl], vdst + sl * 512);
+    } else {  // the last, partial tile: rows past the end re-read row S-1 (finite data, masked)
+#pragma unroll
+      for (int sl = 0; sl < LT; ++sl) {
+        const long long e = (long long)min(jt * kBC + trow(sl), S - 1) * kv_tok + swz<CH>(tchk(sl), trow(sl)) * 8;
+        load_lds16_async<false>(kbase + e, kdst + sl * 512);
+        load_lds16_async<false>(vbase + e, vdst + sl * 512);
+      }
+    }
+  };
+
+  // ---- per-lane LDS read offsets: as in the kernel above ----
+  const int kb_lane = col * D + swz<CH>(hh, col) * 8;
+  const int tr_j = (lane & 15) >> 2, tr_c = lane & 3, tr_dq = (lane >> 4) & 1;
+  int voff_par[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const int row = hh * 4 + tr_j;
+    voff_par[par] = row * D + swz<CH>(par * 4 + tr_dq * 2 + (tr_c >> 1), row) * 8 + (tr_c & 1) * 4;
+  }
+  auto vimm = [](int t, int db) {
+    const int dbase = (db & ~1) * 32;
+    const int tshift = CH == 16 ? (((db >> 1) & 1) ? -64 : 64) : 0;
+    return dbase + t * (8 * D + tshift);
+  };
+
+  auto compute_tile = [&](int jt, const uint16_t* Kt, const uint16_t* Vt) {
+    const int kb0 = jt * kBC;
+    constexpr int R = 4 < NQ ? 4 : NQ;
+    bf16x8 ka[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) ka[i] = *reinterpret_cast<const bf16x8*>(Kt + (kb_lane ^ (16 * i)));
+    f32x16 sv = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < NQ; ++kk) {
+      sv = mfma32x32x16(ka[kk % R], qreg[kk], sv);
+      if (kk + R < NQ) ka[kk % R] = *reinterpret_cast<const bf16x8*>(Kt + (kb_lane ^ (16 * (kk + R))));
+    }
+    if ((causal && kb0 + 31 > p0) || kb0 + 32 > S) {  // the diagonal block or the sequence end
+      const int base = kb0 + hh * 4;
+      const int hi = (causal ? min(p, S - 1) : S - 1) - base;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if ((i >> 2) * 8 + (i & 3) > hi) sv[i] = -INFINITY;
+    }
+    auto block_max = [&]() {
+      float mt = sv[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mt = fmaxf(mt, sv[i]);
+      return pair_max32(mt) * c;
+    };
+    auto set_ref = [&](float mr) {
+      m = mr;
+      mneg = mr == -INFINITY ? -0.f : -mr;
+    };
+    if (__builtin_expect(__ballot(m == -INFINITY) != 0, 0)) {
+      const float mb = block_max();
+      if (m == -INFINITY) set_ref(mb);
+    }
+    uint32_t pk[2][4];
+    float psum;
+    auto exps = [&]() {
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const float e0 = fast_exp2(fmaf(sv[i], c, mneg));
+        const float e1 = fast_exp2(fmaf(sv[i + 1], c, mneg));
+        psum = i == 0 ? e0 + e1 : psum + (e0 + e1);
+        pk[i >> 3][(i & 7) >> 1] = pack_bf16x2(e0, e1);
+      }
+    };
+    exps();
+    if (__builtin_expect(__ballot(!(psum <= kOvf)) != 0, 0)) {  // rare: a score far above the reference
+      const float mb = block_max();
+      const bool move = mb > m + kSlack;
+      const float alpha = move ? fast_exp2(m - mb) : 1.f;
+      if (move) set_ref(mb);
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+      exps();
+    }
+    lsum += psum;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const bf16x8 bop = __builtin_bit_cast(bf16x8, U4{pk[s2][0], pk[s2][1], pk[s2][2], pk[s2][3]});
+      const uint16_t* Vb = Vt + 16 * s2 * D;
+      auto vread = [&](int db) {
+        const uint2 lo = lds_read_tr16(Vb + voff_par[db & 1] + vimm(0, db));
+        const uint2 hi = lds_read_tr16(Vb + voff_par[db & 1] + vimm(1, db));
+        return __builtin_bit_cast(bf16x8, U4{lo.x, lo.y, hi.x, hi.y});
+      };
+      bf16x8 va[2];
+      va[0] = vread(0);
+      if (NDB > 1) va[1] = vread(1);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        o[db] = mfma32x32x16(va[db & 1], bop, o[db]);
+        if (db + 2 < NDB) va[db & 1] = vread(db + 2);
+      }
+    }
+  };
+
+  // ---- the wave's own ring: tile i+1 loads while tile i is computed ----
+  if (my_n > 0) issue_tile(ks, ring[w][0][0], ring[w][0][1]);
+  for (int i = 0; i < my_n; ++i) {
+    if (i + 1 < my_n) {
+      issue_tile(ks + KS * (i + 1), ring[w][(i + 1) & 1][0], ring[w][(i + 1) & 1][1]);
+      wait_vmem_n<2 * LT>();  // tile i has landed, tile i+1 may fly
+    } else {
+      wait_vmem();
+    }
+    compute_tile(ks + KS * i, ring[w][i & 1][0], ring[w][i & 1][1]);
+  }
+
+  // ---- merge the KS waves of each block: (max, sum, output) through LDS (each wave's own ring) ----
+  auto mo = [&](int vw) { return reinterpret_cast<float*>(&ring[vw][0][0][0]); };
+  const float ltot = pair_sum32(lsum);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4)
+      *reinterpret_cast<f32x4*>(mo(w) + col * MP + db * 32 + g4 * 8 + hh * 4) =
+          f32x4{o[db][g4 * 4], o[db][g4 * 4 + 1], o[db][g4 * 4 + 2], o[db][g4 * 4 + 3]};
+  if (hh == 0) {
+    mo(w)[32 * MP + col * 2] = m;  // -inf for a wave without tiles (its sum and output are 0)
+    mo(w)[32 * MP + col * 2 + 1] = ltot;
+  }
+  __syncthreads();
+  // thread t: row r = t / (8 / QB) of the group's 32 * QB rows, D / (8 / QB) dims from d0
+  constexpr int TPR = 8 / QB;   // threads per query row
+  constexpr int PER = D / TPR;  // output dims per thread
+  const int r = tid / TPR, qq = r % 32, w0 = (r / 32) * KS, d0 = (tid % TPR) * PER;
+  const int pr = (qg * QB + r / 32) * 32 + qq;  // the row's position
+  float mx = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < KS; ++u) mx = fmaxf(mx, mo(w0 + u)[32 * MP + qq * 2]);
+  float l = 0.f, acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int u = 0; u < KS; ++u) {
+    const float mv = mo(w0 + u)[32 * MP + qq * 2];
+    const float wgt = mv == -INFINITY ? 0.f : fast_exp2(mv - mx);
+    l = fmaf(wgt, mo(w0 + u)[32 * MP + qq * 2 + 1], l);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] = fmaf(wgt, mo(w0 + u)[qq * MP + d0 + e], acc[e]);
+  }
+  if (pr < S) {
+    const float inv = 1.f / l;
+    uint16_t* op = out + (((long long)b * S + pr) * Nh + h) * D + d0;
+#pragma unroll
+    for (int e = 0; e < PER; e += 8)
+      stg16(op + e, U4{pack_bf16x2(acc[e] * inv, acc[e + 1] * inv), pack_bf16x2(acc[e + 2] * inv, acc[e + 3] * inv),
+                       pack_bf16x2(acc[e + 4] * inv, acc[e + 5] * inv), pack_bf16x2(acc[e + 6] * inv, acc[e + 7] * inv)});
+  }
+}
+
+// The plain prefill takes the split-key kernel when the usual grid is under two rounds of the
+// chip's work-group slots (3 per CU x 256) and the rows are long enough (S >= 512) for one wave's
+// chain over every key tile to dominate. Two key splits (two 32-row blocks per work-group): on the
+// GPT-2-small shape (96 heads x 1024 tokens) 30.8-31.2 us against 33.7-34.3 us for the kernel above;
+// four splits were slower (38 us: twice the work-groups, each paying its prologue and merge), and
+// one split (private rings only) equal to two; two splits also halve the chain of long sequences
+// with few heads.
+constexpr long long kSplitMaxWG = 2 * 3 * 256;
+constexpr int kSplitMinS = 512;
+
+constexpr int kSplitKS = 2;  // key splits per query block (4 waves: 4 / KS blocks per work-group)
+
+template <int D>
+hipError_t launch_splitk(const PrefillArgs& a, hipStream_t st) {
+  constexpr int QB = 4 / kSplitKS;
+  const int n_qb = (a.S + 32 * QB - 1) / (32 * QB);  // groups of QB blocks of 32 rows
+  const long long n_wg = (long long)n_qb * a.B * a.Nh;
+  if (n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  prefill_splitk_kernel<D, kSplitKS><<<dim3((unsigned)n_wg), dim3(kThreads), 0, st>>>(
+      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
+      static_cast<uint16_t*>(a.out), a.table, a.B, a.S, a.Nh, a.Nkv, a.scale_log2, a.causal, n_qb);
+  return hipGetLastError();
+}
+
 template <int DQK, int DV, int HPW, bool kCache, bool kWin>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t st) {
   constexpr int BP = 32 * (4 / HPW);
@@ -454,6 +740,13 @@ hipError_t launch_d(const PrefillArgs& a, hipStream_t st) {
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st) {
   if (a.Dv != a.D) return a.D == 192 && a.Dv == 128 ? launch_d<192, 128>(a, st) : hipErrorInvalidValue;
+  if (!a.q_start && a.window == 0 && a.S >= kSplitMinS && (a.D == 64 || a.D == 128) &&
+      (a.table == nullptr || (a.rope_dims == a.D && !a.rope_inter))) {
+    const int G = a.Nh / a.Nkv;
+    const int hpw = G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1;
+    const long long n_wg = (long long)((a.S + 32 * (4 / hpw) - 1) / (32 * (4 / hpw))) * a.B * (a.Nh / hpw);
+    if (n_wg < kSplitMaxWG) return a.D == 64 ? launch_splitk<64>(a, st) : launch_splitk<128>(a, st);
+  }
   switch (a.D) {
     case 64:
       return launch_d<64, 64>(a, st);

@@ -24,7 +24,8 @@ def _same_bits(outs):
     return all(np.array_equal(outs[0], o) for o in outs[1:])
 
 
-@pytest.mark.parametrize("D,Nh,Nkv,S,rope", [(128, 8, 2, 333, 5e5), (64, 12, 12, 200, 0.0)])
+@pytest.mark.parametrize("D,Nh,Nkv,S,rope", [(128, 8, 2, 333, 5e5), (64, 12, 12, 200, 0.0),
+                                              (64, 4, 4, 700, 1e4), (128, 4, 2, 600, 0.0)])  # last two: split-key
 def test_prefill_repeatable(D, Nh, Nkv, S, rope):
     import causal_head_attention_gqa_amd as attn
     B = 2

@@ -84,6 +84,54 @@ def test_prefill_score_growth_beyond_reference(case):
     assert max_abs(got, want) <= BF16_TOL
 
 
+# Shapes the plain prefill sends to the split-key kernel (the usual grid is under two rounds of
+# work-group slots and S >= 512): two waves share each 32-row query block and split its key tiles.
+SPLITK_BF16 = [
+    # B, S, Nh, Nkv, D, rope, causal
+    (1, 600, 4, 4, 64, 0.0, True),     # MHA, ragged tail (600 = 18 x 32 + 24)
+    (2, 512, 8, 2, 128, 5e5, True),    # GQA group 4, RoPE
+    (1, 700, 6, 6, 64, 1e4, False),    # full attention, RoPE
+    (1, 530, 4, 1, 128, 0.0, True),    # MQA, ragged tail
+    (1, 545, 2, 2, 64, 1e4, True),     # a q-block with one wave's worth of tiles at the start
+]
+
+
+@pytest.mark.parametrize("case", SPLITK_BF16, ids=lambda c: "B%dS%dH%dK%dD%d_r%g_c%d" % c)
+def test_prefill_split_key_kernel(case):
+    B, S, Nh, Nkv, D, rope, causal = case
+    got, want, _ = _run(B, S, Nh, Nkv, D, "bf16", rope, causal, wid=150 + S)
+    assert max_abs(got, want) <= BF16_TOL
+
+
+@pytest.mark.parametrize("k0,k1", [(40, None), (0, 32)], ids=["later", "first"])
+def test_prefill_split_key_score_growth(k0, k1):
+    """The split-key kernel's exact path: keys scaled so that later scores exceed a wave's first
+    block's max by far (or fall far below it)."""
+    import causal_head_attention_gqa_amd as attn
+    B, S, Nh, Nkv, D = 1, 600, 4, 2, 128
+    wid = 190
+    q = synth.normal(wid, 0, (B, S, Nh, D), "bf16")
+    kf = synth.as_f32(synth.normal(wid, 1, (B, S, Nkv, D), "bf16"), "bf16").copy()
+    kf[:, k0:k1] *= 20.0
+    k = synth.f32_to_bf16_bits(kf)
+    v = synth.normal(wid, 2, (B, S, Nkv, D), "bf16")
+    out = attn.prefill(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"))
+    got = to_host_f64(out)
+    want = oracle.prefill(values(q, "bf16"), values(k, "bf16"), values(v, "bf16"))
+    assert np.all(np.isfinite(got))
+    assert max_abs(got, want) <= BF16_TOL
+
+
+def test_prefill_split_key_row0_is_v0_exactly():
+    import causal_head_attention_gqa_amd as attn
+    torch = __import__("torch")
+    q = synth.normal(195, 0, (2, 640, 4, 64), "bf16")
+    kv = synth.normal(195, 1, (2, 640, 4, 64), "bf16")
+    vd = to_dev(synth.normal(195, 2, (2, 640, 4, 64), "bf16"), "bf16")
+    out = attn.prefill(to_dev(q, "bf16"), to_dev(kv, "bf16"), vd, rope_theta=1e4)
+    assert torch.equal(out[:, 0], vd[:, 0])
+
+
 SMALL_F32 = [
     (1, 128, 4, 4, 16, 1e4, True),
     (2, 150, 4, 2, 32, 1e4, True),

@@ -197,3 +197,37 @@ def test_grid_covers_every_tile_once_and_stays_in_bounds(case):
         q_hi = ((b * S + pw) * Nh + h) * dqk + 8 + (dqk // 16 - 1) * 16 + 8
         o_hi = ((b * S + pw) * Nh + h) * dv + 4 + (dv // 32 - 1) * 32 + 3 * 8 + 4
         assert q_hi.max() <= B * S * Nh * dqk and o_hi.max() <= B * S * Nh * dv
+
+
+@pytest.mark.parametrize("KS", [1, 2, 4])
+@pytest.mark.parametrize("S,causal", [(600, True), (545, True), (512, False), (1024, True)])
+def test_split_key_grid_covers_every_block_tile_once(KS, S, causal):
+    """The split-key prefill: work-group qg holds query blocks qg*QB .. qg*QB+QB-1 (QB = 4/KS);
+    wave w takes block w // KS and key tiles w % KS, w % KS + KS, ...; every (block, visible key
+    tile) is computed by exactly one wave, and the merge's 256 threads write every (row, dim) of
+    the group once."""
+    QB = 4 // KS
+    n_qb = (S + 32 * QB - 1) // (32 * QB)
+    seen = {}
+    for qg in range(n_qb):
+        for w in range(4):
+            p0 = (qg * QB + w // KS) * 32
+            last = 0 if p0 >= S else (min(S, p0 + 32) if causal else S)
+            n_tiles = (last + 31) // 32
+            ks = w % KS
+            my_n = (n_tiles - ks + KS - 1) // KS if n_tiles > ks else 0
+            for i in range(my_n):
+                key = (p0 // 32, ks + KS * i)
+                assert key not in seen
+                seen[key] = w
+    want = {(qb, j) for qb in range((S + 31) // 32) for j in range(((min(S, 32 * qb + 32) if causal else S) + 31) // 32)}
+    assert set(seen) == want
+    for D in (64, 128):
+        TPR = 8 // QB
+        PER = D // TPR
+        cells = set()
+        for t in range(256):
+            r, d0 = t // TPR, (t % TPR) * PER
+            for e in range(PER):
+                cells.add((r, d0 + e))
+        assert cells == {(r, d) for r in range(32 * QB) for d in range(D)}
