@@ -36,8 +36,8 @@ DecodePlan decode_plan(int B, int Nh, int Nkv, int Dqk, int Dv, int max_ctx) {
   p.mla = is_mla_shape(Nkv, Dqk, Dv);
   if (max_ctx <= 0 || B <= 0) return p;
   if (p.mla) {
-    // one work-group per (sequence, head group, chunk); one such work-group fills a CU (64-head
-    // groups: 124 KiB of LDS, one wave per SIMD), so aim for about 256 work-groups
+    // one work-group per (sequence, head group, chunk); one such work-group fills a CU (128- and
+    // 64-head groups: 153 and 160 KiB of LDS, one wave per SIMD), so aim for about 256 work-groups
     const long long groups = (long long)B * (Nh / mla_heads_per_group(Nh));
     const int tiles = (max_ctx + 31) / 32;
     long long want = (256 + groups - 1) / groups;  // about one work-group per CU
@@ -372,6 +372,7 @@ int attn_decode(const void* q, const void* kcache, const void* vcache, const int
   const bool mla = is_mla_shape(Nkv, Dqk, Dv);
   if (mla) {
     if (vcache != kcache || ldv != ldk || Nh % 16 != 0) return ATTN_ERR_UNSUPPORTED;
+    if (ldk * 64 > 0x7fffffffLL) return ATTN_ERR_INVALID;  // 32-bit byte offsets within a 32-row tile
   } else {
     if (Dqk != Dv || (Dqk != 64 && Dqk != 128)) return ATTN_ERR_UNSUPPORTED;
     if (Nh / Nkv > 16 && (Nh / Nkv) % 16 != 0) return ATTN_ERR_UNSUPPORTED;  // heads go in groups of 16

@@ -123,6 +123,13 @@ __device__ __forceinline__ void load_lds16_async_sv(const void* sbase, uint32_t 
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
 }
 
+// The same, with the 5 wait states that a base pair written by a vector instruction would need
+// inside the asm: for loads placed among other work, where a branch target may come right before.
+__device__ __forceinline__ void load_lds16_async_sv_nop(const void* sbase, uint32_t voff, const void* lds_base) {
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
+}
+
 // Work-group barrier without the memory fences of __syncthreads(): for tiles filled by
 // load_lds16_async after an explicit vmcnt wait, where the fence's wait for every outstanding
 // load (including later stages still in flight) is not wanted.

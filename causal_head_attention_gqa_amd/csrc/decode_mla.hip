@@ -6,9 +6,11 @@
 // (the first 512 dims of the same row), and the scale is given by the caller (1/sqrt(192) for
 // DeepSeek-V3's 128 + 64 per-head query dims).
 //
-// With 128 heads per row the work is ~242 FLOP per cached byte, so the matrix cores are used. Two
-// kernels: head counts that are multiples of 64 use the pair kernel further below (32 heads per
-// pair of waves on 32x32x16 products); other head counts use this one, 16 heads per wave:
+// With 128 heads per row the work is ~242 FLOP per cached byte, so the matrix cores are used. Three
+// kernels: head counts that are multiples of 128 without in-kernel RoPE use the wide kernel at the
+// end of the file (all heads of a row in one work-group, 64 per pair of waves); other multiples of
+// 64 use the pair kernel further below (32 heads per pair of waves on 32x32x16 products); other
+// head counts use this one, 16 heads per wave:
 //   - a work-group = NW waves x 16 heads owns (sequence, 16*NW heads, one context chunk); with
 //     NW = 8 all 128 heads share the work-group, so every cached row crosses HBM once per chunk;
 //   - 32-token tiles (36 KiB) go from HBM straight into an LDS ring of NB stages
@@ -26,6 +28,8 @@
 // Work-group ids are mapped so that the head groups of one (sequence, chunk) run on one XCD and
 // share its L2 when the heads do not fit one work-group.
 #include "kernels.hpp"
+
+#include <type_traits>
 
 namespace attn {
 
@@ -673,6 +677,404 @@ hipError_t launch(const DecodeArgs& a, hipStream_t st) {
 }
 }  // namespace pair
 
+// ---- 64 heads per wave pair, all 128 heads of a row in one work-group (head counts that are
+// multiples of 128, no in-kernel RoPE) ----
+//
+// The pair kernel above reads one 1 KiB operand from LDS per 32x32x16 product, which makes the LDS
+// read rate, not the matrix cores, its limit. Here each wave holds the query operands and the
+// accumulators of 64 heads (two 32-head groups), so every K and V operand it reads from LDS feeds
+// two products:
+//   - a work-group = 4 waves owns (sequence, 128 heads, one context chunk); waves 2p and 2p+1 share
+//     heads 64p .. 64p+63, wave 2p+r contracts dims 288r .. 288r+287 of them (36 products per
+//     tile), the partial scores of both groups are exchanged through LDS as in the pair kernel, and
+//     wave 2p+r accumulates O^T for output dims 256r .. 256r+255 of all 64 heads (32 products);
+//   - per lane: 144 query registers and 256 accumulator registers (the whole accumulator file),
+//     which fits one wave per SIMD only because nothing but the matrix products touches the
+//     accumulators inside the loop: the reference max per head is fixed at the first tile, so no
+//     rescale is ever applied to O (heads whose scores outgrow it are recomputed exactly after the
+//     loop, as in the pair kernel);
+//   - per tile and work-group the LDS carries 72 KiB of K reads, 64 KiB of transposing V reads,
+//     64 KiB of score exchange and the 36 KiB tile itself for 128 heads, against twice the K and V
+//     reads for the same heads in the pair kernel; each cached row crosses HBM once;
+//   - a 3-stage LDS ring (108 KiB) plus 32 KiB of exchange buffers;
+//   - the chunks of one sequence are dispatched to one XCD (ids of equal id % 8), so the query rows
+//     every chunk re-reads stay in that XCD's L2.
+namespace wide {
+constexpr int kWaves = 4;
+constexpr int kHeads = 128;           // heads per work-group
+constexpr int kStages = 4;            // tile j (V) and j+1 (K) are read while j+2 and j+3 load
+constexpr int kSPW = NSLOT / kWaves;  // 9 tile-load instructions per wave and tile
+constexpr int kKS = DQ / 16;          // 36 k-steps of Q.K
+constexpr int kDB = DV / 2 / 32;      // 8 output blocks of 32 dims per wave
+static_assert(NSLOT % kWaves == 0, "tile loads split evenly over the waves");
+
+__global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_wide_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[kStages][TILE];
+  __shared__ __attribute__((aligned(16))) uint32_t xp[2][kWaves][2][64][4];  // P (bf16 pairs), two buffers
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = w & 1;      // output half of P.V; the pair's head group this wave owns
+  const int hf = lane >> 5;
+  const int col = lane & 31;
+  // id -> (sequence, chunk, head group); ids of equal id % 8 share an XCD and hold all the chunks
+  // (and head groups) of sequences id % 8, id % 8 + 8, ...
+  const int n_hg = a.Nh / kHeads;
+  const int id = blockIdx.x;
+  const int kx = id / 8;
+  const int hgrp = kx % n_hg;
+  const int k2 = kx / n_hg;
+  const int b = id % 8 + 8 * (k2 / a.nsplit);
+  const int s = k2 % a.nsplit;
+  if (b >= a.B) return;
+  const int ctx = min(max(a.ctx_lens[b], 0), a.max_ctx);
+  const int t0 = s * a.chunk;
+  const int hp = hgrp * kHeads + (w >> 1) * 64;  // the pair's heads: hp + 32g + col, g = 0, 1
+  if (t0 >= ctx) {
+    if (a.nsplit == 1) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        uint16_t* op = a.out + ((long long)b * a.Nh + hp + 32 * g + col) * DV + r * (DV / 2) + hf * 4;
+#pragma unroll
+        for (int db = 0; db < kDB; ++db)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) *reinterpret_cast<uint2*>(op + db * 32 + e * 8) = make_uint2(0u, 0u);
+      }
+    }
+    return;
+  }
+  const int t1 = min(ctx, t0 + a.chunk);
+
+  // ---- tile loads: wave w fills slots w*9 .. w*9+8; lane i of slot sl covers tile bytes
+  // sl*1024 + 16i = row*1152 + 16pc and fetches logical chunk pc ^ key(row) of that row. One
+  // byte offset per slot serves the full tiles; the chunk's last, partial tile clamps its rows. ----
+  const long long ldk = a.ldk;  // Nkv == 1
+  const uint16_t* seq = a.kc + (long long)b * a.max_ctx * ldk;
+  auto slot_row = [&](int u) { return ((w * kSPW + u) * 1024 + 16 * lane) / (DQ * 2); };
+  auto slot_chunk = [&](int u) {
+    const int ob = (w * kSPW + u) * 1024 + 16 * lane;
+    return ((ob % (DQ * 2)) / 16) ^ pair::key(ob / (DQ * 2));
+  };
+  uint32_t loff[kSPW];
+#pragma unroll
+  for (int u = 0; u < kSPW; ++u) loff[u] = 2u * (uint32_t)(slot_row(u) * (int)ldk + slot_chunk(u) * 8);
+  const int n_tiles = (t1 - t0 + TT - 1) / TT;
+  auto issue_tile = [&](int j, uint16_t* dst) {
+    const int tb = t0 + j * TT;
+    const uint16_t* base = seq + (long long)tb * ldk;  // wave-uniform (scalar registers)
+    const int lim = t1 - 1 - tb;                       // last row of the tile inside the chunk
+    // each path starts with 5 wait states, so no branch into it can bring a base that a vector
+    // instruction wrote just before the first load (the pair is written by scalar instructions)
+    if (lim >= TT - 1) {
+      asm volatile("s_nop 4" ::: "memory");
+#pragma unroll
+      for (int u = 0; u < kSPW; ++u) load_lds16_async_sv(base, loff[u], dst + (w * kSPW + u) * 512);
+    } else {
+      asm volatile("s_nop 4" ::: "memory");
+#pragma unroll
+      for (int u = 0; u < kSPW; ++u) {
+        const int row = slot_row(u);  // rows past the chunk re-read row lim (masked)
+        const uint32_t off = row <= lim ? loff[u] : loff[u] - 2u * (uint32_t)((row - lim) * (int)ldk);
+        load_lds16_async_sv(base, off, dst + (w * kSPW + u) * 512);
+      }
+    }
+  };
+  // Q^T operand of k-step kk: own head hp + 32r + col, dims 16kk + 8hf .. +7. Only tile 0 loads with
+  // the query rows (all work-groups start together, so the first requests queue behind each other);
+  // tiles 1 and 2 are issued once these have landed and load during the products of tile 0.
+  bf16x8 qreg[kKS];
+  issue_tile(0, ring[0]);
+  {
+    const uint16_t* qp = a.q + ((long long)b * a.Nh + hp + 32 * r + col) * DQ + hf * 8;
+#pragma unroll
+    for (int kk = 0; kk < kKS; ++kk) qreg[kk] = as_bf16x8(ldg16(qp + kk * 16));
+  }
+  retire_vmem();  // the query rows and tile 0 have landed
+  issue_tile(min(1, n_tiles - 1), ring[1]);
+  issue_tile(min(2, n_tiles - 1), ring[2]);
+
+  f32x16 o[2][kDB];
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int i = 0; i < kDB; ++i) o[g][i] = f32x16{};
+  float m = 0.f, lsum = 0.f;  // own head: fixed reference max (log2 units) and this lane's sum
+  bool ovf = false;
+  constexpr float kOvf = 1.8446744e19f;  // 2^64
+
+  // K operand of k-step kk: row col, logical chunk 2kk + hf = 8(kk>>2) + (2(kk&3) + hf); the key
+  // changes only the low 3 bits, so the physical chunk is 8(kk>>2) + ((2(kk&3) + hf) ^ key)
+  const int kkey = pair::key(col);
+  int koff[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) koff[u] = col * DQ + (((2 * u + hf) ^ kkey) << 3);
+  // V operand (transposing read) of (ks, db): as in the pair kernel, output half r
+  const int tj = (lane & 15) >> 2, tc = lane & 3, dq = (lane >> 4) & 1;
+  const int x = 2 * dq + (tc >> 1);
+  int vb[2][2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      vb[par][t] = (4 * hf + tj) * DQ + 8 * (32 * r + 4 * (par ^ (tj >> 1)) + (x ^ (2 * hf) ^ t)) + (tc & 1) * 4;
+
+  // S^T[32 tokens x 32 own heads] of the tile in T over all 576 dims: one accumulation chain,
+  // kKR K operands in flight. With kSpread, this wave's 9 loads of a full tile (base, dst) are
+  // issued among the products, one after every fourth, so that their issue overlaps the products.
+  auto qk = [&](const uint16_t* T, auto spread, const uint16_t* base, uint16_t* dst) {
+    constexpr bool kSpread = decltype(spread)::value;
+    constexpr int kKR = 4;
+    auto kread = [&](int kk) { return *reinterpret_cast<const bf16x8*>(T + koff[kk & 3] + 64 * (kk >> 2)); };
+    bf16x8 ka[kKR];
+#pragma unroll
+    for (int u = 0; u < kKR; ++u) ka[u] = kread(u);
+    f32x16 sv = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < kKS; ++kk) {
+      sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk % kKR], qreg[kk], sv, 0, 0, 0);
+      if (kk + kKR < kKS) ka[kk % kKR] = kread(kk + kKR);
+      if constexpr (kSpread) {
+        static_assert(kKS == 4 * kSPW, "one load per four products");
+        if (kk % 4 == 0) load_lds16_async_sv_nop(base, loff[kk / 4], dst + (w * kSPW + kk / 4) * 512);
+      }
+    }
+    return sv;
+  };
+  using NoSpread = std::integral_constant<bool, false>;
+  using Spread = std::integral_constant<bool, true>;
+  // scores of tile j past the chunk's end -> -inf (token of score i: 8(i>>2) + 4hf + (i&3))
+  auto mask = [&](f32x16& sv, int j) {
+    const int tbase = t0 + j * TT;
+    if (tbase + TT > t1) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (tbase + (i >> 2) * 8 + hf * 4 + (i & 3) >= t1) sv[i] = -INFINITY;
+    }
+  };
+  // exponentials of the pair (2i, 2i+1) against the reference max, packed to bf16
+  auto expo = [&](const f32x16& sv, int i, float& psum) {
+    const float e0 = fast_exp2(fmaf(sv[2 * i], a.scale_log2, -m));
+    const float e1 = fast_exp2(fmaf(sv[2 * i + 1], a.scale_log2, -m));
+    psum += e0 + e1;
+    return pack_bf16x2(e0, e1);
+  };
+  auto put_p = [&](const uint32_t (&pk)[2][4], int buf) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      *reinterpret_cast<uint4*>(&xp[buf][w][ks][lane][0]) = make_uint4(pk[ks][0], pk[ks][1], pk[ks][2], pk[ks][3]);
+  };
+
+  // ---- tile 0: scores, the reference max, P ----
+  uint32_t pk[2][4];
+  barrier_only();  // every wave's part of tile 0 is in LDS
+  {
+    f32x16 sv = qk(ring[0], NoSpread{}, nullptr, nullptr);
+    mask(sv, 0);
+    float mt = sv[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mt = fmaxf(mt, sv[i]);
+    m = pair_max32(mt) * a.scale_log2;  // fixed reference max: the first tile's max per head
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pk[i >> 2][i & 3] = expo(sv, i, psum);
+    lsum += psum;
+    ovf |= !(psum <= kOvf);
+    put_p(pk, 0);
+  }
+
+  // ---- step j: P.V of tile j (P exchanged at the barrier) while the scores and P of tile j+1 are
+  // made: Q.K of tile j+1 first, then its exponentials interleaved with the P.V products. One
+  // barrier per step: tile j+1 has landed in every wave, every wave's P(j) is in LDS, and every
+  // wave is done with stage (j-1) % 4, which the load of tile j+3 then refills. A load past the
+  // last tile re-reads the last one into a stage that is never read again, so every step keeps
+  // one fixed vmcnt. P goes through two LDS buffers: P(j+1) is written while P(j) may still be
+  // read by the partner. ----
+  for (int j = 0; j < n_tiles; ++j) {
+    wait_vmem_n<kSPW>();  // tile j+1 has landed (tile j+2 may still fly)
+    barrier_only();
+    const bool more = j + 1 < n_tiles;
+    // the load of tile j+3 (a re-read of the last tile past the end): spread over the products of
+    // Q.K(j+1) when that tile is full and there is a Q.K, else issued at once
+    const int jl = min(j + 3, n_tiles - 1);
+    const bool spread = more && t0 + jl * TT + TT <= t1;
+    if (!spread) issue_tile(jl, ring[(j + 3) & 3]);
+    uint4 pq[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) pq[ks] = *reinterpret_cast<const uint4*>(&xp[j & 1][w ^ 1][ks][lane][0]);
+    f32x16 sn = f32x16{};
+    if (spread) {
+      sn = qk(ring[(j + 1) & 3], Spread{}, seq + (long long)(t0 + jl * TT) * ldk, ring[(j + 3) & 3]);
+      mask(sn, j + 1);
+    } else if (more) {
+      sn = qk(ring[(j + 1) & 3], NoSpread{}, nullptr, nullptr);
+      mask(sn, j + 1);
+    }
+    // O^T[256 dims x 32 heads] += V^T P^T for both head groups of the pair: each V operand feeds two
+    // products (group r = own P, group 1 - r = the partner's); the exponentials of tile j+1 are
+    // spread over the first eight product pairs
+    const uint16_t* T = ring[j & 3];
+    uint32_t pn[2][4];
+    float psum = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 pown = __builtin_bit_cast(bf16x8, U4{pk[ks][0], pk[ks][1], pk[ks][2], pk[ks][3]});
+      const bf16x8 poth = __builtin_bit_cast(bf16x8, U4{pq[ks].x, pq[ks].y, pq[ks].z, pq[ks].w});
+      const bf16x8 bop0 = r == 0 ? pown : poth;
+      const bf16x8 bop1 = r == 0 ? poth : pown;
+      auto vread = [&](int db) {
+        const uint16_t* p = T + (16 * ks) * DQ + 32 * (db & ~1);
+        const uint2 lo = lds_read_tr16(p + vb[db & 1][0]);
+        const uint2 hi = lds_read_tr16(p + 8 * DQ + vb[db & 1][1]);
+        return __builtin_bit_cast(bf16x8, U4{lo.x, lo.y, hi.x, hi.y});
+      };
+      constexpr int kVR = 2;  // V operands in flight
+      bf16x8 va[kVR];
+#pragma unroll
+      for (int u = 0; u < kVR; ++u) va[u] = vread(u);
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        o[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db % kVR], bop0, o[0][db], 0, 0, 0);
+        o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db % kVR], bop1, o[1][db], 0, 0, 0);
+        if (db + kVR < kDB) va[db % kVR] = vread(db + kVR);
+        if (ks == 0) pn[db >> 2][db & 3] = expo(sn, db, psum);
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pk[ks][e] = pn[ks][e];
+    if (more) {
+      lsum += psum;
+      ovf |= !(psum <= kOvf);
+      put_p(pk, (j + 1) & 1);
+    }
+  }
+  wait_vmem();  // the re-reads must land before the work-group's LDS is released
+
+  // ---- (max, sum) and the overflow flags of the own heads to the partner, through the last
+  // 1,040 bytes of the ring once every wave is done with it ----
+  float* xml = reinterpret_cast<float*>(&ring[kStages - 1][0]) + TILE / 2 - 260;  // [wave][max, sum][32]
+  uint32_t* xbad = reinterpret_cast<uint32_t*>(xml + kWaves * 2 * 32);            // [wave]
+  const float ltot = pair_sum32(lsum);
+  const uint64_t bal = __ballot(ovf);
+  __syncthreads();
+  if (hf == 0) {
+    xml[(w * 2 + 0) * 32 + col] = m;
+    xml[(w * 2 + 1) * 32 + col] = ltot;
+  }
+  if (lane == 0) xbad[w] = (uint32_t)((bal | (bal >> 32)) & 0xffffffffull);
+  __syncthreads();
+  const uint32_t bad_g[2] = {xbad[(w & ~1) + 0], xbad[(w & ~1) + 1]};
+
+  // ---- result: lane holds head hp + 32g + col, dims 256r + 32db + 8e + 4hf + i in o[g][db][4e + i].
+  // Staged through this wave's 32 KiB of the (now idle) ring as 64 rows of 256 dims in bf16, so
+  // that the stores are whole 512-byte half rows (two heads per store instruction) instead of
+  // 8-byte pieces of 32 rows. 16-byte chunk c of row hl sits at chunk c ^ (hl & 31), with its two
+  // 8-byte halves swapped when bit 4 of hl is set: the 64-bit writes (32 lanes = 32 rows) and the
+  // 128-bit reads (16 lanes = 16 chunks of one row) then hit distinct LDS bank groups. ----
+  uint16_t* stg = &ring[0][0] + w * (64 * 256);
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int hl = 32 * g + col;
+    const float inv = 1.f / xml[(((w & ~1) + g) * 2 + 1) * 32 + col];  // a chunk's output over its own sum
+    const int half = hf ^ ((hl >> 4) & 1);
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        *reinterpret_cast<uint2*>(stg + hl * 256 + (((4 * db + e) ^ (hl & 31)) << 3) + (half << 2)) =
+            make_uint2(pack_bf16x2(o[g][db][4 * e] * inv, o[g][db][4 * e + 1] * inv),
+                       pack_bf16x2(o[g][db][4 * e + 2] * inv, o[g][db][4 * e + 3] * inv));
+  }
+#pragma unroll 4
+  for (int i = 0; i < 32; ++i) {
+    const int hl = 2 * i + hf;  // lanes 0-31: row 2i, lanes 32-63: row 2i+1; chunk col of the row
+    uint4 v = *reinterpret_cast<const uint4*>(stg + hl * 256 + ((col ^ (hl & 31)) << 3));
+    if ((hl >> 4) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
+    if ((bad_g[hl >> 5] >> (hl & 31)) & 1) continue;  // recomputed below
+    const long long row = (long long)b * a.Nh + hp + hl;
+    uint16_t* op = (a.nsplit == 1 ? a.out + row * DV : a.part_o + (row * a.nsplit + s) * DV) + r * (DV / 2) + col * 8;
+    *reinterpret_cast<uint4*>(op) = v;
+  }
+  if (a.nsplit > 1 && hf == 0 && !((bad_g[r] >> col) & 1)) {
+    const long long slot = ((long long)b * a.Nh + hp + 32 * r + col) * a.nsplit + s;
+    a.part_ml[slot * 2 + 0] = m;
+    a.part_ml[slot * 2 + 1] = xml[(w * 2 + 1) * 32 + col];
+  }
+
+  // ---- heads whose scores outgrew the reference max by ~2^60 or more: recomputed exactly by a
+  // plain two-pass loop over the chunk's rows (vector ALU, blocks of 4096 tokens), each wave for
+  // its 256 output dims of both groups of the pair. ----
+  uint64_t bad = (uint64_t)bad_g[0] | ((uint64_t)bad_g[1] << 32);
+  __syncthreads();  // every wave is done with the ring: its LDS holds the recompute's scratch
+  if (bad == 0) return;
+  float* qs = reinterpret_cast<float*>(&ring[0][0]) + w * (kStages * TILE / 2 / kWaves);  // 576 + 4096 floats
+  float* sc = qs + DQ;
+  for (; bad; bad &= bad - 1) {
+    const int c = __builtin_ctzll(bad);
+    const int hc = hp + c;
+    const uint16_t* qp = a.q + ((long long)b * a.Nh + hc) * DQ;
+    for (int d = lane; d < DQ; d += 64) qs[d] = bf16_to_f32(qp[d]);
+    float mr = -INFINITY, lr = 0.f, o4[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int tb = t0; tb < t1; tb += 4096) {
+      const int n = min(4096, t1 - tb);
+      float mx = -INFINITY;
+      for (int i = lane; i < n; i += 64) {
+        const uint16_t* kp = seq + (long long)(tb + i) * ldk;
+        float acc = 0.f;
+        for (int d = 0; d < DQ; d += 8) {
+          const U4 kv = ldg16(kp + d);
+          acc = fmaf(qs[d + 0], bf16lo(kv.x), acc);
+          acc = fmaf(qs[d + 1], bf16hi(kv.x), acc);
+          acc = fmaf(qs[d + 2], bf16lo(kv.y), acc);
+          acc = fmaf(qs[d + 3], bf16hi(kv.y), acc);
+          acc = fmaf(qs[d + 4], bf16lo(kv.z), acc);
+          acc = fmaf(qs[d + 5], bf16hi(kv.z), acc);
+          acc = fmaf(qs[d + 6], bf16lo(kv.w), acc);
+          acc = fmaf(qs[d + 7], bf16hi(kv.w), acc);
+        }
+        acc *= a.scale_log2;
+        sc[i] = acc;
+        mx = fmaxf(mx, acc);
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      const float mn = fmaxf(mr, mx);
+      const float al = mr == -INFINITY ? 0.f : fast_exp2(mr - mn);
+      lr *= al;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o4[e] *= al;
+      mr = mn;
+      for (int i = 0; i < n; ++i) {
+        const float pw = fast_exp2(sc[i] - mr);
+        lr += pw;
+        const uint2 vv = *reinterpret_cast<const uint2*>(seq + (long long)(tb + i) * ldk + r * (DV / 2) + 4 * lane);
+        o4[0] = fmaf(pw, bf16lo(vv.x), o4[0]);
+        o4[1] = fmaf(pw, bf16hi(vv.x), o4[1]);
+        o4[2] = fmaf(pw, bf16lo(vv.y), o4[2]);
+        o4[3] = fmaf(pw, bf16hi(vv.y), o4[3]);
+      }
+    }
+    const float inv = 1.f / lr;
+    const long long sl = ((long long)b * a.Nh + hc) * a.nsplit + s;
+    uint16_t* op = (a.nsplit == 1 ? a.out + ((long long)b * a.Nh + hc) * DV : a.part_o + sl * DV) + r * (DV / 2) + 4 * lane;
+    *reinterpret_cast<uint2*>(op) = make_uint2(pack_bf16x2(o4[0] * inv, o4[1] * inv), pack_bf16x2(o4[2] * inv, o4[3] * inv));
+    if (a.nsplit > 1 && (c >> 5) == r && lane == 0) {
+      a.part_ml[sl * 2 + 0] = mr;
+      a.part_ml[sl * 2 + 1] = lr;
+    }
+  }
+}
+
+hipError_t launch(const DecodeArgs& a, hipStream_t st) {
+  const long long n_wg = 8 * (((long long)a.B + 7) / 8) * a.nsplit * (a.Nh / kHeads);
+  if (n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  decode_mla_wide_kernel<<<dim3((unsigned)n_wg), dim3(kWaves * 64), 0, st>>>(a);
+  return hipGetLastError();
+}
+}  // namespace wide
+
 template <int NW>
 hipError_t launch_nw(const DecodeArgs& a, hipStream_t st) {
   const long long n_hg = a.Nh / (16 * NW);
@@ -688,9 +1090,12 @@ hipError_t launch_nw(const DecodeArgs& a, hipStream_t st) {
 }  // namespace
 
 int mla_waves_per_group(int Nh) { return Nh % 128 == 0 ? 8 : Nh % 64 == 0 ? 4 : Nh % 32 == 0 ? 2 : 1; }
-int mla_heads_per_group(int Nh) { return Nh % pair::kHeads == 0 ? pair::kHeads : 16 * mla_waves_per_group(Nh); }
+int mla_heads_per_group(int Nh) {
+  return Nh % wide::kHeads == 0 ? wide::kHeads : Nh % pair::kHeads == 0 ? pair::kHeads : 16 * mla_waves_per_group(Nh);
+}
 
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t st) {
+  if (a.Nh % wide::kHeads == 0 && !(a.rope_theta > 0)) return wide::launch(a, st);
   if (a.Nh % pair::kHeads == 0) return pair::launch(a, st);
   switch (mla_waves_per_group(a.Nh)) {
     case 8:

@@ -171,6 +171,10 @@ MLA_PAIR_CASES = [
     (2, 64, 333, [333, 32], 0.0),
     (2, 64, 200, [200, 77], 1e4),      # decoupled q^R RoPE (held by the upper reduction half)
     (2, 192, 130, [130, 96], 5e5),     # three head groups
+    # multiples of 128 without RoPE: one work-group holds all heads of a row (64 per wave pair)
+    (9, 128, 700, [700, 1, 33, 64, 65, 512, 513, 95, 640], 0.0),  # grid with empty ids (B % 8 != 0)
+    (2, 256, 333, [333, 32], 0.0),     # two 128-head groups
+    (2, 128, 200, [200, 77], 1e4),     # with RoPE: the pair kernel
 ]
 
 
@@ -201,13 +205,14 @@ def test_mla_decode_single_chunk():
     assert max_abs(got, want) <= BF16_TOL
 
 
-@pytest.mark.parametrize("B,T,ctx,rope", [(2, 300, [300, 200], 0.0), (2, 300, [300, 260], 1e4),
-                                          (256, 160, None, 0.0)], ids=["splits", "rope", "one-chunk"])
-def test_mla_decode_score_growth_beyond_reference(B, T, ctx, rope):
+@pytest.mark.parametrize("B,T,ctx,rope,Nh", [(2, 300, [300, 200], 0.0, 64), (2, 300, [300, 260], 1e4, 64),
+                                             (256, 160, None, 0.0, 64), (2, 300, [300, 200], 0.0, 128),
+                                             (256, 160, None, 0.0, 128)],
+                         ids=["splits", "rope", "one-chunk", "h128-splits", "h128-one-chunk"])
+def test_mla_decode_score_growth_beyond_reference(B, T, ctx, rope, Nh):
     """Scores that grow far past the first tile's max (the decoupled k^R dims of later tokens
     scaled by 200, so V = c^KV stays of order one): such heads leave the fast path's fixed
     reference max and are recomputed exactly; the result still matches the oracle."""
-    Nh = 64
     ctx = np.asarray(ctx if ctx is not None else np.full(B, T), np.int32)
     q = synth.normal(497, 0, (B, Nh, 576), "bf16")
     kf = synth.as_f32(synth.normal(497, 1, (B, T, 1, 576), "bf16"), "bf16").copy()
@@ -227,9 +232,9 @@ def test_mla_decode_score_growth_beyond_reference(B, T, ctx, rope):
 
 
 @pytest.mark.parametrize("mla,B,Nh", [(False, 3, 8), (False, 600, 8), (True, 3, 64), (True, 256, 64), (True, 3, 32),
-                                     (True, 256, 32)],
+                                     (True, 256, 32), (True, 3, 128), (True, 256, 128)],
                          ids=["gqa-split", "gqa-one-chunk", "mla64-split", "mla64-one-chunk", "mla32-split",
-                              "mla32-one-chunk"])
+                              "mla32-one-chunk", "mla128-split", "mla128-one-chunk"])
 def test_decode_empty_context_gives_zero_row(mla, B, Nh):
     """A context of 0 keys (a precondition violation the kernels clamp) gives an all-zero output row,
     whether or not the call splits the context (single chunk: no merge follows); the other rows are
@@ -255,15 +260,15 @@ def test_decode_empty_context_gives_zero_row(mla, B, Nh):
     assert max_abs(got[keep], want) <= BF16_TOL
 
 
-@pytest.mark.parametrize("mla", [False, True], ids=["gqa", "mla"])
-def test_decode_padded_cache_rows(mla):
+@pytest.mark.parametrize("mla,mla_heads", [(False, 0), (True, 64), (True, 128)], ids=["gqa", "mla64", "mla128"])
+def test_decode_padded_cache_rows(mla, mla_heads):
     """Cache rows with a pitch larger than the head dim (the binding passes the stride as the row
     pitch); the padding holds NaN, so reading it would show in the output."""
     import causal_head_attention_gqa_amd as attn
     torch = __import__("torch")
     B, T = 3, 200
     ctx = np.array([200, 37, 129], np.int32)
-    Nh, Nkv, D, pitch = (64, 1, 576, 640) if mla else (16, 4, 128, 136)
+    Nh, Nkv, D, pitch = (mla_heads, 1, 576, 640) if mla else (16, 4, 128, 136)
     q = synth.normal(540 + D, 0, (B, Nh, D), "bf16")
     kc = synth.normal(540 + D, 1, (B, T, Nkv, D), "bf16")
     vc = None if mla else synth.normal(540 + D, 2, (B, T, Nkv, D), "bf16")

@@ -1,5 +1,6 @@
-"""Host-side model of the MLA-absorbed decode kernel's tile addressing for head counts that are
-multiples of 64 (pairs of waves sharing 32 heads; no GPU).
+"""Host-side model of the MLA-absorbed decode kernels' tile addressing for head counts that are
+multiples of 64 (pairs of waves sharing 32 heads) and 128 (the wide kernel: 64 heads per pair of
+waves, all heads of a row in one work-group); no GPU.
 
 The formulas below restate, for every lane of the four waves, the index arithmetic of the pair
 kernel in decode_mla.hip: the 16-byte chunk swizzle of the 576-dim cache rows, the direct-to-LDS
@@ -12,7 +13,10 @@ that the K-slot order of the P operand (taken from the score accumulator layout)
 operand's, and that the reads are free of LDS bank conflicts under the gfx950 bank model the
 kernels are tuned with (128-bit reads in four passes of 16 lanes selected by lane bit 5 and the
 parity of lane bits 2-4; 64-bit reads in two passes of 32 lanes; a conflict is two lanes of a
-pass on different 16-byte / 8-byte units of the same bank group).
+pass on different 16-byte / 8-byte units of the same bank group). For the wide kernel: its
+work-group id map (every (sequence, chunk, head group) once, all of a sequence on one XCD), the
+scalar-base load offsets with the clamp of the chunk's last tile, the K reads over all 576 dims,
+and the LDS staging of its output (round trip and bank conflicts).
 """
 import numpy as np
 import pytest
@@ -176,3 +180,106 @@ def test_exchange_buffer_layout():
                     assert base + i not in seen
                     seen.add(base + i)
     assert seen == set(range(WAVES * 4 * 64 * 4))
+
+
+# ---- the 128-heads-per-work-group kernel (head counts that are multiples of 128, no RoPE) ----
+
+def wide_id_map(B, nsplit, n_hg):
+    """Work-group id -> (sequence, chunk, head group) or None, as the wide kernel computes it."""
+    n_wg = 8 * ((B + 7) // 8) * nsplit * n_hg
+    out = []
+    for i in range(n_wg):
+        kx = i // 8
+        hg, k2 = kx % n_hg, kx // n_hg
+        b, s = i % 8 + 8 * (k2 // nsplit), k2 % nsplit
+        out.append(None if b >= B else (b, s, hg))
+    return out
+
+
+@pytest.mark.parametrize("B,nsplit,n_hg", [(1, 1, 1), (3, 8, 1), (8, 8, 1), (9, 3, 2), (32, 8, 1), (33, 5, 2),
+                                           (256, 1, 1)])
+def test_wide_grid_covers_every_unit_once_on_one_xcd(B, nsplit, n_hg):
+    m = wide_id_map(B, nsplit, n_hg)
+    units = [u for u in m if u is not None]
+    assert sorted(units) == [(b, s, g) for b in range(B) for s in range(nsplit) for g in range(n_hg)]
+    # every chunk and head group of a sequence runs on the XCD of id % 8 == b % 8
+    for i, u in enumerate(m):
+        if u is not None:
+            assert i % 8 == u[0] % 8
+
+
+def wide_slot_offsets(w, lane, ldk):
+    """Per slot u: (tile row, logical chunk, byte offset of the full-tile load) of wave w's lane."""
+    out = []
+    for u in range(SPW):
+        ob = (w * SPW + u) * 1024 + 16 * lane
+        row, pc = ob // (DQ * 2), (ob % (DQ * 2)) // 16
+        lc = pc ^ key(row)
+        out.append((row, lc, 2 * (row * ldk + lc * 8)))
+    return out
+
+
+@pytest.mark.parametrize("ldk", [576, 640, 4096])
+@pytest.mark.parametrize("lim", [31, 30, 17, 0])
+def test_wide_scalar_base_offsets_clamp_rows(ldk, lim):
+    """Full tiles: base + loff; the chunk's last tile (last valid row lim < 31): rows past lim read
+    row lim, i.e. loff - 2(row - lim) ldk. Every byte offset is the pointer form's, inside the
+    tile's valid rows, and fits the 32-bit offset operand."""
+    for w in range(WAVES):
+        for lane in range(64):
+            for row, lc, off in wide_slot_offsets(w, lane, ldk):
+                assert 0 <= lc < DQ // 8
+                got = off if row <= lim else off - 2 * (row - lim) * ldk
+                want = 2 * (min(row, lim) * ldk + lc * 8)
+                assert got == want
+                assert 0 <= got and got + 16 <= 2 * (lim * ldk + DQ) and got < 2 ** 31
+
+
+def test_wide_k_operand_reads_all_576_dims():
+    """K operand of k-step kk (0..35), the whole row of the own heads: row col, dims 16kk + 8hf."""
+    tile, lds = logical_tile()
+    for kk in range(36):
+        for lane in range(64):
+            col, hf = lane & 31, lane >> 5
+            off = col * DQ + (((2 * (kk & 3) + hf) ^ key(col)) << 3) + 64 * (kk >> 2)
+            assert 0 <= off and off + 8 <= TILE
+            assert list(lds[off:off + 8]) == list(tile[col, 16 * kk + 8 * hf:16 * kk + 8 * hf + 8]), (kk, lane)
+
+
+def test_wide_output_staging_round_trip_and_banks():
+    """The output of a wave (64 rows x 256 dims, bf16) is written to LDS by 64-bit stores (lane
+    (col, hf) of group g: row 32g + col, chunk 4db + e, half hf) at chunk c ^ (row & 31), half
+    hf ^ bit 4 of the row, then read back by 128-bit loads (lane: row 2i + hf, chunk col) and the
+    halves swapped back: every element lands once and comes back where the stores expect it, and
+    both access patterns are free of bank conflicts."""
+    lds = {}
+    for g in range(2):
+        for db in range(8):
+            for e in range(4):
+                addrs = []
+                for lane in range(64):
+                    col, hf = lane & 31, lane >> 5
+                    hl, c = 32 * g + col, 4 * db + e
+                    a = hl * 256 + ((c ^ (hl & 31)) << 3) + ((hf ^ ((hl >> 4) & 1)) << 2)
+                    for i in range(4):
+                        assert a + i not in lds
+                        lds[a + i] = (hl, 8 * c + 4 * hf + i)  # (row, dim) of the value
+                    addrs.append(2 * a)
+                for half in range(2):  # 64-bit accesses: two passes of 32 lanes
+                    assert _pass_conflicts(addrs[32 * half:32 * half + 32], 8, 32) == 0
+    assert sorted(lds) == list(range(64 * 256))
+    for i in range(32):
+        addrs = []
+        for lane in range(64):
+            col, hf = lane & 31, lane >> 5
+            hl = 2 * i + hf
+            a = hl * 256 + ((col ^ (hl & 31)) << 3)
+            v = [lds[a + k] for k in range(8)]
+            if (hl >> 4) & 1:
+                v = v[4:] + v[:4]
+            assert v == [(hl, 8 * col + k) for k in range(8)]
+            addrs.append(2 * a)
+        for b5 in range(2):
+            for par in range(2):
+                lanes = [l for l in range(64) if (l >> 5) == b5 and bin((l >> 2) & 7).count("1") % 2 == par]
+                assert _pass_conflicts([addrs[l] for l in lanes], 16, 16) == 0
