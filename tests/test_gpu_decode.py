@@ -68,26 +68,29 @@ def test_decode_gqa_small(case):
     assert max_abs(got, want) <= BF16_TOL
 
 
-def test_decode_contexts_at_chunk_edges():
-    """64 sequences x 8 KV heads: the plan splits contexts into 1024-token chunks; contexts of 1, at,
-    just below and just above the chunk edges (one key into a new chunk) against the oracle."""
-    B, Nh, Nkv, D, T = 64, 8, 8, 64, 2049
-    edges = [1, 2, 1023, 1024, 1025, 2047, 2048, 2049]
+@pytest.mark.parametrize("D", [64, 128])
+def test_decode_contexts_at_chunk_edges(D):
+    """64 sequences x 8 KV heads (Dh 64 and 128): the plan splits contexts into 1024-token chunks;
+    contexts of 1, at, just below and just above the chunk edges (one key into a new chunk), and at
+    quarter-chunk edges, against the oracle."""
+    B, Nh, Nkv, T = 64, 8, 8, 2049
+    edges = [1, 2, 255, 256, 257, 511, 512, 513, 1023, 1024, 1025, 2047, 2048, 2049]
     ctx = np.array([edges[i % len(edges)] for i in range(B)], np.int32)
-    q = synth.normal(560, 0, (B, Nh, D), "bf16")
-    kc = synth.normal(560, 1, (B, T, Nkv, D), "bf16")
-    vc = synth.normal(560, 2, (B, T, Nkv, D), "bf16")
+    q = synth.normal(560 + D, 0, (B, Nh, D), "bf16")
+    kc = synth.normal(560 + D, 1, (B, T, Nkv, D), "bf16")
+    vc = synth.normal(560 + D, 2, (B, T, Nkv, D), "bf16")
     got = _gpu_decode(q, kc, vc, ctx)
     pick = np.arange(len(edges))  # one sequence per context length
     want = _oracle_decode(q[pick], kc[pick], vc[pick], ctx[pick])
     assert max_abs(got[pick], want) <= BF16_TOL
 
 
-def test_decode_more_than_64_sequences():
-    """130 sequences x 8 KV heads with contexts up to 1100: 1024-token chunks, so the kernel's work-item
-    order (every full chunk, then the short last chunks) spans three blocks of 64 sequences in both
-    parts; sequences from each block against the oracle."""
-    B, Nh, Nkv, D, T = 130, 8, 8, 64, 1100
+@pytest.mark.parametrize("D", [64, 128])
+def test_decode_more_than_64_sequences(D):
+    """130 sequences x 8 KV heads (Dh 64 and 128) with contexts up to 1100: 1024-token chunks, so the
+    kernel's work-item order (every full chunk, then the short last chunks) spans three blocks of 64
+    sequences in both parts; sequences from each block against the oracle."""
+    B, Nh, Nkv, T = 130, 8, 8, 1100
     rng = np.random.default_rng(575)
     ctx = rng.integers(1, T, B, endpoint=True).astype(np.int32)
     ctx[[5, 70, 129]] = [1024, 1100, 1025]
@@ -125,8 +128,9 @@ def test_decode_workspace_needs_no_clearing():
         assert max_abs(got, _oracle_decode(q, kc, vc, ctx)) <= BF16_TOL, f"call {i}"
 
 
-def test_decode_never_reads_beyond_context():
-    B, Nh, Nkv, D, T = 3, 8, 2, 128, 700
+@pytest.mark.parametrize("Nkv", [2, 4])
+def test_decode_never_reads_beyond_context(Nkv):
+    B, Nh, D, T = 3, 8, 128, 700
     ctx = np.array([5, 333, 700], np.int32)
     q = synth.normal(450, 0, (B, Nh, D), "bf16")
     kc = synth.normal(450, 1, (B, T, Nkv, D), "bf16")
@@ -231,10 +235,10 @@ def test_mla_decode_score_growth_beyond_reference(B, T, ctx, rope, Nh):
     assert max_abs(got, want) <= BF16_TOL
 
 
-@pytest.mark.parametrize("mla,B,Nh", [(False, 3, 8), (False, 600, 8), (True, 3, 64), (True, 256, 64), (True, 3, 32),
-                                     (True, 256, 32), (True, 3, 128), (True, 256, 128)],
-                         ids=["gqa-split", "gqa-one-chunk", "mla64-split", "mla64-one-chunk", "mla32-split",
-                              "mla32-one-chunk", "mla128-split", "mla128-one-chunk"])
+@pytest.mark.parametrize("mla,B,Nh", [(False, 3, 8), (False, 600, 8), (False, 3, 16), (False, 600, 32), (True, 3, 64),
+                                     (True, 256, 64), (True, 3, 32), (True, 256, 32), (True, 3, 128), (True, 256, 128)],
+                         ids=["gqa-split", "gqa-one-chunk", "gqa4-split", "gqa4-one-chunk", "mla64-split",
+                              "mla64-one-chunk", "mla32-split", "mla32-one-chunk", "mla128-split", "mla128-one-chunk"])
 def test_decode_empty_context_gives_zero_row(mla, B, Nh):
     """A context of 0 keys (a precondition violation the kernels clamp) gives an all-zero output row,
     whether or not the call splits the context (single chunk: no merge follows); the other rows are
@@ -249,9 +253,10 @@ def test_decode_empty_context_gives_zero_row(mla, B, Nh):
         kc = synth.normal(wid, 1, (B, T, 1, 576), "bf16")
         vc, kw = None, dict(scale=1.0 / math.sqrt(192), mla=True)
     else:
+        Nkv = Nh // 4  # 2, 4 or 8 KV heads of 4 query heads each
         q = synth.normal(wid, 0, (B, Nh, 128), "bf16")
-        kc = synth.normal(wid, 1, (B, T, 2, 128), "bf16")
-        vc, kw = synth.normal(wid, 2, (B, T, 2, 128), "bf16"), {}
+        kc = synth.normal(wid, 1, (B, T, Nkv, 128), "bf16")
+        vc, kw = synth.normal(wid, 2, (B, T, Nkv, 128), "bf16"), {}
     got = _gpu_decode(q, kc, vc, ctx, **kw)
     empty = ctx == 0
     assert np.all(got[empty] == 0.0)
