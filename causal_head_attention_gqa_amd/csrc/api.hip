@@ -356,6 +356,7 @@ size_t attn_decode_workspace_bytes(int B, int Nh, int Nkv, int Dqk, int Dv, int 
   if (B <= 0 || Nh <= 0 || Nkv <= 0 || Dv <= 0 || max_ctx <= 0 || dtype != ATTN_BF16) return 0;
   if (Nh % Nkv != 0) return 0;
   const DecodePlan p = decode_plan(B, Nh, Nkv, Dqk, Dv, max_ctx);
+  if (p.mla && p.nsplit == 1) return 0;  // one chunk per sequence: the kernel writes the output itself
   const size_t slots = (size_t)B * (size_t)Nh * (size_t)p.nsplit;
   return align_up(slots * (size_t)Dv * sizeof(uint16_t)) + align_up(slots * 2 * sizeof(float));
 }
@@ -383,18 +384,20 @@ int attn_decode(const void* q, const void* kcache, const void* vcache, const int
       (reinterpret_cast<uintptr_t>(ctx_lens) & 3u))
     return ATTN_ERR_INVALID;
   const size_t need = attn_decode_workspace_bytes(B, Nh, Nkv, Dqk, Dv, max_ctx, dtype);
-  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return ATTN_ERR_WORKSPACE;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))) return ATTN_ERR_WORKSPACE;
 
   const DecodePlan p = decode_plan(B, Nh, Nkv, Dqk, Dv, max_ctx);
-  const size_t slots = (size_t)B * (size_t)Nh * (size_t)p.nsplit;
+  const size_t slots = need > 0 ? (size_t)B * (size_t)Nh * (size_t)p.nsplit : 0;
   DecodeArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.kc = static_cast<const uint16_t*>(kcache);
   a.vc = static_cast<const uint16_t*>(vcache);
   a.ctx_lens = ctx_lens;
   a.out = static_cast<uint16_t*>(out);
-  a.part_o = static_cast<uint16_t*>(workspace);
-  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(slots * (size_t)Dv * sizeof(uint16_t)));
+  // no partials when the workspace is not needed (the kernels then never touch these pointers)
+  a.part_o = need > 0 ? static_cast<uint16_t*>(workspace) : nullptr;
+  a.part_ml = need > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + align_up(slots * (size_t)Dv * sizeof(uint16_t)))
+                       : nullptr;
   a.B = B;
   a.Nh = Nh;
   a.Nkv = Nkv;

@@ -240,7 +240,7 @@ def decode(q, kcache, vcache, ctx_lens, *, scale: float | None = None, rope_thet
     if out is None:
         out = torch.empty((B, Nh, Dv), dtype=q.dtype, device=q.device)
     _check_out(out, (B, Nh, Dv), q.dtype, q.device)
-    ws_ptr, ws_len = _workspace(workspace, max(decode_workspace_bytes(B, Nh, Nkv, Dqk, Dv, max_ctx, dt), 1),
+    ws_ptr, ws_len = _workspace(workspace, decode_workspace_bytes(B, Nh, Nkv, Dqk, Dv, max_ctx, dt),
                                 q.device)
     st = load().attn_decode(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), ctx_lens.data_ptr(), out.data_ptr(),
                             B, Nh, Nkv, Dqk, Dv, max_ctx, kcache.stride(2), vcache.stride(2), float(rope_theta),

@@ -183,7 +183,9 @@ int attn_kv_append(const void* k_new, const void* v_new, void* kcache, void* vca
  * Supported (ATTN_BF16 only): Dqk == Dv in {64, 128} with Nh % Nkv == 0 and a group size
  *   G = Nh / Nkv of at most 16 or a multiple of 16 (query heads are processed 16 at a time);
  *   and the MLA form Dqk = 576, Dv = 512, Nkv = 1, vcache == kcache, ldv == ldk, Nh % 16 == 0.
- * workspace: at least attn_decode_workspace_bytes(...) bytes (split-KV partial results).
+ * workspace: at least attn_decode_workspace_bytes(...) bytes (split-KV partial results); may be
+ *   NULL when that figure is 0 (the MLA form when every sequence fits one chunk: the kernel then
+ *   writes the output directly).
  * ------------------------------------------------------------------------------------------ */
 size_t attn_decode_workspace_bytes(int B, int Nh, int Nkv, int Dqk, int Dv, int max_ctx, int dtype);
 

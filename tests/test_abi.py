@@ -107,6 +107,10 @@ def test_workspace_queries():
     assert lib.prefill_workspace_bytes(4, 8192, 8, 128, 5e5, 1) == 8192 * 64 * 8 + 4 * 8192 * 8 * 128 * 2
     ws = lib.decode_workspace_bytes(64, 32, 8, 128, 128, 8192, 1)
     assert ws > 0 and ws % 256 == 0
+    # MLA: split partials (bf16 rows + fp32 max/sum) for 8 chunks of 512 tokens at B = 32 ...
+    assert lib.decode_workspace_bytes(32, 128, 1, 576, 512, 4096, 1) == 32 * 128 * 8 * 512 * 2 + 32 * 128 * 8 * 2 * 4
+    # ... none once every sequence is one chunk (256 sequences fill the chip)
+    assert lib.decode_workspace_bytes(256, 128, 1, 576, 512, 64, 1) == 0
 
 
 def test_prefill_cached_argument_errors():

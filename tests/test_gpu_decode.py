@@ -195,16 +195,31 @@ def test_mla_decode_head_pairs(case):
     assert max_abs(got, want) <= BF16_TOL
 
 
-def test_mla_decode_single_chunk():
+@pytest.mark.parametrize("Nh", [64, 128])
+def test_mla_decode_single_chunk(Nh):
     """Enough (sequence, head group) units that each sequence is one chunk: the kernel writes the
-    normalised output itself (no split partials, no merge)."""
-    B, Nh, T = 256, 64, 64
+    normalised output itself (no split partials, no merge), so the call needs no workspace: the C
+    entry point is called with a NULL one and matches the oracle."""
+    import ctypes
+    import causal_head_attention_gqa_amd as attn
+    from causal_head_attention_gqa_amd import lib
+    torch = __import__("torch")
+    B, T = 256, 64
     rng = np.random.default_rng(490)
     ctx = rng.integers(1, T, B, endpoint=True).astype(np.int32)
     q = synth.normal(490, 0, (B, Nh, 576), "bf16")
     kc = synth.normal(490, 1, (B, T, 1, 576), "bf16")
     scale = 1.0 / math.sqrt(192)
-    got = _gpu_decode(q, kc, None, ctx, scale=scale, mla=True)
+    assert attn.decode_workspace_bytes(B, Nh, 1, 576, 512, T, attn.ATTN_BF16) == 0
+    qd, kd = to_dev(q, "bf16"), to_dev(kc, "bf16")
+    cd = torch.as_tensor(ctx, device="cuda")
+    out = torch.full((B, Nh, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+    st = attn.load().attn_decode(qd.data_ptr(), kd.data_ptr(), kd.data_ptr(), cd.data_ptr(), out.data_ptr(), B, Nh, 1,
+                                 576, 512, T, 576, 576, ctypes.c_float(0.0), ctypes.c_float(scale), attn.ATTN_BF16,
+                                 None, 0, lib._stream_ptr(qd.device))
+    assert st == 0
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
     want = _oracle_decode(q, kc, None, ctx, scale=scale, mla=True)
     assert max_abs(got, want) <= BF16_TOL
 

@@ -53,9 +53,9 @@ def test_noalloc_refuses_requests_beyond_the_scratch():
     lib = attn.load()
     cap = attn.decode_noalloc_max_bytes()
     assert cap == 64 << 20
-    # 4096 sequences x 128 MLA heads x 4 chunks of fp32 partials: far beyond 64 MiB
-    need = attn.decode_workspace_bytes(4096, 128, 1, 576, 512, 4096, attn.ATTN_BF16)
+    # 4096 sequences x 32 heads x 8 chunks of 1024 tokens of bf16 partials: far beyond 64 MiB
+    need = attn.decode_workspace_bytes(4096, 32, 8, 128, 128, 8192, attn.ATTN_BF16)
     assert need > cap
-    st = lib.attn_decode_noalloc(16, 16, 16, 16, 16, 4096, 128, 1, 576, 512, 4096, 576, 576, 0.0, 0.0,
+    st = lib.attn_decode_noalloc(16, 16, 16, 16, 16, 4096, 32, 8, 128, 128, 8192, 128, 128, 0.0, 0.0,
                                  attn.ATTN_BF16, None)
     assert st == 3  # ATTN_ERR_WORKSPACE, returned before any launch
