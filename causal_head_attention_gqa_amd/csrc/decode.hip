@@ -286,7 +286,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
       acc = fmaf(wgt, mo(v)[hl * (D + 4) + d], acc);
       l = fmaf(wgt, mm(v)[hl * 2 + 1], l);
     }
-    const long long slot = ((long long)b * a.Nh + h0 + hl) * a.nsplit + s;
+    const long long slot = part_slot(a, b, h0 + hl, s);
     a.part_o[slot * D + d] = f32_to_bf16(acc / l);  // every written chunk holds a key: l > 0
     if (d == 0) {
       a.part_ml[slot * 2 + 0] = mx;
@@ -312,7 +312,8 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(DecodeArgs a) {
   const int b = wid / a.Nh;
   const int ctx = min(max(a.ctx_lens[b], 0), a.max_ctx);
   const int ns = (ctx + a.chunk - 1) / a.chunk;
-  const long long slot0 = (long long)wid * a.nsplit;
+  const int h = wid % a.Nh;
+  const long long slot0 = part_slot(a, b, h, 0);  // chunk s: slot0 + s * Nh
   const int nvec = a.Dv / 4;                   // 4-column groups per row
   const int nc = nvec < 64 ? nvec : 64;        // lanes per phase
   const int spl = 64 / nc;                     // chunk phases
@@ -326,7 +327,7 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(DecodeArgs a) {
   const uint2* po = reinterpret_cast<const uint2*>(a.part_o + slot0 * a.Dv);
   // the reference max over all chunks (lane s holds chunk s, s + 64, ...)
   float mx = -INFINITY;
-  for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, ml[2 * s]);
+  for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, ml[2 * (long long)s * a.Nh]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   auto fma4 = [](float w, uint2 v, float4& acc) {
@@ -347,9 +348,9 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(DecodeArgs a) {
     for (int u = 0; u < kU; ++u) {
       const int s = s0 + u * spl;
       const bool in = s < ns;
-      mls[u] = in ? *reinterpret_cast<const float2*>(ml + 2 * s) : make_float2(-INFINITY, 0.f);
+      mls[u] = in ? *reinterpret_cast<const float2*>(ml + 2 * (long long)s * a.Nh) : make_float2(-INFINITY, 0.f);
 #pragma unroll
-      for (int k = 0; k < KC; ++k) v[u][k] = in ? po[(long long)s * nvec + c0 + 64 * k] : make_uint2(0u, 0u);
+      for (int k = 0; k < KC; ++k) v[u][k] = in ? po[(long long)s * a.Nh * nvec + c0 + 64 * k] : make_uint2(0u, 0u);
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) {

@@ -290,7 +290,7 @@ __global__ __launch_bounds__(NW * 64, (NW >= 8 ? 2 : 1)) void decode_mla_kernel(
           make_uint2(pack_bf16x2(o[db][0] * inv, o[db][1] * inv), pack_bf16x2(o[db][2] * inv, o[db][3] * inv));
     return;
   }
-  const long long slot = ((long long)b * a.Nh + h) * a.nsplit + s;
+  const long long slot = part_slot(a, b, h, s);
   uint16_t* po = a.part_o + slot * DV + rg * 4;
   const float inv = 1.f / ltot;  // the chunk's output, normalised by its own sum, in bf16
 #pragma unroll
@@ -552,7 +552,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_pair_kernel(DecodeA
 
   // ---- result: lane holds head h, dims 256r + 32db + 8g + 4hf + i in o[db][4g + i] ----
   const float ltot = pair_sum32(lsum);
-  const long long slot = ((long long)b * a.Nh + h) * a.nsplit + s;
+  const long long slot = part_slot(a, b, h, s);
   const uint64_t bal = __ballot(ovf);
   uint64_t bad = (bal | (bal >> 32)) & 0xffffffffull;  // heads flagged by either of their lanes
   if (!((bad >> col) & 1)) {
@@ -652,7 +652,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_pair_kernel(DecodeA
       *reinterpret_cast<uint2*>(a.out + ((long long)b * a.Nh + hc) * DV + r * (DV / 2) + 4 * lane) =
           make_uint2(pack_bf16x2(o4[0] * inv, o4[1] * inv), pack_bf16x2(o4[2] * inv, o4[3] * inv));
     } else {
-      const long long sl = ((long long)b * a.Nh + hc) * a.nsplit + s;
+      const long long sl = part_slot(a, b, hc, s);
       const float inv = 1.f / lr;
       *reinterpret_cast<uint2*>(a.part_o + sl * DV + r * (DV / 2) + 4 * lane) =
           make_uint2(pack_bf16x2(o4[0] * inv, o4[1] * inv), pack_bf16x2(o4[2] * inv, o4[3] * inv));
@@ -994,11 +994,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_wide_kernel(DecodeA
     if ((hl >> 4) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
     if ((bad_g[hl >> 5] >> (hl & 31)) & 1) continue;  // recomputed below
     const long long row = (long long)b * a.Nh + hp + hl;
-    uint16_t* op = (a.nsplit == 1 ? a.out + row * DV : a.part_o + (row * a.nsplit + s) * DV) + r * (DV / 2) + col * 8;
+    uint16_t* op = (a.nsplit == 1 ? a.out + row * DV : a.part_o + part_slot(a, b, hp + hl, s) * DV) + r * (DV / 2) + col * 8;
     *reinterpret_cast<uint4*>(op) = v;
   }
   if (a.nsplit > 1 && hf == 0 && !((bad_g[r] >> col) & 1)) {
-    const long long slot = ((long long)b * a.Nh + hp + 32 * r + col) * a.nsplit + s;
+    const long long slot = part_slot(a, b, hp + 32 * r + col, s);
     a.part_ml[slot * 2 + 0] = m;
     a.part_ml[slot * 2 + 1] = xml[(w * 2 + 1) * 32 + col];
   }
@@ -1057,7 +1057,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_wide_kernel(DecodeA
       }
     }
     const float inv = 1.f / lr;
-    const long long sl = ((long long)b * a.Nh + hc) * a.nsplit + s;
+    const long long sl = part_slot(a, b, hc, s);
     uint16_t* op = (a.nsplit == 1 ? a.out + ((long long)b * a.Nh + hc) * DV : a.part_o + sl * DV) + r * (DV / 2) + 4 * lane;
     *reinterpret_cast<uint2*>(op) = make_uint2(pack_bf16x2(o4[0] * inv, o4[1] * inv), pack_bf16x2(o4[2] * inv, o4[3] * inv));
     if (a.nsplit > 1 && (c >> 5) == r && lane == 0) {

@@ -71,14 +71,19 @@ struct DecodeArgs {
   const uint16_t* vc;
   const int* ctx_lens;
   uint16_t* out;
-  uint16_t* part_o;  // [B][Nh][nsplit][Dv] bf16: the chunk's output normalised by its own sum
-  float* part_ml;    // [B][Nh][nsplit][2]  fp32 (reference max in log2 units, sum)
+  uint16_t* part_o;  // [B][nsplit][Nh][Dv] bf16: the chunk's output normalised by its own sum
+  float* part_ml;    // [B][nsplit][Nh][2]  fp32 (reference max in log2 units, sum)
   int B, Nh, Nkv, Dqk, Dv, max_ctx;
   long long ldk, ldv;
   float scale_log2;
   double rope_theta;  // <= 0: none
   int chunk, nsplit;
 };
+// Partial slot of (sequence b, query head h, chunk s): chunk-major within a sequence, so that the
+// heads of one chunk are adjacent and a work-group's partials form one contiguous block.
+__device__ __forceinline__ long long part_slot(const DecodeArgs& a, int b, int h, int s) {
+  return ((long long)b * a.nsplit + s) * a.Nh + h;
+}
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t st);
 int mla_waves_per_group(int Nh);  // waves (16 heads each) per MLA work-group
