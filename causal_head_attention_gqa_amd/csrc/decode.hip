@@ -299,12 +299,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 // out = sum 2^(m_s - m*) l_s (o_s / l_s) / l* ("Transformer 架构完全深度解析" §十三: the running max
 // and sum recurrences applied to whole chunks). Each chunk left its output normalised by its own
 // sum, o_s / l_s, in bf16 (half the bytes of fp32; the merge is a convex combination of them, so
-// their rounding stays within one bf16 step of the output). One wave per (b, h); a lane owns
-// 4-column groups c0 + 64k of the output and, when a row has fewer than 64 such groups, one phase
-// of the chunks (chunks ph, ph + SPL, ...); every load of up to 8 chunks per phase is issued before
-// the first is used, so a row costs one round trip to memory, and the phases are summed across
-// lanes at the end.
-template <int KC>
+// their rounding stays within one bf16 step of the output). One wave per (b, h); a lane owns one
+// 8-column group (16 bytes) c0 of the output and, when a row has fewer than 64 such groups, one
+// phase of the chunks (chunks ph, ph + SPL, ...); every load of up to 8 chunks per phase is issued
+// before the first is used (non-temporal: each partial is read once), so a row costs one round trip
+// to memory, and the phases are summed across lanes at the end.
 __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(DecodeArgs a) {
   const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -314,71 +313,59 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(DecodeArgs a) {
   const int ns = (ctx + a.chunk - 1) / a.chunk;
   const int h = wid % a.Nh;
   const long long slot0 = part_slot(a, b, h, 0);  // chunk s: slot0 + s * Nh
-  const int nvec = a.Dv / 4;                   // 4-column groups per row
-  const int nc = nvec < 64 ? nvec : 64;        // lanes per phase
-  const int spl = 64 / nc;                     // chunk phases
-  const int c0 = lane % nc, ph = lane / nc;
+  const int nvec = a.Dv / 8;                   // 8-column groups per row (a divisor of 64)
+  const int spl = 64 / nvec;                   // chunk phases
+  const int c0 = lane % nvec, ph = lane / nvec;
   uint16_t* op = a.out + (long long)wid * a.Dv;
   if (ns == 0) {
-    for (int c = lane; c < nvec; c += 64) *reinterpret_cast<uint2*>(op + 4 * c) = make_uint2(0u, 0u);
+    if (ph == 0) *reinterpret_cast<uint4*>(op + 8 * c0) = make_uint4(0u, 0u, 0u, 0u);
     return;
   }
   const float* ml = a.part_ml + slot0 * 2;
-  const uint2* po = reinterpret_cast<const uint2*>(a.part_o + slot0 * a.Dv);
+  const uint16_t* po = a.part_o + slot0 * a.Dv;
   // the reference max over all chunks (lane s holds chunk s, s + 64, ...)
   float mx = -INFINITY;
   for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, ml[2 * (long long)s * a.Nh]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  auto fma4 = [](float w, uint2 v, float4& acc) {
-    acc.x = fmaf(w, bf16lo(v.x), acc.x);
-    acc.y = fmaf(w, bf16hi(v.x), acc.y);
-    acc.z = fmaf(w, bf16lo(v.y), acc.z);
-    acc.w = fmaf(w, bf16hi(v.y), acc.w);
-  };
-  float4 acc[KC];
+  float acc[8];
 #pragma unroll
-  for (int k = 0; k < KC; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   float l = 0.f;  // sum of the weights of this lane's phase (summed over the phases below)
   constexpr int kU = 8;  // chunks per phase in flight
   for (int s0 = ph; s0 < ns; s0 += kU * spl) {
-    uint2 v[kU][KC];
+    U4 v[kU];
     float2 mls[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int s = s0 + u * spl;
       const bool in = s < ns;
       mls[u] = in ? *reinterpret_cast<const float2*>(ml + 2 * (long long)s * a.Nh) : make_float2(-INFINITY, 0.f);
-#pragma unroll
-      for (int k = 0; k < KC; ++k) v[u][k] = in ? po[(long long)s * a.Nh * nvec + c0 + 64 * k] : make_uint2(0u, 0u);
+      v[u] = in ? ldg16_nt(po + ((long long)s * a.Nh * nvec + c0) * 8) : U4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const float wgt = mls[u].x == -INFINITY ? 0.f : fast_exp2(mls[u].x - mx) * mls[u].y;
       l += wgt;
+      const uint32_t wv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
-      for (int k = 0; k < KC; ++k) fma4(wgt, v[u][k], acc[k]);
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] = fmaf(wgt, bf16lo(wv[e]), acc[2 * e]);
+        acc[2 * e + 1] = fmaf(wgt, bf16hi(wv[e]), acc[2 * e + 1]);
+      }
     }
   }
-  // sum the phases (lanes c0, c0 + nc, ...) and the sums of all chunks
-  for (int off = nc; off < 64; off <<= 1) {
+  // sum the phases (lanes c0, c0 + nvec, ...) and the sums of all chunks
+  for (int off = nvec; off < 64; off <<= 1) {
 #pragma unroll
-    for (int k = 0; k < KC; ++k) {
-      acc[k].x += __shfl_xor(acc[k].x, off);
-      acc[k].y += __shfl_xor(acc[k].y, off);
-      acc[k].z += __shfl_xor(acc[k].z, off);
-      acc[k].w += __shfl_xor(acc[k].w, off);
-    }
+    for (int i = 0; i < 8; ++i) acc[i] += __shfl_xor(acc[i], off);
     l += __shfl_xor(l, off);
   }
   const float inv = 1.f / l;
-  if (ph == 0) {
-#pragma unroll
-    for (int k = 0; k < KC; ++k)
-      if (c0 + 64 * k < nvec)
-        *reinterpret_cast<uint2*>(op + 4 * (c0 + 64 * k)) =
-            make_uint2(pack_bf16x2(acc[k].x * inv, acc[k].y * inv), pack_bf16x2(acc[k].z * inv, acc[k].w * inv));
-  }
+  if (ph == 0)
+    *reinterpret_cast<uint4*>(op + 8 * c0) =
+        make_uint4(pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                   pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv));
 }
 
 constexpr int kDecodeNB = 2;  // LDS ring stages per wave (2: two work-groups fit a CU)
@@ -408,13 +395,8 @@ hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t st) {
 hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t st) {
   const long long waves = (long long)a.B * a.Nh;
   if (waves == 0) return hipSuccess;
-  if (a.Dv % 4 != 0 || a.Dv > 512 || (a.Dv / 4 < 64 && 64 % (a.Dv / 4) != 0) || (a.Dv / 4 > 64 && a.Dv % 256 != 0))
-    return hipErrorInvalidValue;
-  const dim3 grid((unsigned)((waves + 3) / 4));
-  if (a.Dv <= 256)
-    decode_reduce_kernel<1><<<grid, dim3(kThreads), 0, st>>>(a);
-  else
-    decode_reduce_kernel<2><<<grid, dim3(kThreads), 0, st>>>(a);
+  if (a.Dv % 8 != 0 || a.Dv > 512 || 64 % (a.Dv / 8) != 0) return hipErrorInvalidValue;
+  decode_reduce_kernel<<<dim3((unsigned)((waves + 3) / 4)), dim3(kThreads), 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -680,23 +680,23 @@ hipError_t launch(const DecodeArgs& a, hipStream_t st) {
 // ---- 64 heads per wave pair, all 128 heads of a row in one work-group (head counts that are
 // multiples of 128, no in-kernel RoPE) ----
 //
-// The pair kernel above reads one 1 KiB operand from LDS per 32x32x16 product, which makes the LDS
-// read rate, not the matrix cores, its limit. Here each wave holds the query operands and the
-// accumulators of 64 heads (two 32-head groups), so every K and V operand it reads from LDS feeds
-// two products:
+// The pair kernel above reads every V operand from LDS for one 32-head product and exchanges fp32
+// partial scores. Here the accumulators of a wave cover 64 heads, so each V operand feeds two
+// products:
 //   - a work-group = 4 waves owns (sequence, 128 heads, one context chunk); waves 2p and 2p+1 share
-//     heads 64p .. 64p+63, wave 2p+r contracts dims 288r .. 288r+287 of them (36 products per
-//     tile), the partial scores of both groups are exchanged through LDS as in the pair kernel, and
-//     wave 2p+r accumulates O^T for output dims 256r .. 256r+255 of all 64 heads (32 products);
-//   - per lane: 144 query registers and 256 accumulator registers (the whole accumulator file),
-//     which fits one wave per SIMD only because nothing but the matrix products touches the
+//     heads 64p .. 64p+63. Wave 2p+r contracts all 576 dims of its own 32 heads 64p+32r .. +31
+//     (36 products per tile, 144 query registers per lane), makes their P in bf16, and swaps it with
+//     its partner through LDS; it then accumulates O^T for output dims 256r .. 256r+255 of all 64
+//     heads (32 products per tile; 256 accumulator registers, the whole accumulator file);
+//   - this fits one wave per SIMD only because nothing but the matrix products touches the
 //     accumulators inside the loop: the reference max per head is fixed at the first tile, so no
 //     rescale is ever applied to O (heads whose scores outgrow it are recomputed exactly after the
 //     loop, as in the pair kernel);
-//   - per tile and work-group the LDS carries 72 KiB of K reads, 64 KiB of transposing V reads,
-//     64 KiB of score exchange and the 36 KiB tile itself for 128 heads, against twice the K and V
-//     reads for the same heads in the pair kernel; each cached row crosses HBM once;
-//   - a 3-stage LDS ring (108 KiB) plus 32 KiB of exchange buffers;
+//   - per tile and work-group the LDS carries 144 KiB of K reads, 64 KiB of transposing V reads,
+//     8 KiB of P written and read, and the 36 KiB tile itself, for 128 heads; the pair kernel needs
+//     as many K reads, twice the V reads and 32 KiB of partial scores for the same heads, and each
+//     cached row crosses HBM once here instead of twice;
+//   - a 4-stage LDS ring (144 KiB) plus two 8 KiB P buffers;
 //   - the chunks of one sequence are dispatched to one XCD (ids of equal id % 8), so the query rows
 //     every chunk re-reads stay in that XCD's L2.
 namespace wide {
@@ -780,17 +780,34 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_wide_kernel(DecodeA
       }
     }
   };
-  // Q^T operand of k-step kk: own head hp + 32r + col, dims 16kk + 8hf .. +7. Only tile 0 loads with
-  // the query rows (all work-groups start together, so the first requests queue behind each other);
-  // tiles 1 and 2 are issued once these have landed and load during the products of tile 0.
+  // Q^T operand of k-step kk: own head hp + 32r + col, dims 16kk + 8hf .. +7. The wave's 32 query
+  // rows are 36 KiB of contiguous memory: they go through the ring first, in the byte layout of a
+  // tile (swizzled 16-byte chunks, whole rows per load instruction instead of 32-byte pieces of 32
+  // rows), and are read out with the K operand pattern. Load slot u lands in stage u & 3 at 1-KiB
+  // column 9w + (u >> 2): exactly the columns this wave's own tile loads fill later, so no other
+  // wave writes them and the tile loads may start as soon as this wave has read its rows.
   bf16x8 qreg[kKS];
-  issue_tile(0, ring[0]);
   {
-    const uint16_t* qp = a.q + ((long long)b * a.Nh + hp + 32 * r + col) * DQ + hf * 8;
+    const uint16_t* qrows = a.q + ((long long)b * a.Nh + hp + 32 * r) * DQ;  // wave-uniform
+    asm volatile("s_nop 4" ::: "memory");
 #pragma unroll
-    for (int kk = 0; kk < kKS; ++kk) qreg[kk] = as_bf16x8(ldg16(qp + kk * 16));
+    for (int u = 0; u < NSLOT; ++u) {
+      const int ob = u * 1024 + 16 * lane;
+      const int row = ob / (DQ * 2);
+      const uint32_t off = 2u * (uint32_t)(row * DQ + ((((ob % (DQ * 2)) / 16) ^ pair::key(row)) << 3));
+      load_lds16_async_sv(qrows, off, &ring[u & 3][0] + (kSPW * w + (u >> 2)) * 512);
+    }
+    retire_vmem();  // this wave's query rows have landed in its columns of the ring
+    const int qkey = pair::key(col);
+#pragma unroll
+    for (int kk = 0; kk < kKS; ++kk) {
+      const int bq = col * (DQ * 2) + 16 * (8 * (kk >> 2) + ((2 * (kk & 3) + hf) ^ qkey));
+      const int u = bq >> 10;
+      qreg[kk] = *reinterpret_cast<const bf16x8*>(&ring[u & 3][0] + (kSPW * w + (u >> 2)) * 512 + ((bq & 1023) >> 1));
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read out before the tile loads refill the columns
   }
-  retire_vmem();  // the query rows and tile 0 have landed
+  issue_tile(0, ring[0]);
   issue_tile(min(1, n_tiles - 1), ring[1]);
   issue_tile(min(2, n_tiles - 1), ring[2]);
 
@@ -834,6 +851,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_wide_kernel(DecodeA
     for (int kk = 0; kk < kKS; ++kk) {
       sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk % kKR], qreg[kk], sv, 0, 0, 0);
       if (kk + kKR < kKS) ka[kk % kKR] = kread(kk + kKR);
+      // keeps the read of k-step kk + kKR here: left alone, the scheduler moves each read down to
+      // its product and every product then waits for a full LDS round trip
+      __builtin_amdgcn_sched_barrier(0);
       if constexpr (kSpread) {
         static_assert(kKS == 4 * kSPW, "one load per four products");
         if (kk % 4 == 0) load_lds16_async_sv_nop(base, loff[kk / 4], dst + (w * kSPW + kk / 4) * 512);
@@ -867,6 +887,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_wide_kernel(DecodeA
 
   // ---- tile 0: scores, the reference max, P ----
   uint32_t pk[2][4];
+  wait_vmem_n<2 * kSPW>();  // tile 0 has landed (tiles 1 and 2 may still fly)
   barrier_only();  // every wave's part of tile 0 is in LDS
   {
     f32x16 sv = qk(ring[0], NoSpread{}, nullptr, nullptr);
@@ -885,8 +906,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_wide_kernel(DecodeA
 
   // ---- step j: P.V of tile j (P exchanged at the barrier) while the scores and P of tile j+1 are
   // made: Q.K of tile j+1 first, then its exponentials interleaved with the P.V products. One
-  // barrier per step: tile j+1 has landed in every wave, every wave's P(j) is in LDS, and every
-  // wave is done with stage (j-1) % 4, which the load of tile j+3 then refills. A load past the
+  // barrier per step: tile j+1 has landed in every wave, every wave's P(j) is in LDS (both waves of
+  // a pair read both groups' P(j) from there after Q.K), and every wave is done with stage
+  // (j-1) % 4, which the load of tile j+3 then refills. A load past the
   // last tile re-reads the last one into a stage that is never read again, so every step keeps
   // one fixed vmcnt. P goes through two LDS buffers: P(j+1) is written while P(j) may still be
   // read by the partner. ----
@@ -899,9 +921,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_wide_kernel(DecodeA
     const int jl = min(j + 3, n_tiles - 1);
     const bool spread = more && t0 + jl * TT + TT <= t1;
     if (!spread) issue_tile(jl, ring[(j + 3) & 3]);
-    uint4 pq[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) pq[ks] = *reinterpret_cast<const uint4*>(&xp[j & 1][w ^ 1][ks][lane][0]);
     f32x16 sn = f32x16{};
     if (spread) {
       sn = qk(ring[(j + 1) & 3], Spread{}, seq + (long long)(t0 + jl * TT) * ldk, ring[(j + 3) & 3]);
@@ -918,10 +937,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_wide_kernel(DecodeA
     float psum = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 pown = __builtin_bit_cast(bf16x8, U4{pk[ks][0], pk[ks][1], pk[ks][2], pk[ks][3]});
-      const bf16x8 poth = __builtin_bit_cast(bf16x8, U4{pq[ks].x, pq[ks].y, pq[ks].z, pq[ks].w});
-      const bf16x8 bop0 = r == 0 ? pown : poth;
-      const bf16x8 bop1 = r == 0 ? poth : pown;
+      // P(j) of both head groups of the pair (waves 2p and 2p+1), read back from LDS only here so
+      // that no P registers stay live across Q.K
+      const bf16x8 bop0 = *reinterpret_cast<const bf16x8*>(&xp[j & 1][w & ~1][ks][lane][0]);
+      const bf16x8 bop1 = *reinterpret_cast<const bf16x8*>(&xp[j & 1][w | 1][ks][lane][0]);
       auto vread = [&](int db) {
         const uint16_t* p = T + (16 * ks) * DQ + 32 * (db & ~1);
         const uint2 lo = lds_read_tr16(p + vb[db & 1][0]);
@@ -938,17 +957,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_wide_kernel(DecodeA
         o[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db % kVR], bop1, o[1][db], 0, 0, 0);
         if (db + kVR < kDB) va[db % kVR] = vread(db + kVR);
         if (ks == 0) pn[db >> 2][db & 3] = expo(sn, db, psum);
+        __builtin_amdgcn_sched_barrier(0);  // V reads kVR products ahead, exponentials among the products
       }
     }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pk[ks][e] = pn[ks][e];
     if (more) {
       lsum += psum;
       ovf |= !(psum <= kOvf);
-      put_p(pk, (j + 1) & 1);
     }
+    put_p(pn, (j + 1) & 1);  // also past the last tile (never read), so the exponentials stay among the products
   }
   wait_vmem();  // the re-reads must land before the work-group's LDS is released
 

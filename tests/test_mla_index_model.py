@@ -16,7 +16,8 @@ parity of lane bits 2-4; 64-bit reads in two passes of 32 lanes; a conflict is t
 pass on different 16-byte / 8-byte units of the same bank group). For the wide kernel: its
 work-group id map (every (sequence, chunk, head group) once, all of a sequence on one XCD), the
 scalar-base load offsets with the clamp of the chunk's last tile, the K reads over all 576 dims,
-and the LDS staging of its output (round trip and bank conflicts).
+the staging of its query rows through the ring, and the LDS staging of its output (round trip and
+bank conflicts).
 """
 import numpy as np
 import pytest
@@ -283,3 +284,43 @@ def test_wide_output_staging_round_trip_and_banks():
             for par in range(2):
                 lanes = [l for l in range(64) if (l >> 5) == b5 and bin((l >> 2) & 7).count("1") % 2 == par]
                 assert _pass_conflicts([addrs[l] for l in lanes], 16, 16) == 0
+
+
+def test_wide_query_staging_through_the_ring():
+    """The wide kernel's query rows: wave w's 32 rows (36 KiB, contiguous) are loaded like a tile
+    (slot u, lane i: bytes 1024u + 16i = row * 1152 + 16pc, logical chunk pc ^ key(row)) into stage
+    u & 3 at 1-KiB column 9w + (u >> 2); k-step kk is read back at the tile position of (row col,
+    chunk 2kk + hf). Every load reads inside the wave's rows, lands once inside the wave's own
+    columns (the ones its tile loads refill later, so no other wave touches them), every read
+    returns q[col][16kk + 8hf .. +7], and the reads are free of bank conflicts (the remap moves
+    whole 1-KiB slots, so the bank pattern is the K reads')."""
+    STAGE = TILE  # elements per ring stage
+    for w in range(WAVES):
+        lds = {}
+        for u in range(NSLOT):
+            for lane in range(64):
+                ob = u * 1024 + 16 * lane
+                row, pc = ob // (DQ * 2), (ob % (DQ * 2)) // 16
+                src = row * DQ + ((pc ^ key(row)) << 3)  # element offset within the wave's rows
+                assert 0 <= src and src + 8 <= 32 * DQ
+                dst = (u & 3) * STAGE + (9 * w + (u >> 2)) * 512 + lane * 8
+                assert (dst % STAGE) // (9 * 512) == w  # this wave's column of the stage
+                for k in range(8):
+                    assert dst + k not in lds
+                    lds[dst + k] = src + k
+        # the same columns are the ones wave w's tile loads fill: slots 9w .. 9w + 8 of every stage
+        cols = {(d % STAGE) // 512 for d in lds}
+        assert cols == set(range(9 * w, 9 * w + 9))
+        for kk in range(36):
+            addrs = []
+            for lane in range(64):
+                col, hf = lane & 31, lane >> 5
+                bq = col * (DQ * 2) + 16 * (8 * (kk >> 2) + ((2 * (kk & 3) + hf) ^ key(col)))
+                u = bq >> 10
+                a = (u & 3) * STAGE + (9 * w + (u >> 2)) * 512 + ((bq & 1023) >> 1)
+                assert [lds[a + k] for k in range(8)] == [col * DQ + 16 * kk + 8 * hf + k for k in range(8)]
+                addrs.append(2 * a)
+            for b5 in range(2):
+                for par in range(2):
+                    lanes = [l for l in range(64) if (l >> 5) == b5 and bin((l >> 2) & 7).count("1") % 2 == par]
+                    assert _pass_conflicts([addrs[l] for l in lanes], 16, 16) == 0
