@@ -301,50 +301,59 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 // sum, o_s / l_s, in bf16 (half the bytes of fp32; the merge is a convex combination of them, so
 // their rounding stays within one bf16 step of the output). One wave per (b, h); a lane owns one
 // 8-column group (16 bytes) c0 of the output and, when a row has fewer than 64 such groups, one
-// phase of the chunks (chunks ph, ph + SPL, ...); every load of up to 8 chunks per phase is issued
-// before the first is used (non-temporal: each partial is read once), so a row costs one round trip
-// to memory, and the phases are summed across lanes at the end.
+// phase of the chunks (chunks ph, ph + SPL, ...); the loads of up to 8 chunks per phase are issued
+// together with that of the context length (non-temporal: each partial is read once), so a row of up
+// to 8 * SPL chunks costs one round trip to memory, and the phases are summed across lanes at the end.
 __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(DecodeArgs a) {
   const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (wid >= a.B * a.Nh) return;
   const int b = wid / a.Nh;
-  const int ctx = min(max(a.ctx_lens[b], 0), a.max_ctx);
-  const int ns = (ctx + a.chunk - 1) / a.chunk;
   const int h = wid % a.Nh;
   const long long slot0 = part_slot(a, b, h, 0);  // chunk s: slot0 + s * Nh
   const int nvec = a.Dv / 8;                   // 8-column groups per row (a divisor of 64)
   const int spl = 64 / nvec;                   // chunk phases
   const int c0 = lane % nvec, ph = lane / nvec;
   uint16_t* op = a.out + (long long)wid * a.Dv;
+  const float* ml = a.part_ml + slot0 * 2;
+  const uint16_t* po = a.part_o + slot0 * a.Dv;
+  // one pass: chunks s0, s0 + spl, ... (kU of them) of this lane's phase. The slots of all nsplit
+  // chunks exist, so the first pass is loaded before the context length is known (slots past the
+  // sequence's last chunk hold stale data and are masked below).
+  constexpr int kU = 8;
+  U4 v[kU];
+  float2 mls[kU];
+  auto load_pass = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int s = s0 + u * spl;
+      const bool in = s < a.nsplit;
+      mls[u] = in ? *reinterpret_cast<const float2*>(ml + 2 * (long long)s * a.Nh) : make_float2(-INFINITY, 0.f);
+      v[u] = in ? ldg16_nt(po + ((long long)s * a.Nh * nvec + c0) * 8) : U4{0u, 0u, 0u, 0u};
+    }
+  };
+  const int ctx = min(max(a.ctx_lens[b], 0), a.max_ctx);
+  load_pass(ph);
+  const int ns = (ctx + a.chunk - 1) / a.chunk;
   if (ns == 0) {
     if (ph == 0) *reinterpret_cast<uint4*>(op + 8 * c0) = make_uint4(0u, 0u, 0u, 0u);
     return;
   }
-  const float* ml = a.part_ml + slot0 * 2;
-  const uint16_t* po = a.part_o + slot0 * a.Dv;
-  // the reference max over all chunks (lane s holds chunk s, s + 64, ...)
+  // the reference max over the written chunks: this phase's, then across the phases
   float mx = -INFINITY;
-  for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, ml[2 * (long long)s * a.Nh]);
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  for (int u = 0; u < kU; ++u)
+    if (ph + u * spl < ns) mx = fmaxf(mx, mls[u].x);
+  for (int s = ph + kU * spl; s < ns; s += spl) mx = fmaxf(mx, ml[2 * (long long)s * a.Nh]);
+  for (int off = nvec; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   float l = 0.f;  // sum of the weights of this lane's phase (summed over the phases below)
-  constexpr int kU = 8;  // chunks per phase in flight
-  for (int s0 = ph; s0 < ns; s0 += kU * spl) {
-    U4 v[kU];
-    float2 mls[kU];
+  auto use_pass = [&](int s0) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int s = s0 + u * spl;
-      const bool in = s < ns;
-      mls[u] = in ? *reinterpret_cast<const float2*>(ml + 2 * (long long)s * a.Nh) : make_float2(-INFINITY, 0.f);
-      v[u] = in ? ldg16_nt(po + ((long long)s * a.Nh * nvec + c0) * 8) : U4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
+      if (s0 + u * spl >= ns) break;
       const float wgt = mls[u].x == -INFINITY ? 0.f : fast_exp2(mls[u].x - mx) * mls[u].y;
       l += wgt;
       const uint32_t wv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
@@ -354,6 +363,11 @@ __global__ __launch_bounds__(kThreads) void decode_reduce_kernel(DecodeArgs a) {
         acc[2 * e + 1] = fmaf(wgt, bf16hi(wv[e]), acc[2 * e + 1]);
       }
     }
+  };
+  use_pass(ph);
+  for (int s0 = ph + kU * spl; s0 < ns; s0 += kU * spl) {
+    load_pass(s0);
+    use_pass(s0);
   }
   // sum the phases (lanes c0, c0 + nvec, ...) and the sums of all chunks
   for (int off = nvec; off < 64; off <<= 1) {
