@@ -808,8 +808,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_wide_kernel(DecodeA
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read out before the tile loads refill the columns
   }
   issue_tile(0, ring[0]);
-  issue_tile(min(1, n_tiles - 1), ring[1]);
-  issue_tile(min(2, n_tiles - 1), ring[2]);
+  if (n_tiles > 1) issue_tile(1, ring[1]);
+  if (n_tiles > 2) issue_tile(2, ring[2]);
 
   f32x16 o[2][kDB];
 #pragma unroll
@@ -887,7 +887,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_wide_kernel(DecodeA
 
   // ---- tile 0: scores, the reference max, P ----
   uint32_t pk[2][4];
-  wait_vmem_n<2 * kSPW>();  // tile 0 has landed (tiles 1 and 2 may still fly)
+  // tile 0 has landed (tiles 1 and 2 may still fly)
+  if (n_tiles > 2)
+    wait_vmem_n<2 * kSPW>();
+  else if (n_tiles > 1)
+    wait_vmem_n<kSPW>();
+  else
+    wait_vmem_n<0>();
   barrier_only();  // every wave's part of tile 0 is in LDS
   {
     f32x16 sv = qk(ring[0], NoSpread{}, nullptr, nullptr);
@@ -908,19 +914,21 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_wide_kernel(DecodeA
   // made: Q.K of tile j+1 first, then its exponentials interleaved with the P.V products. One
   // barrier per step: tile j+1 has landed in every wave, every wave's P(j) is in LDS (both waves of
   // a pair read both groups' P(j) from there after Q.K), and every wave is done with stage
-  // (j-1) % 4, which the load of tile j+3 then refills. A load past the
-  // last tile re-reads the last one into a stage that is never read again, so every step keeps
-  // one fixed vmcnt. P goes through two LDS buffers: P(j+1) is written while P(j) may still be
-  // read by the partner. ----
+  // (j-1) % 4, which the load of tile j+3 then refills. P goes through two LDS buffers: P(j+1) is
+  // written while P(j) may still be read by the partner. ----
   for (int j = 0; j < n_tiles; ++j) {
-    wait_vmem_n<kSPW>();  // tile j+1 has landed (tile j+2 may still fly)
+    // tile j+1 has landed (tile j+2, if there is one, may still fly)
+    if (j + 2 < n_tiles)
+      wait_vmem_n<kSPW>();
+    else
+      wait_vmem_n<0>();
     barrier_only();
     const bool more = j + 1 < n_tiles;
-    // the load of tile j+3 (a re-read of the last tile past the end): spread over the products of
-    // Q.K(j+1) when that tile is full and there is a Q.K, else issued at once
-    const int jl = min(j + 3, n_tiles - 1);
-    const bool spread = more && t0 + jl * TT + TT <= t1;
-    if (!spread) issue_tile(jl, ring[(j + 3) & 3]);
+    // the load of tile j+3: spread over the products of Q.K(j+1) when that tile is full, else
+    // issued at once (a partial last tile clamps its rows)
+    const int jl = j + 3;
+    const bool spread = jl < n_tiles && t0 + jl * TT + TT <= t1;
+    if (jl < n_tiles && !spread) issue_tile(jl, ring[jl & 3]);
     f32x16 sn = f32x16{};
     if (spread) {
       sn = qk(ring[(j + 1) & 3], Spread{}, seq + (long long)(t0 + jl * TT) * ldk, ring[(j + 3) & 3]);
@@ -966,7 +974,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_wide_kernel(DecodeA
     }
     put_p(pn, (j + 1) & 1);  // also past the last tile (never read), so the exponentials stay among the products
   }
-  wait_vmem();  // the re-reads must land before the work-group's LDS is released
+  wait_vmem();  // (the last step waited for every load already)
 
   // ---- (max, sum) and the overflow flags of the own heads to the partner, through the last
   // 1,040 bytes of the ring once every wave is done with it ----
