@@ -89,9 +89,9 @@ int attn_prefill(const void* q, const void* k, const void* v, void* out,
  *   (128 + i, 160 + i), frequency rope_theta^(-2i/64), positions 0 .. S-1); the rotated keys go
  *   to the workspace. causal as attn_prefill; scale <= 0 selects 1 / sqrt(192).
  * Supported: bf16 storage (fp32 accumulation), Nh % Nkv == 0.
- * workspace: at least attn_prefill_mla_workspace_bytes(...) bytes (0 without RoPE).
- * Status: the kernel is built but not enabled yet; after validating its arguments (the errors
- * above) the call returns ATTN_ERR_UNSUPPORTED without launching anything.
+ * B == 0 or S == 0 is a valid empty call (nothing launched).
+ * workspace: at least attn_prefill_mla_workspace_bytes(...) bytes (0 without RoPE): the angle
+ *   table and the keys with their rotated k^R block (k itself is never modified).
  * ------------------------------------------------------------------------------------------ */
 size_t attn_prefill_mla_workspace_bytes(int B, int S, int Nkv, float rope_theta);
 
