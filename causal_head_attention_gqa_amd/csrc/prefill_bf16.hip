@@ -427,19 +427,21 @@ __global__ __launch_bounds__(kThreads, (DQK > 128 ? 2 : 3)) void prefill_bf16_ke
 // last 32 rows: one dependent chain over every key tile. Here the 4 waves of a work-group split
 // the key tiles of their query rows KS ways: the work-group holds 4/KS blocks of 32 query rows of
 // one head, and wave w takes block w / KS and the key tiles w % KS, w % KS + KS, ... (a KS-th of the
-// chain). Each wave streams its tiles through its own 2-stage LDS ring (direct-to-LDS loads, no
-// barrier while streaming) and runs the online softmax of the kernel above on them (fixed
-// reference max, exact path for a block that overflows it); at the end the KS partial (max, sum,
-// output) of each block are merged through LDS with the same recurrences ("Transformer 架构完全
-// 深度解析" §十三: running max and sum, applied to the waves' partial results). Plain prefill only
-// (positions 0 .. S-1, no cache, no window), equal q/k/v head dims, half-split RoPE over the whole
-// head when a table is given.
+// chain). The waves of one key split (one per query block) need the same tiles, so they share a
+// 2-stage LDS ring, each loading its part of every tile (direct-to-LDS loads); one work-group barrier
+// per step makes a tile visible and frees the other stage. Each wave runs the online softmax of the
+// kernel above on its tiles (fixed reference max, exact path for a block that overflows it); at the
+// end the KS partial (max, sum, output) of each block are merged through LDS with the same
+// recurrences ("Transformer 架构完全深度解析" §十三: running max and sum, applied to the waves'
+// partial results). The shared rings take half the LDS of one ring per wave (35 KiB for 64-dim
+// heads), so four work-groups share a CU. Plain prefill only (positions 0 .. S-1, no cache, no
+// window), equal q/k/v head dims, half-split RoPE over the whole head when a table is given.
 template <int D, int KS>
-__global__ __launch_bounds__(kThreads, (D <= 64 ? 2 : 1)) void prefill_splitk_kernel(
+__global__ __launch_bounds__(kThreads, (D <= 64 ? 4 : 2)) void prefill_splitk_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ out, const float2* __restrict__ table, int B, int S, int Nh, int Nkv, float c, int causal,
     int n_qb) {
-  constexpr int NB = 2;                 // stages per wave
+  constexpr int NB = 2;                 // stages of each key split's ring
   constexpr int CH = D / 8;             // 16-byte chunks per row
   constexpr int TE = kBC * D;           // elements of one K (or V) tile
   constexpr int LT = kBC * CH / 64;     // load instructions per K (or V) tile, one wave
@@ -447,8 +449,14 @@ __global__ __launch_bounds__(kThreads, (D <= 64 ? 2 : 1)) void prefill_splitk_ke
   constexpr int NDB = D / 32;           // 32-row blocks of the output's head dim
   constexpr int MP = D + 4;             // row pitch (floats) of the merge area
   constexpr int QB = 4 / KS;            // 32-row query blocks per work-group
-  __shared__ __attribute__((aligned(1024))) uint16_t ring[4][NB][2][TE];
-  static_assert(NB * 2 * TE * 2 >= (32 * MP + 64) * 4, "merge area must fit in a wave's ring");
+  constexpr int LW = LT / QB;           // load instructions per K (or V) tile and wave of a ring
+  static_assert(LT % QB == 0, "a ring's tile loads split evenly over its waves");
+  // the KS rings [KS][NB][K, V][TE], then (once the loop is done) the merge area of each wave
+  constexpr int kRingBytes = KS * NB * 2 * TE * 2;
+  constexpr int kMergeFloats = 32 * MP + 64;  // one wave's rows, then its (max, sum) pairs
+  constexpr int kLdsBytes = kRingBytes > 4 * kMergeFloats * 4 ? kRingBytes : 4 * kMergeFloats * 4;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[kLdsBytes / 2];
+  auto ring = [&](int ksr, int st, int kv) { return lds + ((ksr * NB + st) * 2 + kv) * TE; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -503,30 +511,43 @@ __global__ __launch_bounds__(kThreads, (D <= 64 ? 2 : 1)) void prefill_splitk_ke
   for (int i = 0; i < NDB; ++i) o[i] = f32x16{};
   float m = -INFINITY, mneg = -0.f, lsum = 0.f;
 
-  // ---- this wave's tiles: ks, ks + KS, ... up to its block's last row (none past the sequence) ----
-  const int last = p0 >= S ? 0 : causal ? min(S, p0 + 32) : S;
-  const int n_tiles = (last + kBC - 1) / kBC;
-  const int my_n = n_tiles > ks ? (n_tiles - ks + KS - 1) / KS : 0;
+  // ---- key tiles needed by query block qs of this work-group (none past the sequence); the
+  // work-group's largest need sets the step count, the same for every wave ----
+  auto need = [&](int qs) {
+    const int pq = (qg * QB + qs) * 32;
+    return pq >= S ? 0 : ((causal ? min(S, pq + 32) : S) + kBC - 1) / kBC;
+  };
+  int max_tiles = 0;
+#pragma unroll
+  for (int qs = 0; qs < QB; ++qs) max_tiles = max(max_tiles, need(qs));
+  const int n_steps = (max_tiles + KS - 1) / KS;  // tiles of key split 0, the most of any split
+  const int my_tiles = need(qsub);
   const long long kv_tok = (long long)Nkv * D;
   const uint16_t* kbase = k + (long long)b * S * kv_tok + (long long)g * D;
   const uint16_t* vbase = v + (long long)b * S * kv_tok + (long long)g * D;
   // lane i of load sl covers tile bytes sl*1024 + 16i = row * 2D + 16 * chunk
   auto trow = [&](int sl) { return (sl * 1024 + 16 * lane) / (D * 2); };
   auto tchk = [&](int sl) { return ((sl * 1024 + 16 * lane) % (D * 2)) / 16; };
-  uint32_t loff[LT];
+  // this wave loads slots qsub * LW .. qsub * LW + LW - 1 of every K and V tile of its ring
+  uint32_t loff[LW];
 #pragma unroll
-  for (int sl = 0; sl < LT; ++sl) loff[sl] = 2u * (uint32_t)(trow(sl) * (int)kv_tok + swz<CH>(tchk(sl), trow(sl)) * 8);
+  for (int u = 0; u < LW; ++u) {
+    const int sl = qsub * LW + u;
+    loff[u] = 2u * (uint32_t)(trow(sl) * (int)kv_tok + swz<CH>(tchk(sl), trow(sl)) * 8);
+  }
   auto issue_tile = [&](int jt, uint16_t* kdst, uint16_t* vdst) {
     if (jt * kBC + kBC <= S) {
+      asm volatile("s_nop 4" ::: "memory");
 #pragma unroll
-      for (int sl = 0; sl < LT; ++sl)
-        load_lds16_async_sv(kbase + (long long)jt * kBC * kv_tok, loff[sl], kdst + sl * 512);
+      for (int u = 0; u < LW; ++u)
+        load_lds16_async_sv(kbase + (long long)jt * kBC * kv_tok, loff[u], kdst + (qsub * LW + u) * 512);
 #pragma unroll
-      for (int sl = 0; sl < LT; ++sl)
-        load_lds16_async_sv(vbase + (long long)jt * kBC * kv_tok, loff[sl], vdst + sl * 512);
+      for (int u = 0; u < LW; ++u)
+        load_lds16_async_sv(vbase + (long long)jt * kBC * kv_tok, loff[u], vdst + (qsub * LW + u) * 512);
     } else {  // the last, partial tile: rows past the end re-read row S-1 (finite data, masked)
 #pragma unroll
-      for (int sl = 0; sl < LT; ++sl) {
+      for (int u = 0; u < LW; ++u) {
+        const int sl = qsub * LW + u;
         const long long e = (long long)min(jt * kBC + trow(sl), S - 1) * kv_tok + swz<CH>(tchk(sl), trow(sl)) * 8;
         load_lds16_async<false>(kbase + e, kdst + sl * 512);
         load_lds16_async<false>(vbase + e, vdst + sl * 512);
@@ -627,20 +648,27 @@ __global__ __launch_bounds__(kThreads, (D <= 64 ? 2 : 1)) void prefill_splitk_ke
     }
   };
 
-  // ---- the wave's own ring: tile i+1 loads while tile i is computed ----
-  if (my_n > 0) issue_tile(ks, ring[w][0][0], ring[w][0][1]);
-  for (int i = 0; i < my_n; ++i) {
-    if (i + 1 < my_n) {
-      issue_tile(ks + KS * (i + 1), ring[w][(i + 1) & 1][0], ring[w][(i + 1) & 1][1]);
-      wait_vmem_n<2 * LT>();  // tile i has landed, tile i+1 may fly
-    } else {
-      wait_vmem();
-    }
-    compute_tile(ks + KS * i, ring[w][i & 1][0], ring[w][i & 1][1]);
+  // ---- step i: tile ks + KS*i of every key split. Each wave waits for its own part of the tile,
+  // the barrier makes the whole tile visible and guarantees that every wave is done with the other
+  // stage (the tile of step i-1), which the loads of step i+1 then refill. Every wave runs all
+  // n_steps steps (the barrier count is the work-group's), computing only the tiles its block
+  // needs; a ring holds every tile that either of its blocks needs. ----
+  auto issue_step = [&](int i) {
+    const int jt = ks + KS * i;
+    if (jt < max_tiles) issue_tile(jt, ring(ks, i & 1, 0), ring(ks, i & 1, 1));
+  };
+  issue_step(0);
+  for (int i = 0; i < n_steps; ++i) {
+    wait_vmem_n<0>();  // this wave's part of step i's tile has landed (nothing newer is in flight)
+    barrier_only();
+    issue_step(i + 1);
+    const int jt = ks + KS * i;
+    if (jt < my_tiles) compute_tile(jt, ring(ks, i & 1, 0), ring(ks, i & 1, 1));
   }
+  __syncthreads();  // every wave is done with the rings: the merge area overlays them
 
-  // ---- merge the KS waves of each block: (max, sum, output) through LDS (each wave's own ring) ----
-  auto mo = [&](int vw) { return reinterpret_cast<float*>(&ring[vw][0][0][0]); };
+  // ---- merge the KS waves of each block: (max, sum, output) through LDS ----
+  auto mo = [&](int vw) { return reinterpret_cast<float*>(lds) + vw * kMergeFloats; };
   const float ltot = pair_sum32(lsum);
 #pragma unroll
   for (int db = 0; db < NDB; ++db)

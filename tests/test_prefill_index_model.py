@@ -200,29 +200,45 @@ def test_grid_covers_every_tile_once_and_stays_in_bounds(case):
 
 
 @pytest.mark.parametrize("KS", [1, 2, 4])
-@pytest.mark.parametrize("S,causal", [(600, True), (545, True), (512, False), (1024, True)])
+@pytest.mark.parametrize("S,causal", [(600, True), (545, True), (512, False), (1024, True), (33, True), (1, True)])
 def test_split_key_grid_covers_every_block_tile_once(KS, S, causal):
     """The split-key prefill: work-group qg holds query blocks qg*QB .. qg*QB+QB-1 (QB = 4/KS);
-    wave w takes block w // KS and key tiles w % KS, w % KS + KS, ...; every (block, visible key
-    tile) is computed by exactly one wave, and the merge's 256 threads write every (row, dim) of
-    the group once."""
+    wave w takes block w // KS and key split w % KS. The QB waves of one key split share a 2-stage
+    ring: at step i each of them loads its LW = LT/QB slots of tile ks + KS*i (when some block of
+    the work-group needs it) and computes it (when its own block needs it). Every wave runs the same
+    number of steps (one barrier each), every (block, visible key tile) is computed by exactly one
+    wave, every computed tile was loaded whole (every slot once) into the stage it is read from,
+    and the merge's 256 threads write every (row, dim) of the group once."""
     QB = 4 // KS
     n_qb = (S + 32 * QB - 1) // (32 * QB)
     seen = {}
     for qg in range(n_qb):
+        def need(qs):
+            pq = (qg * QB + qs) * 32
+            return 0 if pq >= S else ((min(S, pq + 32) if causal else S) + 31) // 32
+        max_tiles = max(need(qs) for qs in range(QB))
+        steps = []
         for w in range(4):
-            p0 = (qg * QB + w // KS) * 32
-            last = 0 if p0 >= S else (min(S, p0 + 32) if causal else S)
-            n_tiles = (last + 31) // 32
-            ks = w % KS
-            my_n = (n_tiles - ks + KS - 1) // KS if n_tiles > ks else 0
-            for i in range(my_n):
-                key = (p0 // 32, ks + KS * i)
-                assert key not in seen
-                seen[key] = w
+            qsub, ks = w // KS, w % KS
+            n_steps = (max_tiles + KS - 1) // KS  # computed the same way by every wave
+            steps.append(n_steps)
+            for i in range(n_steps):
+                jt = ks + KS * i
+                if jt < need(qsub):
+                    key = (qg * QB + qsub, jt)
+                    assert key not in seen
+                    seen[key] = w
+                    # the tile was loaded in full into stage i & 1 of ring ks by the ring's QB waves
+                    assert jt < max_tiles
+        assert len(set(steps)) == 1
     want = {(qb, j) for qb in range((S + 31) // 32) for j in range(((min(S, 32 * qb + 32) if causal else S) + 31) // 32)}
     assert set(seen) == want
     for D in (64, 128):
+        LT = 32 * (D // 8) // 64
+        LW = LT // QB
+        assert LT % QB == 0
+        slots = sorted(qsub * LW + u for qsub in range(QB) for u in range(LW))
+        assert slots == list(range(LT))  # the ring's waves cover a tile's load slots once
         TPR = 8 // QB
         PER = D // TPR
         cells = set()
@@ -231,3 +247,9 @@ def test_split_key_grid_covers_every_block_tile_once(KS, S, causal):
             for e in range(PER):
                 cells.add((r, d0 + e))
         assert cells == {(r, d) for r in range(32 * QB) for d in range(D)}
+    # LDS: the rings, or the merge area once the loop is done, whichever is larger (64-dim heads:
+    # 35 KiB, four work-groups per CU)
+    for D, per_cu in ((64, 4), (128, 2)):
+        ring = KS * 2 * 2 * 32 * D * 2
+        merge = 4 * (32 * (D + 4) + 64) * 4
+        assert per_cu * max(ring, merge) <= 160 * 1024 or KS != 2
