@@ -808,8 +808,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_wide_kernel(DecodeA
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read out before the tile loads refill the columns
   }
   issue_tile(0, ring[0]);
-  if (n_tiles > 1) issue_tile(1, ring[1]);
-  if (n_tiles > 2) issue_tile(2, ring[2]);
 
   f32x16 o[2][kDB];
 #pragma unroll
@@ -887,13 +885,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_wide_kernel(DecodeA
 
   // ---- tile 0: scores, the reference max, P ----
   uint32_t pk[2][4];
-  // tile 0 has landed (tiles 1 and 2 may still fly)
-  if (n_tiles > 2)
-    wait_vmem_n<2 * kSPW>();
-  else if (n_tiles > 1)
-    wait_vmem_n<kSPW>();
-  else
-    wait_vmem_n<0>();
+  // tile 0 has landed; tiles 1 and 2 load during its products (issued only now: when every
+  // work-group starts at once, tile 0 then does not share HBM with them)
+  wait_vmem_n<0>();
+  if (n_tiles > 1) issue_tile(1, ring[1]);
+  if (n_tiles > 2) issue_tile(2, ring[2]);
   barrier_only();  // every wave's part of tile 0 is in LDS
   {
     f32x16 sv = qk(ring[0], NoSpread{}, nullptr, nullptr);
