@@ -34,10 +34,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
 }
 
 __device__ __forceinline__ U4 ldg16(const void* p) { return *reinterpret_cast<const U4*>(p); }
-// The same load with the non-temporal hint, for data that is read once.
+// 16-byte load and store with the non-temporal hint, for data that is read (written) once.
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 __device__ __forceinline__ U4 ldg16_nt(const void* p) {
-  typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
   return __builtin_bit_cast(U4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+}
+__device__ __forceinline__ void stg16_nt(void* p, U4 v) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
 }
 __device__ __forceinline__ void stg16(void* p, U4 v) { *reinterpret_cast<U4*>(p) = v; }
 

@@ -1015,7 +1015,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_wide_kernel(DecodeA
     if ((bad_g[hl >> 5] >> (hl & 31)) & 1) continue;  // recomputed below
     const long long row = (long long)b * a.Nh + hp + hl;
     uint16_t* op = (a.nsplit == 1 ? a.out + row * DV : a.part_o + part_slot(a, b, hp + hl, s) * DV) + r * (DV / 2) + col * 8;
-    *reinterpret_cast<uint4*>(op) = v;
+    stg16_nt(op, U4{v.x, v.y, v.z, v.w});  // every work-group writes at once at its end: streaming stores
   }
   if (a.nsplit > 1 && hf == 0 && !((bad_g[r] >> col) & 1)) {
     const long long slot = part_slot(a, b, hp + 32 * r + col, s);
