@@ -126,16 +126,25 @@ __device__ __forceinline__ void load_lds16_async(const void* gptr, const void* l
 // pair is never the result of a vector instruction such as v_readfirstlane. A VMEM instruction
 // that reads an SGPR written by a VALU instruction needs 5 wait states, which the compiler does not
 // insert in front of inline assembly (the build rejects such sequences in the generated code).
+// kStream adds the non-temporal hint (rows read once), as for load_lds16_async.
+template <bool kStream = false>
 __device__ __forceinline__ void load_lds16_async_sv(const void* sbase, uint32_t voff, const void* lds_base) {
   const uint32_t lds_addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
+  if constexpr (kStream)
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
+  else
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
 }
 
 // The same, with the 5 wait states that a base pair written by a vector instruction would need
 // inside the asm: for loads placed among other work, where a branch target may come right before.
+template <bool kStream = false>
 __device__ __forceinline__ void load_lds16_async_sv_nop(const void* sbase, uint32_t voff, const void* lds_base) {
   const uint32_t lds_addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base;
-  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
+  if constexpr (kStream)
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
+  else
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
 }
 
 // Work-group barrier without the memory fences of __syncthreads(): for tiles filled by

@@ -748,7 +748,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_wide_kernel(DecodeA
 
   // ---- tile loads: wave w fills slots w*9 .. w*9+8; lane i of slot sl covers tile bytes
   // sl*1024 + 16i = row*1152 + 16pc and fetches logical chunk pc ^ key(row) of that row. One
-  // byte offset per slot serves the full tiles; the chunk's last, partial tile clamps its rows. ----
+  // byte offset per slot serves the full tiles; the chunk's last, partial tile clamps its rows.
+  // The cache rows are read once: non-temporal loads (the query rows, read by every chunk of the
+  // sequence, keep the default policy). ----
   const long long ldk = a.ldk;  // Nkv == 1
   const uint16_t* seq = a.kc + (long long)b * a.max_ctx * ldk;
   auto slot_row = [&](int u) { return ((w * kSPW + u) * 1024 + 16 * lane) / (DQ * 2); };
@@ -769,14 +771,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_wide_kernel(DecodeA
     if (lim >= TT - 1) {
       asm volatile("s_nop 4" ::: "memory");
 #pragma unroll
-      for (int u = 0; u < kSPW; ++u) load_lds16_async_sv(base, loff[u], dst + (w * kSPW + u) * 512);
+      for (int u = 0; u < kSPW; ++u) load_lds16_async_sv<true>(base, loff[u], dst + (w * kSPW + u) * 512);
     } else {
       asm volatile("s_nop 4" ::: "memory");
 #pragma unroll
       for (int u = 0; u < kSPW; ++u) {
         const int row = slot_row(u);  // rows past the chunk re-read row lim (masked)
         const uint32_t off = row <= lim ? loff[u] : loff[u] - 2u * (uint32_t)((row - lim) * (int)ldk);
-        load_lds16_async_sv(base, off, dst + (w * kSPW + u) * 512);
+        load_lds16_async_sv<true>(base, off, dst + (w * kSPW + u) * 512);
       }
     }
   };
@@ -854,7 +856,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_wide_kernel(DecodeA
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (kSpread) {
         static_assert(kKS == 4 * kSPW, "one load per four products");
-        if (kk % 4 == 0) load_lds16_async_sv_nop(base, loff[kk / 4], dst + (w * kSPW + kk / 4) * 512);
+        if (kk % 4 == 0) load_lds16_async_sv_nop<true>(base, loff[kk / 4], dst + (w * kSPW + kk / 4) * 512);
       }
     }
     return sv;
