@@ -78,7 +78,7 @@ __device__ __forceinline__ bool decode_item(const DecodeArgs& a, int item, int& 
     const unsigned long long m = __ballot(part);
     const int cnt = __popcll(m);
     if (j < cnt) {
-      const bool hit = part && __popcll(m & ((1ull << lane) - 1)) == j;
+      const bool hit = part && (int)__popcll(m & ((1ull << lane) - 1)) == j;
       const int l = __builtin_ctzll(__ballot(hit));
       b_out = b0 + l;
       s_out = __shfl(ctx, l) / a.chunk;

@@ -95,7 +95,6 @@ __device__ __forceinline__ void rope_qr_hilo(U4& a, U4& b, U4& alo, U4& blo, int
 // kRope: rotate q^R in-kernel (a.rope_theta > 0) and add the products of its bf16 residuals.
 template <int NW, bool kRope>
 __global__ __launch_bounds__(NW * 64, (NW >= 8 ? 2 : 1)) void decode_mla_kernel(DecodeArgs a) {
-  constexpr int NT = NW * 64;
   constexpr int SPW = (NSLOT + NW - 1) / NW;  // load slots per wave (some waves one fewer)
   constexpr int WAITN = NSLOT / NW;           // loads of the next tile every wave has issued
   __shared__ __attribute__((aligned(1024))) uint16_t ring[NB][TILE];

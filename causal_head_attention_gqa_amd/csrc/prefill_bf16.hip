@@ -81,6 +81,7 @@ __global__ __launch_bounds__(kThreads, (DQK > 128 ? 2 : 3)) void prefill_bf16_ke
   static_assert(kBC * CHK % 256 == 0 && kBC * CHV % 256 == 0, "tile loads must split over 4 waves");
 
   // one array per ring stage, so the compiler can tell which direct-to-LDS loads a read depends on
+  static_assert(kStages == 3, "the ring below is written out for three stages");
   __shared__ __attribute__((aligned(1024))) uint16_t Ks0[kBC * DQK];
   __shared__ __attribute__((aligned(1024))) uint16_t Vs0[kBC * DV];
   __shared__ __attribute__((aligned(1024))) uint16_t Ks1[kBC * DQK];
