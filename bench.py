@@ -295,6 +295,29 @@ def run_extras(torch, attn, steps: int, warmup: int):
     emit("mla_prefill", ms_m, acc.prefill_flops(Mp.B, Mp.S, Mp.Nh, Mp.Dh, causal=True, Dv=Mp.dv), "TFLOP/s",
          acc.PEAK_BF16_TFLOPS, {"flop_per_pair": 2 * (Mp.Dh + Mp.dv), "includes": "k^R rotation pass"},
          wl=f"DeepSeek-V3 MLA non-absorbed prefill B{Mp.B} S{Mp.S} Nh{Mp.Nh} q/k {Mp.Dh} v {Mp.dv} RoPE{Mp.rope_theta:g}")
+    del mq, mk, mv, mo, mws
+
+    # MLA-absorbed decode with the decoupled q^R block rotated in-kernel at ctx-1 (the same workload as
+    # the bench step's MLA part otherwise; cold-cache replicas as there)
+    M = synth.MLA_DECODE
+    rq = device_normal(torch, (M.B, M.Nh, M.Dqk), 1000 * M.wid + 0)
+    rkv = [device_normal(torch, (M.B, M.max_ctx, 1, M.Dqk), 1000 * M.wid + 1 + 10 * r) for r in range(MLA_REPLICAS)]
+    rctx_np = M.ctx_lens()
+    rctx = torch.as_tensor(rctx_np, device="cuda")
+    rout = torch.empty((M.B, M.Nh, M.Dv), dtype=torch.bfloat16, device="cuda")
+    rws = torch.empty(attn.decode_workspace_bytes(M.B, M.Nh, 1, M.Dqk, M.Dv, M.max_ctx, attn.ATTN_BF16),
+                      dtype=torch.uint8, device="cuda")
+    rcalls = [0]
+
+    def mla_rope():
+        kv = rkv[rcalls[0] % MLA_REPLICAS]
+        rcalls[0] += 1
+        attn.decode(rq, kv, kv[..., :M.Dv], rctx, scale=M.scale, rope_theta=1e4, out=rout, workspace=rws)
+
+    ms_r = timed(mla_rope)
+    emit("mla_decode_rope", ms_r, acc.decode_bytes(rctx_np, M.B, M.Nh, 1, M.Dqk, M.Dv, 2, shared_row=True), "GB/s",
+         acc.PEAK_HBM_GBS, {"rope_theta": 1e4, "includes": "q^R (dims 512..575) rotated in-kernel at ctx-1; merge"},
+         wl=f"MLA-absorbed decode B{M.B} ctx{M.max_ctx} {M.Nh}x{M.Dqk}/{M.Dv}")
     for ln in lines:
         print(json.dumps(ln))
 

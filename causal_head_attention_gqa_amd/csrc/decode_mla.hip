@@ -677,7 +677,7 @@ hipError_t launch(const DecodeArgs& a, hipStream_t st) {
 }  // namespace pair
 
 // ---- 64 heads per wave pair, all 128 heads of a row in one work-group (head counts that are
-// multiples of 128, no in-kernel RoPE) ----
+// multiples of 128) ----
 //
 // The pair kernel above reads every V operand from LDS for one 32-head product and exchanges fp32
 // partial scores. Here the accumulators of a wave cover 64 heads, so each V operand feeds two
@@ -707,6 +707,8 @@ constexpr int kKS = DQ / 16;          // 36 k-steps of Q.K
 constexpr int kDB = DV / 2 / 32;      // 8 output blocks of 32 dims per wave
 static_assert(NSLOT % kWaves == 0, "tile loads split evenly over the waves");
 
+// kRope: rotate q^R in-kernel (a.rope_theta > 0) and add the products of its bf16 residuals.
+template <bool kRope>
 __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_wide_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t ring[kStages][TILE];
   __shared__ __attribute__((aligned(16))) uint32_t xp[2][kWaves][2][64][4];  // P (bf16 pairs), two buffers
@@ -808,6 +810,24 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_wide_kernel(DecodeA
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // read out before the tile loads refill the columns
   }
+  bf16x8 qlo[4];  // kRope: bf16 residuals of the rotated q^R (k-steps 32..35)
+  if constexpr (kRope) {
+    // q^R = dims 512..575 = k-steps 32..35: dims 512 + 16u + 8hf + j in qreg[32 + u], their
+    // half-split partners 544 + 16u + 8hf + j in qreg[34 + u]
+    U4 ra[4], lo[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      ra[u] = __builtin_bit_cast(U4, qreg[kKS - 4 + u]);
+      lo[u] = U4{0, 0, 0, 0};
+    }
+    rope_qr_hilo(ra[0], ra[2], lo[0], lo[2], hf * 8, ctx - 1, a.rope_theta);
+    rope_qr_hilo(ra[1], ra[3], lo[1], lo[3], 16 + hf * 8, ctx - 1, a.rope_theta);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      qreg[kKS - 4 + u] = as_bf16x8(ra[u]);
+      qlo[u] = as_bf16x8(lo[u]);
+    }
+  }
   issue_tile(0, ring[0]);
 
   f32x16 o[2][kDB];
@@ -857,6 +877,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_wide_kernel(DecodeA
         static_assert(kKS == 4 * kSPW, "one load per four products");
         if (kk % 4 == 0) load_lds16_async_sv_nop<true>(base, loff[kk / 4], dst + (w * kSPW + kk / 4) * 512);
       }
+    }
+    if constexpr (kRope) {
+      // the q^R residuals against the K operands of k-steps 32..35, still in the ring
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[(kKS - 4 + u) % kKR], qlo[u], sv, 0, 0, 0);
     }
     return sv;
   };
@@ -1032,11 +1058,22 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_wide_kernel(DecodeA
   if (bad == 0) return;
   float* qs = reinterpret_cast<float*>(&ring[0][0]) + w * (kStages * TILE / 2 / kWaves);  // 576 + 4096 floats
   float* sc = qs + DQ;
+  const double kf = kRope ? -2.0 * log2(a.rope_theta) / (double)(DQ - DV) : 0.0;
   for (; bad; bad &= bad - 1) {
     const int c = __builtin_ctzll(bad);
     const int hc = hp + c;
     const uint16_t* qp = a.q + ((long long)b * a.Nh + hc) * DQ;
-    for (int d = lane; d < DQ; d += 64) qs[d] = bf16_to_f32(qp[d]);
+    for (int d = lane; d < DQ; d += 64) {
+      float v = bf16_to_f32(qp[d]);
+      if (kRope && d >= DV) {  // the decoupled RoPE of the main path, kept in fp32 here
+        const int i = (d - DV) & 31;
+        double sn, cs;
+        sincos((double)(ctx - 1) * exp2(kf * (double)i), &sn, &cs);
+        const double x = bf16_to_f32(qp[DV + i]), y = bf16_to_f32(qp[DV + 32 + i]);
+        v = (float)(d < DV + 32 ? x * cs - y * sn : x * sn + y * cs);
+      }
+      qs[d] = v;
+    }
     float mr = -INFINITY, lr = 0.f, o4[4] = {0.f, 0.f, 0.f, 0.f};
     for (int tb = t0; tb < t1; tb += 4096) {
       const int n = min(4096, t1 - tb);
@@ -1091,7 +1128,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_wide_kernel(DecodeA
 hipError_t launch(const DecodeArgs& a, hipStream_t st) {
   const long long n_wg = 8 * (((long long)a.B + 7) / 8) * a.nsplit * (a.Nh / kHeads);
   if (n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  decode_mla_wide_kernel<<<dim3((unsigned)n_wg), dim3(kWaves * 64), 0, st>>>(a);
+  if (a.rope_theta > 0)
+    decode_mla_wide_kernel<true><<<dim3((unsigned)n_wg), dim3(kWaves * 64), 0, st>>>(a);
+  else
+    decode_mla_wide_kernel<false><<<dim3((unsigned)n_wg), dim3(kWaves * 64), 0, st>>>(a);
   return hipGetLastError();
 }
 }  // namespace wide
@@ -1116,7 +1156,7 @@ int mla_heads_per_group(int Nh) {
 }
 
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t st) {
-  if (a.Nh % wide::kHeads == 0 && !(a.rope_theta > 0)) return wide::launch(a, st);
+  if (a.Nh % wide::kHeads == 0) return wide::launch(a, st);
   if (a.Nh % pair::kHeads == 0) return pair::launch(a, st);
   switch (mla_waves_per_group(a.Nh)) {
     case 8:

@@ -175,10 +175,12 @@ MLA_PAIR_CASES = [
     (2, 64, 333, [333, 32], 0.0),
     (2, 64, 200, [200, 77], 1e4),      # decoupled q^R RoPE (held by the upper reduction half)
     (2, 192, 130, [130, 96], 5e5),     # three head groups
-    # multiples of 128 without RoPE: one work-group holds all heads of a row (64 per wave pair)
+    # multiples of 128: one work-group holds all heads of a row (64 per wave pair)
     (9, 128, 700, [700, 1, 33, 64, 65, 512, 513, 95, 640], 0.0),  # grid with empty ids (B % 8 != 0)
     (2, 256, 333, [333, 32], 0.0),     # two 128-head groups
-    (2, 128, 200, [200, 77], 1e4),     # with RoPE: the pair kernel
+    (2, 128, 200, [200, 77], 1e4),     # q^R rotated in-kernel, with its bf16 residual products
+    (9, 128, 700, [700, 1, 33, 64, 65, 512, 513, 95, 640], 1e4),
+    (2, 256, 333, [333, 32], 5e5),
 ]
 
 
@@ -226,8 +228,8 @@ def test_mla_decode_single_chunk(Nh):
 
 @pytest.mark.parametrize("B,T,ctx,rope,Nh", [(2, 300, [300, 200], 0.0, 64), (2, 300, [300, 260], 1e4, 64),
                                              (256, 160, None, 0.0, 64), (2, 300, [300, 200], 0.0, 128),
-                                             (256, 160, None, 0.0, 128)],
-                         ids=["splits", "rope", "one-chunk", "h128-splits", "h128-one-chunk"])
+                                             (256, 160, None, 0.0, 128), (2, 300, [300, 260], 1e4, 128)],
+                         ids=["splits", "rope", "one-chunk", "h128-splits", "h128-one-chunk", "h128-rope"])
 def test_mla_decode_score_growth_beyond_reference(B, T, ctx, rope, Nh):
     """Scores that grow far past the first tile's max (the decoupled k^R dims of later tokens
     scaled by 200, so V = c^KV stays of order one): such heads leave the fast path's fixed
@@ -338,6 +340,15 @@ def test_mla_decode_full():
     got = _gpu_decode(q, kc, None, ctx, scale=w.scale, mla=True)
     want = _oracle_decode(q, kc, None, ctx, scale=w.scale, mla=True)
     assert got.shape == (32, 128, 512)
+    assert max_abs(got, want) <= BF16_TOL
+
+
+def test_mla_decode_full_rope():
+    """The full MLA-absorbed decode with the decoupled q^R rotated in-kernel at position ctx-1."""
+    w = synth.MLA_DECODE
+    q, kc, _, ctx = w.inputs()
+    got = _gpu_decode(q, kc, None, ctx, scale=w.scale, rope=1e4, mla=True)
+    want = _oracle_decode(q, kc, None, ctx, scale=w.scale, rope=1e4, mla=True)
     assert max_abs(got, want) <= BF16_TOL
 
 

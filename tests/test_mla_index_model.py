@@ -183,7 +183,7 @@ def test_exchange_buffer_layout():
     assert seen == set(range(WAVES * 4 * 64 * 4))
 
 
-# ---- the 128-heads-per-work-group kernel (head counts that are multiples of 128, no RoPE) ----
+# ---- the 128-heads-per-work-group kernel (head counts that are multiples of 128) ----
 
 def wide_id_map(B, nsplit, n_hg):
     """Work-group id -> (sequence, chunk, head group) or None, as the wide kernel computes it."""
@@ -324,3 +324,28 @@ def test_wide_query_staging_through_the_ring():
                 for par in range(2):
                     lanes = [l for l in range(64) if (l >> 5) == b5 and bin((l >> 2) & 7).count("1") % 2 == par]
                     assert _pass_conflicts([addrs[l] for l in lanes], 16, 16) == 0
+
+
+def test_wide_rope_pairs_and_residual_operands():
+    """In-kernel q^R RoPE in the wide kernel: lane (col, hf) holds dims 16kk + 8hf .. +7 in query
+    register kk, so the rotation partners 512 + i and 544 + i (i = 16u + 8hf + j) sit in the same
+    lane, in registers 32 + u and 34 + u (u = 0, 1), with i0 = 16u + 8hf as the rotation is called.
+    After the 36-step chain with four K operands in flight (slot kk % 4 refilled with k-step kk + 4
+    while kk + 4 < 36), slot (32 + u) % 4 still holds k-step 32 + u: the residual products pair the
+    residual of register 32 + u with the K dims it was rotated for."""
+    DV_ = 512
+    for hf in range(2):
+        for u in range(2):
+            i0 = 16 * u + 8 * hf
+            for j in range(8):
+                a = 16 * (32 + u) + 8 * hf + j
+                b = 16 * (34 + u) + 8 * hf + j
+                assert a == DV_ + i0 + j and b == DV_ + 32 + i0 + j
+    KR, KS = 4, 36
+    slot = [kk for kk in range(KR)]
+    for kk in range(KS):
+        assert slot[kk % KR] == kk  # the product of k-step kk reads its own K operand
+        if kk + KR < KS:
+            slot[kk % KR] = kk + KR
+    for u in range(4):
+        assert slot[(KS - 4 + u) % KR] == KS - 4 + u
