@@ -62,13 +62,21 @@ __device__ __forceinline__ float rows_sum(float x) {
   return pair_sum32(__uint_as_float(r[0]) + __uint_as_float(r[1]));
 }
 
+// Angle of the decoupled RoPE at position pos for frequency index f = lane % 32: (sin, cos) of
+// pos * theta^(-2f/64) in fp64. One position serves every query head of a sequence, so the 32
+// angles are evaluated once per wave (one per lane) and rope_qr_hilo fetches the ones it needs
+// from the lanes that hold them; every lane of the wave calls both.
+__device__ __forceinline__ void rope_lane_angle(int pos, double theta, double& sn, double& cs) {
+  const double k2 = -2.0 * log2(theta) / (double)(DQ - DV);
+  sincos((double)pos * exp2(k2 * (double)(threadIdx.x & 31)), &sn, &cs);
+}
+
 // decoupled RoPE of one lane's q^R pairs: dims 512 + i held in `a` (i = i0 .. i0+7), their
-// half-split partners 544 + i in `b`; frequency theta^(-2i/64), position pos. The rotated fp32
+// half-split partners 544 + i in `b`, rotated by the angles of rope_lane_angle. The rotated fp32
 // value x is kept as two bf16 numbers, hi = bf16(x) in a / b and lo = bf16(x - hi) in alo / blo
 // (x - hi is exact in fp32): the products then see q^R to ~2^-17 instead of bf16's 2^-9, which
 // matters when k^R is large and the softmax is nearly one-hot.
-__device__ __forceinline__ void rope_qr_hilo(U4& a, U4& b, U4& alo, U4& blo, int i0, int pos, double theta) {
-  const double k2 = -2.0 * log2(theta) / (double)(DQ - DV);
+__device__ __forceinline__ void rope_qr_hilo(U4& a, U4& b, U4& alo, U4& blo, int i0, double sn_l, double cs_l) {
   uint32_t* pa = &a.x;
   uint32_t* pb = &b.x;
   uint32_t* la = &alo.x;
@@ -78,8 +86,7 @@ __device__ __forceinline__ void rope_qr_hilo(U4& a, U4& b, U4& alo, U4& blo, int
     float ra[2], rb[2];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      double sn, cs;
-      sincos((double)pos * exp2(k2 * (double)(i0 + 2 * e + hf)), &sn, &cs);
+      const double sn = __shfl(sn_l, i0 + 2 * e + hf), cs = __shfl(cs_l, i0 + 2 * e + hf);
       const double x = hf ? bf16hi(pa[e]) : bf16lo(pa[e]);
       const double y = hf ? bf16hi(pb[e]) : bf16lo(pb[e]);
       ra[hf] = (float)(x * cs - y * sn);
@@ -139,7 +146,9 @@ __global__ __launch_bounds__(NW * 64, (NW >= 8 ? 2 : 1)) void decode_mla_kernel(
       // decoupled RoPE on the q^R block (dims 512..575, slide 06 of "Transformer 与 LLM"): half-split
       // pairs (512 + i, 544 + i), frequency theta^(-2i/64), position ctx-1; the cache holds rotated
       // k^R. Dims 512 + rg*8 + j sit in raw[16], their partners in raw[17] of the same lane.
-      rope_qr_hilo(raw[DV / 32], raw[DV / 32 + 1], lo[0], lo[1], rg * 8, ctx - 1, a.rope_theta);
+      double sn, cs;
+      rope_lane_angle(ctx - 1, a.rope_theta, sn, cs);
+      rope_qr_hilo(raw[DV / 32], raw[DV / 32 + 1], lo[0], lo[1], rg * 8, sn, cs);
     }
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) qreg[kk] = as_bf16x8(raw[kk]);
@@ -389,8 +398,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_pair_kernel(DecodeA
     if (kRope && r == 1) {
       // q^R = dims 512..575 = k-steps 14..17 of the upper half: dims 512 + 16u + 8hf + j in
       // raw[14 + u], their partners 544 + 16u + 8hf + j in raw[16 + u]
-      rope_qr_hilo(raw[14], raw[16], lo[0], lo[2], hf * 8, ctx - 1, a.rope_theta);
-      rope_qr_hilo(raw[15], raw[17], lo[1], lo[3], 16 + hf * 8, ctx - 1, a.rope_theta);
+      double sn, cs;
+      rope_lane_angle(ctx - 1, a.rope_theta, sn, cs);
+      rope_qr_hilo(raw[14], raw[16], lo[0], lo[2], hf * 8, sn, cs);
+      rope_qr_hilo(raw[15], raw[17], lo[1], lo[3], 16 + hf * 8, sn, cs);
     }
 #pragma unroll
     for (int kk = 0; kk < kKS; ++kk) qreg[kk] = as_bf16x8(raw[kk]);
@@ -820,8 +831,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void decode_mla_wide_kernel(DecodeA
       ra[u] = __builtin_bit_cast(U4, qreg[kKS - 4 + u]);
       lo[u] = U4{0, 0, 0, 0};
     }
-    rope_qr_hilo(ra[0], ra[2], lo[0], lo[2], hf * 8, ctx - 1, a.rope_theta);
-    rope_qr_hilo(ra[1], ra[3], lo[1], lo[3], 16 + hf * 8, ctx - 1, a.rope_theta);
+    double sn, cs;
+    rope_lane_angle(ctx - 1, a.rope_theta, sn, cs);
+    rope_qr_hilo(ra[0], ra[2], lo[0], lo[2], hf * 8, sn, cs);
+    rope_qr_hilo(ra[1], ra[3], lo[1], lo[3], 16 + hf * 8, sn, cs);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       qreg[kKS - 4 + u] = as_bf16x8(ra[u]);
