@@ -139,8 +139,13 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     const uint16_t* qp = a.q + ((long long)b * a.Nh + h0 + (real ? hc : 0)) * D + rg * 8;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) raw[kk] = real ? ldg16(qp + kk * 32) : U4{0, 0, 0, 0};
-    if (a.rope_theta > 0 && real) {
+    if (a.rope_theta > 0) {
+      // one position for every head: lane l evaluates the angle of frequency l % (D/2) once (fp64),
+      // the pairs fetch theirs from the lane that holds it (every lane takes part; the padding
+      // lanes rotate zeros)
       const double k2 = -2.0 * log2(a.rope_theta) / (double)D;
+      double sn_l, cs_l;
+      sincos((double)(ctx - 1) * exp2(k2 * (double)(lane % (D / 2))), &sn_l, &cs_l);
 #pragma unroll
       for (int kk = 0; kk < NKK / 2; ++kk) {
         uint32_t* pa = &raw[kk].x;
@@ -151,8 +156,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
             const int i = kk * 32 + rg * 8 + 2 * e + hf;  // pair (i, i + D/2)
-            double sn, cs;
-            sincos((double)(ctx - 1) * exp2(k2 * (double)i), &sn, &cs);
+            const double sn = __shfl(sn_l, i), cs = __shfl(cs_l, i);
             const double x = hf ? bf16hi(pa[e]) : bf16lo(pa[e]);
             const double y = hf ? bf16hi(pb[e]) : bf16lo(pb[e]);
             ra[hf] = (float)(x * cs - y * sn);
