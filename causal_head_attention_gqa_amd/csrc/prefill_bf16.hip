@@ -95,15 +95,18 @@ __global__ __launch_bounds__(kThreads, (DQK > 128 ? 2 : 3)) void prefill_bf16_ke
   const int HGn = Nh / HPW;
   const int id = blockIdx.x;
   // block order: work-group id runs on XCD id % 8. When the (sequence, head group) pairs split evenly
-  // over the 8 XCDs, XCD x takes its pairs x, x + 8, ... one after the other, each pair's q-tiles
-  // heaviest first, so the work-groups resident on an XCD share one pair's K/V in its L2; otherwise
-  // the heaviest q-tiles of all pairs go first.
+  // over the 8 XCDs, XCD x owns the pairs x, x + 8, ... and takes their q-tiles q-tile-major,
+  // heaviest first across those pairs: its resident work-groups share a few pairs' K/V in its L2,
+  // and its last work-groups are light ones (taking its pairs one after another instead left the
+  // last pair's heavy q-tiles running alone at the end). Otherwise the heaviest q-tiles of all
+  // pairs go first.
   const int npairs = B * HGn;
   int bh, pt;
   if (npairs % 8 == 0) {
     const int li = id / 8;
-    bh = id % 8 + 8 * (li / n_ptiles);
-    pt = n_ptiles - 1 - li % n_ptiles;
+    const int ppx = npairs / 8;  // pairs per XCD
+    bh = id % 8 + 8 * (li % ppx);
+    pt = n_ptiles - 1 - li / ppx;
   } else {
     bh = id % npairs;
     pt = n_ptiles - 1 - id / npairs;

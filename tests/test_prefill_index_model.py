@@ -115,8 +115,9 @@ def grid_map(B, S, Nh, HPW, n_ptiles):
     ids = np.arange(n_ptiles * npairs, dtype=np.int64)
     if npairs % 8 == 0:
         li = ids // 8
-        bh = ids % 8 + 8 * (li // n_ptiles)
-        pt = n_ptiles - 1 - li % n_ptiles
+        ppx = npairs // 8
+        bh = ids % 8 + 8 * (li % ppx)
+        pt = n_ptiles - 1 - li // ppx
     else:
         bh = ids % npairs
         pt = n_ptiles - 1 - ids // npairs
@@ -253,3 +254,19 @@ def test_split_key_grid_covers_every_block_tile_once(KS, S, causal):
         ring = KS * 2 * 2 * 32 * D * 2
         merge = 4 * (32 * (D + 4) + 64) * 4
         assert per_cu * max(ring, merge) <= 160 * 1024 or KS != 2
+
+
+def test_block_order_is_heaviest_first_on_every_xcd():
+    """Llama-3-8B shape (32 (sequence, head group) pairs): work-group id runs on XCD id % 8; each XCD
+    holds only its own pairs (x, x + 8, ...), and in launch order its q-tiles never get heavier, so
+    its last work-groups are the lightest ones of all its pairs."""
+    B, S, Nh, HPW = 4, 8192, 32, 4
+    n_ptiles = S // 32
+    b, h0, pt = grid_map(B, S, Nh, HPW, n_ptiles)
+    bh = b * (Nh // HPW) + h0 // HPW
+    ids = np.arange(len(pt))
+    for x in range(8):
+        sel = ids % 8 == x
+        assert set(np.unique(bh[sel])) == {x, x + 8, x + 16, x + 24}
+        assert np.all(np.diff(pt[sel]) <= 0)
+        assert pt[sel][-1] == 0 and pt[sel][0] == n_ptiles - 1
