@@ -118,11 +118,14 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   // after them). The KV heads of one token sit side by side in a cache row, so consecutive
   // work-groups (dispatched to different XCDs at the same time) read the neighbouring segments of
   // the same rows together: +12 % bandwidth over a chunk-fastest order, which fetched each head's
-  // 256-byte segments of a row at different times.
+  // 256-byte segments of a row at different times. The head group is rotated by the sequence
+  // index, so that a work-group id's XCD (id % 8) reads different KV heads of different sequences:
+  // with one KV head per XCD (each reading one fixed 256-byte slice of every row) some XCDs ran
+  // ~15 % longer than others on the same work.
   const int nhg = a.Nkv * n_hg;
-  const int hgi = blockIdx.x % nhg;
   int b, s;
   if (!decode_item(a, blockIdx.x / nhg, b, s)) return;  // past the last item
+  const int hgi = (int)((blockIdx.x + (unsigned)b) % (unsigned)nhg);
   const int g = hgi / n_hg;
   const int h0 = g * G + (hgi % n_hg) * HG;
   const int ctx = min(max(a.ctx_lens[b], 0), a.max_ctx);

@@ -95,17 +95,21 @@ __global__ __launch_bounds__(kThreads, (DQK > 128 ? 2 : 3)) void prefill_bf16_ke
   const int HGn = Nh / HPW;
   const int id = blockIdx.x;
   // block order: work-group id runs on XCD id % 8. When the (sequence, head group) pairs split evenly
-  // over the 8 XCDs, XCD x owns the pairs x, x + 8, ... and takes their q-tiles q-tile-major,
-  // heaviest first across those pairs: its resident work-groups share a few pairs' K/V in its L2,
-  // and its last work-groups are light ones (taking its pairs one after another instead left the
-  // last pair's heavy q-tiles running alone at the end). Otherwise the heaviest q-tiles of all
-  // pairs go first.
+  // over the 8 XCDs, XCD x owns one pair of each block of 8 consecutive pairs, pair 8j + (x + j) % 8
+  // of block j, and takes their q-tiles q-tile-major, heaviest first across those pairs: its
+  // resident work-groups share a few pairs' K/V in its L2, and its last work-groups are light ones
+  // (taking its pairs one after another instead left the last pair's heavy q-tiles running alone at
+  // the end). The rotation by j gives an XCD different KV heads of different sequences (pair x of
+  // every block would be KV head x of every sequence: one 256-byte slice of every cache row, which
+  // made those XCDs measurably slower than the others). Otherwise the heaviest q-tiles of all pairs
+  // go first.
   const int npairs = B * HGn;
   int bh, pt;
   if (npairs % 8 == 0) {
     const int li = id / 8;
     const int ppx = npairs / 8;  // pairs per XCD
-    bh = id % 8 + 8 * (li % ppx);
+    const int j = li % ppx;
+    bh = 8 * j + (id % 8 + j) % 8;
     pt = n_ptiles - 1 - li / ppx;
   } else {
     bh = id % npairs;

@@ -93,3 +93,26 @@ def test_items_cover_every_chunk_once_longest_first(B, chunk, max_ctx, recipe):
     ctxc = np.clip(ctx, 0, max_ctx)
     for b, s in want:
         assert 0 <= b < B and 0 <= s < nsplit and s * chunk < ctxc[b]
+
+
+@pytest.mark.parametrize("nhg", [8, 16, 1, 2, 4, 3])
+def test_head_groups_rotate_over_xcds_and_cover_each_item(nhg):
+    """The GQA split kernel's head group of work-group id: (id + b) % nhg, where b is the sequence of
+    item id // nhg. Every item's nhg work-groups take every head group once (nothing skipped,
+    nothing twice), and with 8 KV heads the XCD of an id (id % 8) reads different KV heads for
+    different sequences instead of one fixed 256-byte slice of every cache row."""
+    ctx = np.array([5000, 1024, 8192, 3000, 17, 4096, 2048, 6000, 7000], np.int32)
+    max_ctx, chunk = 8192, 1024
+    nsplit = max_ctx // chunk
+    seen_by_xcd = {x: set() for x in range(8)}
+    for item in range(len(ctx) * nsplit):
+        it = decode_item(ctx, max_ctx, chunk, item)
+        if it is None:
+            continue
+        b, s = it
+        hg = [(item * nhg + t + b) % nhg for t in range(nhg)]
+        assert sorted(hg) == list(range(nhg))
+        for t in range(nhg):
+            seen_by_xcd[(item * nhg + t) % 8].add(hg[t])
+    if nhg == 8:
+        assert all(len(v) == 8 for v in seen_by_xcd.values())

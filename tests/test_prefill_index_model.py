@@ -116,7 +116,8 @@ def grid_map(B, S, Nh, HPW, n_ptiles):
     if npairs % 8 == 0:
         li = ids // 8
         ppx = npairs // 8
-        bh = ids % 8 + 8 * (li % ppx)
+        j = li % ppx
+        bh = 8 * j + (ids % 8 + j) % 8
         pt = n_ptiles - 1 - li // ppx
     else:
         bh = ids % npairs
@@ -258,15 +259,21 @@ def test_split_key_grid_covers_every_block_tile_once(KS, S, causal):
 
 def test_block_order_is_heaviest_first_on_every_xcd():
     """Llama-3-8B shape (32 (sequence, head group) pairs): work-group id runs on XCD id % 8; each XCD
-    holds only its own pairs (x, x + 8, ...), and in launch order its q-tiles never get heavier, so
-    its last work-groups are the lightest ones of all its pairs."""
+    holds four pairs of its own, one KV head of each sequence, four different KV heads; and in
+    launch order its q-tiles never get heavier, so its last work-groups are the lightest ones of
+    all its pairs."""
     B, S, Nh, HPW = 4, 8192, 32, 4
     n_ptiles = S // 32
     b, h0, pt = grid_map(B, S, Nh, HPW, n_ptiles)
     bh = b * (Nh // HPW) + h0 // HPW
     ids = np.arange(len(pt))
+    owner = {}
     for x in range(8):
         sel = ids % 8 == x
-        assert set(np.unique(bh[sel])) == {x, x + 8, x + 16, x + 24}
+        pairs = set(np.unique(bh[sel]).tolist())
+        assert len(pairs) == 4 and not any(p in owner for p in pairs)
+        owner.update({p: x for p in pairs})
+        assert sorted(np.unique(b[sel]).tolist()) == [0, 1, 2, 3]
+        assert len(np.unique(h0[sel])) == 4
         assert np.all(np.diff(pt[sel]) <= 0)
         assert pt[sel][-1] == 0 and pt[sel][0] == n_ptiles - 1
