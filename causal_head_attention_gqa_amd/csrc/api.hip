@@ -132,12 +132,20 @@ const char* attn_status_str(int status) {
   }
 }
 
-size_t attn_prefill_workspace_bytes(int B, int S, int Nkv, int Dh, float rope_theta, int dtype) {
+// Workspace bytes attn_prefill cannot run without: the RoPE angle table and the rotated K copy.
+size_t prefill_rope_bytes(int B, int S, int Nkv, int Dh, float rope_theta, int dtype) {
   if (!(rope_theta > 0.f) || B <= 0 || S <= 0 || Nkv <= 0 || Dh <= 0) return 0;
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return 0;
   const size_t table = align_up((size_t)S * (size_t)(Dh / 2) * sizeof(float2));
   const size_t krot = align_up((size_t)B * (size_t)S * (size_t)Nkv * (size_t)Dh * esize(dtype));
   return table + krot;
+}
+
+size_t attn_prefill_workspace_bytes(int B, int S, int Nkv, int Dh, float rope_theta, int dtype) {
+  if (B <= 0 || S <= 0 || Nkv <= 0 || Dh <= 0) return 0;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return 0;
+  // bf16: the work lists' counters after the RoPE part
+  return prefill_rope_bytes(B, S, Nkv, Dh, rope_theta, dtype) + (dtype == ATTN_BF16 ? kPrefillQueueBytes : 0);
 }
 
 int attn_prefill(const void* q, const void* k, const void* v, void* out, int B, int S, int Nh, int Nkv, int Dh,
@@ -155,9 +163,13 @@ int attn_prefill(const void* q, const void* k, const void* v, void* out, int B, 
   if (!q || !k || !v || !out) return ATTN_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_ERR_INVALID;
   const bool rope = rope_theta > 0.f;
-  const size_t need = attn_prefill_workspace_bytes(B, S, Nkv, Dh, rope_theta, dtype);
+  // the RoPE part is required; the counters after it are optional (without them, or without any
+  // workspace when there is no RoPE, each work-group's item follows from its id)
+  const size_t need = prefill_rope_bytes(B, S, Nkv, Dh, rope_theta, dtype);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
     return ATTN_ERR_WORKSPACE;
+  const bool lists = dtype == ATTN_BF16 && workspace != nullptr && aligned16(workspace) &&
+                     workspace_bytes >= need + kPrefillQueueBytes;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const double sc = scale > 0.f ? (double)scale : 1.0 / std::sqrt((double)Dh);
@@ -187,6 +199,7 @@ int attn_prefill(const void* q, const void* k, const void* v, void* out, int B, 
   a.sinks = 0;
   a.rope_dims = Dh;
   a.rope_inter = 0;
+  a.queue = lists ? reinterpret_cast<unsigned int*>(static_cast<char*>(workspace) + need) : nullptr;
 
   if (rope) {
     float2* table = static_cast<float2*>(workspace);

@@ -60,7 +60,11 @@ struct PrefillArgs {
   int sinks;           // with a window: keys 0 .. sinks-1 stay visible to every later query
   int rope_dims;       // with a table: rotary span = the leading rope_dims dims (multiple of 32)
   int rope_inter;      // with a table: adjacent pairs (2j, 2j+1) instead of (i, i + rope_dims/2)
+  // bf16 path: kPrefillQueueBytes of device memory for the work lists' counters (zeroed at the
+  // launch), or nullptr: each work-group's item follows from its id
+  unsigned int* queue;
 };
+constexpr size_t kPrefillQueueBytes = 256;
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t st);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st);
 

@@ -69,7 +69,7 @@ __global__ __launch_bounds__(kThreads, (DQK > 128 ? 2 : 3)) void prefill_bf16_ke
     uint16_t* __restrict__ out, const float2* __restrict__ table, int B, int S, int Nh, int Nkv, float c,
     int causal, int n_ptiles, long long kv_tok, long long kv_batch, int kv_head, const int* __restrict__ q_start,
     int max_keys, int window, int sinks, int rope_dims, int rope_inter, long long v_tok, long long v_batch,
-    int v_head) {
+    int v_head, unsigned int* __restrict__ lists) {
   constexpr int BP = 32 * (4 / HPW);        // query positions per work-group
   constexpr int CHK = DQK / 8;              // 16-byte chunks per K row
   constexpr int CHV = DV / 8;               // 16-byte chunks per V row
@@ -93,25 +93,60 @@ __global__ __launch_bounds__(kThreads, (DQK > 128 ? 2 : 3)) void prefill_bf16_ke
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int HGn = Nh / HPW;
-  const int id = blockIdx.x;
-  // block order: work-group id runs on XCD id % 8. When the (sequence, head group) pairs split evenly
-  // over the 8 XCDs, XCD x owns one pair of each block of 8 consecutive pairs, pair 8j + (x + j) % 8
-  // of block j, and takes their q-tiles q-tile-major, heaviest first across those pairs: its
-  // resident work-groups share a few pairs' K/V in its L2, and its last work-groups are light ones
-  // (taking its pairs one after another instead left the last pair's heavy q-tiles running alone at
-  // the end). The rotation by j gives an XCD different KV heads of different sequences (pair x of
-  // every block would be KV head x of every sequence: one 256-byte slice of every cache row, which
-  // made those XCDs measurably slower than the others). Otherwise the heaviest q-tiles of all pairs
-  // go first.
+  // Work item: (sequence, head group) pair x q-tile. Work-group id runs on XCD id % 8. When the pairs
+  // split evenly over the 8 XCDs, XCD x owns one pair of each block of 8 consecutive pairs, pair
+  // 8j + (x + j) % 8 of block j, and its list of items goes q-tile-major, heaviest first across those
+  // pairs: its resident work-groups share a few pairs' K/V in its L2, and its last work-groups are
+  // light ones (taking its pairs one after another instead left the last pair's heavy q-tiles running
+  // alone at the end). The rotation by j gives an XCD different KV heads of different sequences (pair
+  // x of every block would be KV head x of every sequence: one 256-byte slice of every cache row,
+  // which made those XCDs measurably slower than the others). Otherwise the heaviest q-tiles of all
+  // pairs go first.
+  // Without counters (lists == nullptr) item i of list x is work-group 8i + x. The XCDs run at
+  // different clocks, though, and a fixed share leaves the fast ones idle at the end; with counters
+  // (8, 64 bytes apart, zeroed before the launch; the grid has an eighth more work-groups than
+  // items) a work-group claims the next item of its XCD's list and, once that is used up, of the
+  // first list (in rotation order from its own) that still has items; with none left it exits.
   const int npairs = B * HGn;
   int bh, pt;
   if (npairs % 8 == 0) {
-    const int li = id / 8;
     const int ppx = npairs / 8;  // pairs per XCD
-    const int j = li % ppx;
-    bh = 8 * j + (id % 8 + j) % 8;
-    pt = n_ptiles - 1 - li / ppx;
+    const int per_x = ppx * n_ptiles;
+    int x = (int)(blockIdx.x % 8u), c = (int)(blockIdx.x / 8u);
+    if (lists != nullptr) {
+      __shared__ int s_item;
+      if (w == 0) {
+        int it = -1;
+        unsigned int c0 = 0;
+        if (lane == 0) c0 = atomicAdd(&lists[x * 16], 1u);
+        c0 = __shfl(c0, 0);
+        if (c0 < (unsigned int)per_x) it = x * per_x + (int)c0;
+        // every failed claim finds one more list used up, so 8 rounds bound the search
+        for (int round = 0; it < 0 && round < 8; ++round) {
+          const unsigned int used =
+              lane < 8 ? __hip_atomic_load(&lists[lane * 16], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+          const unsigned long long open = __ballot(lane < 8 && used < (unsigned int)per_x);
+          if (open == 0) break;
+          const unsigned long long rot = ((open >> x) | (open << (8 - x))) & 0xffull;  // bit k: list (x+k)%8
+          const int xk = (x + __builtin_ctzll(rot)) & 7;
+          unsigned int ck = 0;
+          if (lane == 0) ck = atomicAdd(&lists[xk * 16], 1u);
+          ck = __shfl(ck, 0);
+          if (ck < (unsigned int)per_x) it = xk * per_x + (int)ck;
+        }
+        if (lane == 0) s_item = it;
+      }
+      __syncthreads();
+      const int it = s_item;
+      if (it < 0) return;  // every list used up (the whole work-group leaves)
+      x = it / per_x;
+      c = it % per_x;
+    }
+    const int j = c % ppx;
+    bh = 8 * j + (x + j) % 8;
+    pt = n_ptiles - 1 - c / ppx;
   } else {
+    const int id = blockIdx.x;
     bh = id % npairs;
     pt = n_ptiles - 1 - id / npairs;
   }
@@ -426,6 +461,11 @@ __global__ __launch_bounds__(kThreads, (DQK > 128 ? 2 : 3)) void prefill_bf16_ke
         *reinterpret_cast<uint2*>(op + db * 32 + g4 * 8) = wv;
       }
   }
+}
+
+// Zeroes the work lists' counters of prefill_bf16_kernel before its launch.
+__global__ void prefill_lists_reset_kernel(unsigned int* __restrict__ lists) {
+  if (threadIdx.x < 8 * 16) lists[threadIdx.x] = 0u;
 }
 
 // ---- split-key prefill, for grids too small to fill the chip ----
@@ -746,13 +786,19 @@ template <int DQK, int DV, int HPW, bool kCache, bool kWin>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t st) {
   constexpr int BP = 32 * (4 / HPW);
   const int n_ptiles = (a.S + BP - 1) / BP;
-  const long long n_wg = (long long)n_ptiles * a.B * (a.Nh / HPW);
+  const long long npairs = (long long)a.B * (a.Nh / HPW);
+  const long long n_items = (long long)n_ptiles * npairs;
+  // with the work lists (pairs split evenly over the XCDs): an eighth more work-groups, which the
+  // fast XCDs use to take items from the slow ones' lists
+  unsigned int* lists = npairs % 8 == 0 ? a.queue : nullptr;
+  const long long n_wg = lists != nullptr ? n_items + 8 * ((n_items / 8 + 7) / 8) : n_items;
   if (n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (lists != nullptr) prefill_lists_reset_kernel<<<dim3(1), dim3(128), 0, st>>>(lists);
   prefill_bf16_kernel<DQK, DV, HPW, kCache, kWin><<<dim3((unsigned)n_wg), dim3(kThreads), 0, st>>>(
       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
       static_cast<uint16_t*>(a.out), a.table, a.B, a.S, a.Nh, a.Nkv, a.scale_log2, a.causal, n_ptiles, a.kv_tok,
       a.kv_batch, a.kv_head, a.q_start, a.max_keys, a.window, a.sinks, a.rope_dims, a.rope_inter, a.v_tok, a.v_batch,
-      a.v_head);
+      a.v_head, lists);
   return hipGetLastError();
 }
 

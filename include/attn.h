@@ -65,9 +65,14 @@ const char* attn_status_str(int status);
  * scale <= 0 selects 1 / sqrt(Dh).
  * Supported: ATTN_BF16 with Dh in {64, 128}; ATTN_F32 with Dh in {16, 32, 64}.
  * B == 0 or S == 0 is a valid empty call (nothing launched).
- * workspace: device buffer of at least attn_prefill_workspace_bytes(...) bytes (may be NULL
- *   when that figure is 0). Its contents are scratch; it must not be used by another call
- *   until this one has completed on `stream`.
+ * workspace: device buffer of attn_prefill_workspace_bytes(...) bytes. With RoPE its leading part
+ *   (the angle table and the rotated keys) is required: a smaller or NULL workspace is
+ *   ATTN_ERR_WORKSPACE. For ATTN_BF16 the figure ends with 256 bytes of work-list counters, which
+ *   are optional: with them, XCDs that run faster take q-tiles left in the slower XCDs' lists;
+ *   without them (a workspace just short of the figure, or NULL without RoPE) every q-tile has a
+ *   fixed work-group. The output is the same bits either way. The contents are scratch, set by
+ *   the call where it needs them; the workspace must not be used by another call until this one
+ *   has completed on `stream`.
  * ------------------------------------------------------------------------------------------ */
 size_t attn_prefill_workspace_bytes(int B, int S, int Nkv, int Dh, float rope_theta, int dtype);
 

@@ -102,9 +102,11 @@ def test_rope_argument_errors():
 def test_workspace_queries():
     from causal_head_attention_gqa_amd import lib
     _lib()
-    assert lib.prefill_workspace_bytes(4, 8192, 8, 128, 0.0, 1) == 0
-    # RoPE: fp32 (cos, sin) table [S, Dh/2] plus rotated keys
-    assert lib.prefill_workspace_bytes(4, 8192, 8, 128, 5e5, 1) == 8192 * 64 * 8 + 4 * 8192 * 8 * 128 * 2
+    # bf16: 256 bytes for the work lists' counters, optional; fp32 has none
+    assert lib.prefill_workspace_bytes(4, 8192, 8, 128, 0.0, 1) == 256
+    assert lib.prefill_workspace_bytes(4, 8192, 8, 64, 0.0, 0) == 0
+    # RoPE: fp32 (cos, sin) table [S, Dh/2] plus rotated keys (required), then the counters
+    assert lib.prefill_workspace_bytes(4, 8192, 8, 128, 5e5, 1) == 8192 * 64 * 8 + 4 * 8192 * 8 * 128 * 2 + 256
     ws = lib.decode_workspace_bytes(64, 32, 8, 128, 128, 8192, 1)
     assert ws > 0 and ws % 256 == 0
     # MLA: split partials (bf16 rows + fp32 max/sum) for 8 chunks of 512 tokens at B = 32 ...

@@ -231,3 +231,40 @@ def test_llama3_prefill_every_head_sampled_rows():
             worst = max(worst, err)
             n_rows += len(rows)
     assert n_rows >= w.B * w.Nh * 256
+
+
+@pytest.mark.parametrize("B,S,Nh,Nkv,rope", [(4, 2048, 32, 8, 5e5), (2, 400, 32, 8, 0.0), (3, 300, 12, 3, 1e4)],
+                         ids=["llama-2048-rope", "32-pairs-400", "9-pairs-rope"])
+def test_work_lists_give_the_static_order_bits(B, S, Nh, Nkv, rope):
+    """The work lists' counters at the end of the workspace only change which work-group computes a
+    q-tile (and let fast XCDs take items from slow ones): the output equals, bit for bit, that of a
+    call whose workspace stops short of them (and, without RoPE, of a call with no workspace), on
+    two calls in a row (the counters are zeroed by each call). 9 pairs do not split over the XCDs:
+    no lists there. Shapes that take the one-item-per-work-group kernel, not the split-key one."""
+    import ctypes
+    import causal_head_attention_gqa_amd as attn
+    from causal_head_attention_gqa_amd import lib
+    torch = __import__("torch")
+    wid = 720 + S
+    q = to_dev(synth.normal(wid, 0, (B, S, Nh, 128), "bf16"), "bf16")
+    k = to_dev(synth.normal(wid, 1, (B, S, Nkv, 128), "bf16"), "bf16")
+    v = to_dev(synth.normal(wid, 2, (B, S, Nkv, 128), "bf16"), "bf16")
+    full = attn.prefill_workspace_bytes(B, S, Nkv, 128, rope, attn.ATTN_BF16)
+    ws = torch.zeros(full, dtype=torch.uint8, device="cuda")
+
+    def call(ws_ptr, ws_len):
+        out = torch.full_like(q, float("nan"))
+        st = attn.load().attn_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, S, Nh, Nkv, 128,
+                                      ctypes.c_float(rope), 1, ctypes.c_float(0.0), attn.ATTN_BF16, ws_ptr,
+                                      ctypes.c_size_t(ws_len), lib._stream_ptr(q.device))
+        assert st == 0
+        torch.cuda.synchronize()
+        return out
+
+    listed = call(ws.data_ptr(), full)
+    static = call(ws.data_ptr(), full - 256)
+    assert torch.isfinite(listed.float()).all()
+    assert torch.equal(listed, static)
+    assert torch.equal(call(ws.data_ptr(), full), static)
+    if rope == 0.0:
+        assert torch.equal(call(None, 0), static)

@@ -277,3 +277,66 @@ def test_block_order_is_heaviest_first_on_every_xcd():
         assert len(np.unique(h0[sel])) == 4
         assert np.all(np.diff(pt[sel]) <= 0)
         assert pt[sel][-1] == 0 and pt[sel][0] == n_ptiles - 1
+
+
+def claim(lists, x, per_x):
+    """One work-group's claim on XCD x, as the kernel makes it (counters are atomic, so any run is
+    some order of whole claims): its own list first, then the first list in rotation order from x
+    whose counter is below per_x; None once every list is used up."""
+    c0 = lists[x]
+    lists[x] += 1
+    if c0 < per_x:
+        return x, c0
+    for _ in range(8):
+        open_ = [k for k in range(8) if lists[(x + k) % 8] < per_x]
+        if not open_:
+            return None
+        xk = (x + open_[0]) % 8
+        ck = lists[xk]
+        lists[xk] += 1
+        if ck < per_x:
+            return xk, ck
+    return None
+
+
+@pytest.mark.parametrize("B,S,Nh,HPW,seed", [(4, 8192, 32, 4, 0), (4, 8192, 32, 4, 1), (2, 640, 32, 4, 2),
+                                             (8, 96, 8, 1, 3)])
+def test_work_lists_cover_every_item_once(B, S, Nh, HPW, seed):
+    """Work lists with stealing: the grid has an eighth more work-groups than items, each XCD gets
+    work-group ids x, x + 8, ...; in any order of the claims (fast XCDs claiming far ahead of slow
+    ones) every item is computed exactly once and every other work-group leaves. The items of a
+    list map to the static order's (pair, q-tile) of that XCD."""
+    rng = np.random.default_rng(seed)
+    HGn = Nh // HPW
+    npairs = B * HGn
+    assert npairs % 8 == 0
+    n_ptiles = (S + 32 * (4 // HPW) - 1) // (32 * (4 // HPW))
+    n_items = n_ptiles * npairs
+    n_wg = n_items + 8 * ((n_items // 8 + 7) // 8)
+    ppx = npairs // 8
+    per_x = ppx * n_ptiles
+    speed = rng.uniform(0.8, 1.2, 8)  # XCD x issues its next claim after 1 / speed[x] time units
+    t = np.zeros(8)
+    nxt = [[i for i in range(n_wg) if i % 8 == x] for x in range(8)]
+    lists = [0] * 8
+    done = []
+    while any(nxt):
+        x = min((x for x in range(8) if nxt[x]), key=lambda x: t[x])
+        nxt[x].pop(0)
+        t[x] += rng.uniform(0.5, 1.5) / speed[x]
+        r = claim(lists, x, per_x)
+        if r is not None:
+            done.append(r)
+    assert len(done) == n_items
+    items = [(xk, c) for xk, c in done]
+    assert len(set(items)) == n_items
+    # the (pair, q-tile) of list xk, position c is the static order's item of XCD xk
+    b, h0, pt = grid_map(B, S, Nh, HPW, n_ptiles)
+    bh_static = (b * HGn + h0 // HPW)
+    static = {(i % 8, i // 8): (bh_static[i], pt[i]) for i in range(n_items)}
+    got = set()
+    for xk, c in items:
+        j = c % ppx
+        got.add((8 * j + (xk + j) % 8, n_ptiles - 1 - c // ppx))
+        assert static[(xk, c)] == (8 * j + (xk + j) % 8, n_ptiles - 1 - c // ppx)
+    assert len(got) == n_items
