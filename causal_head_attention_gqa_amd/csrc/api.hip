@@ -222,9 +222,15 @@ int attn_prefill(const void* q, const void* k, const void* v, void* out, int B, 
                                                                      : launch_prefill_f32(a, st); }));
 }
 
-size_t attn_prefill_mla_workspace_bytes(int B, int S, int Nkv, float rope_theta) {
+// Required part of the MLA prefill's workspace: the k^R angle table and the keys with their rotated k^R.
+size_t prefill_mla_rope_bytes(int B, int S, int Nkv, float rope_theta) {
   if (!(rope_theta > 0.f) || B <= 0 || S <= 0 || Nkv <= 0) return 0;
   return align_up((size_t)S * 32 * sizeof(float2)) + align_up((size_t)B * S * Nkv * 192 * 2);
+}
+
+size_t attn_prefill_mla_workspace_bytes(int B, int S, int Nkv, float rope_theta) {
+  if (B <= 0 || S <= 0 || Nkv <= 0) return 0;
+  return prefill_mla_rope_bytes(B, S, Nkv, rope_theta) + kPrefillQueueBytes;  // then the work lists' counters
 }
 
 int attn_prefill_mla(const void* q, const void* k, const void* v, void* out, int B, int S, int Nh, int Nkv,
@@ -236,9 +242,11 @@ int attn_prefill_mla(const void* q, const void* k, const void* v, void* out, int
   if (B == 0 || S == 0) return ATTN_OK;
   if (!q || !k || !v || !out) return ATTN_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_ERR_INVALID;
-  const size_t need = attn_prefill_mla_workspace_bytes(B, S, Nkv, rope_theta);
+  // the RoPE part is required, the work lists' counters after it optional
+  const size_t need = prefill_mla_rope_bytes(B, S, Nkv, rope_theta);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
     return ATTN_ERR_WORKSPACE;
+  const bool lists = workspace != nullptr && aligned16(workspace) && workspace_bytes >= need + kPrefillQueueBytes;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const double sc = scale > 0.f ? (double)scale : 1.0 / std::sqrt(192.0);
@@ -268,6 +276,7 @@ int attn_prefill_mla(const void* q, const void* k, const void* v, void* out, int
   a.sinks = 0;
   a.rope_dims = 64;
   a.rope_inter = 0;
+  a.queue = lists ? reinterpret_cast<unsigned int*>(static_cast<char*>(workspace) + need) : nullptr;
   if (rope_theta > 0.f) {
     float2* table = static_cast<float2*>(workspace);
     void* krot = static_cast<char*>(workspace) + align_up((size_t)S * 32 * sizeof(float2));
@@ -282,9 +291,15 @@ int attn_prefill_mla(const void* q, const void* k, const void* v, void* out, int
   return hip_status(timed_launch(st, [&] { return launch_prefill_bf16(a, st); }));
 }
 
-size_t attn_prefill_cached_workspace_bytes(int max_ctx, int Dh, float rope_theta) {
+// Required part of the chunked prefill's workspace: the angle table of the query positions.
+size_t prefill_cached_rope_bytes(int max_ctx, int Dh, float rope_theta) {
   if (!(rope_theta > 0.f) || max_ctx <= 0 || Dh <= 0) return 0;
   return align_up((size_t)max_ctx * (size_t)(Dh / 2) * sizeof(float2));
+}
+
+size_t attn_prefill_cached_workspace_bytes(int max_ctx, int Dh, float rope_theta) {
+  if (max_ctx <= 0 || Dh <= 0) return 0;
+  return prefill_cached_rope_bytes(max_ctx, Dh, rope_theta) + kPrefillQueueBytes;  // then the lists' counters
 }
 
 int attn_prefill_cached(const void* q, const void* kcache, const void* vcache, const int32_t* q_start, void* out,
@@ -305,7 +320,10 @@ int attn_prefill_cached(const void* q, const void* kcache, const void* vcache, c
   if (B == 0 || S == 0) return ATTN_OK;
   if (!q || !kcache || !vcache || !q_start || !out) return ATTN_ERR_INVALID;
   if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned16(out)) return ATTN_ERR_INVALID;
-  const size_t need = attn_prefill_cached_workspace_bytes(max_ctx, Dh, rope_theta);
+  // the angle table is required, the work lists' counters after it optional (bf16)
+  const size_t need = prefill_cached_rope_bytes(max_ctx, Dh, rope_theta);
+  const bool lists = dtype == ATTN_BF16 && workspace != nullptr && aligned16(workspace) &&
+                     workspace_bytes >= need + kPrefillQueueBytes;
   if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)))
     return ATTN_ERR_WORKSPACE;
 
@@ -337,6 +355,7 @@ int attn_prefill_cached(const void* q, const void* kcache, const void* vcache, c
   a.sinks = sinks;
   a.rope_dims = rope_dims;
   a.rope_inter = rope_interleaved ? 1 : 0;
+  a.queue = lists ? reinterpret_cast<unsigned int*>(static_cast<char*>(workspace) + need) : nullptr;
   if (rope_theta > 0.f) {
     float2* table = static_cast<float2*>(workspace);
     const hipError_t e = launch_rope_table(table, max_ctx, rope_dims, (double)rope_theta, st);

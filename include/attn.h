@@ -95,8 +95,9 @@ int attn_prefill(const void* q, const void* k, const void* v, void* out,
  *   to the workspace. causal as attn_prefill; scale <= 0 selects 1 / sqrt(192).
  * Supported: bf16 storage (fp32 accumulation), Nh % Nkv == 0.
  * B == 0 or S == 0 is a valid empty call (nothing launched).
- * workspace: at least attn_prefill_mla_workspace_bytes(...) bytes (0 without RoPE): the angle
- *   table and the keys with their rotated k^R block (k itself is never modified).
+ * workspace: attn_prefill_mla_workspace_bytes(...) bytes. With RoPE its leading part, the angle
+ *   table and the keys with their rotated k^R block (k itself is never modified), is required;
+ *   the last 256 bytes are optional work-list counters, as for attn_prefill (same bits either way).
  * ------------------------------------------------------------------------------------------ */
 size_t attn_prefill_mla_workspace_bytes(int B, int S, int Nkv, float rope_theta);
 
@@ -133,7 +134,8 @@ int attn_prefill_mla(const void* q, const void* k, const void* v, void* out, int
  *          a part of the head). It must match the rotation the cached keys received.
  *          scale <= 0 selects 1 / sqrt(Dh).
  * Supported: ATTN_BF16, Dh in {64, 128}, 1 <= S <= max_ctx, ld % 8 == 0, ld >= Dh.
- * workspace: at least attn_prefill_cached_workspace_bytes(...) bytes (the RoPE angle table).
+ * workspace: attn_prefill_cached_workspace_bytes(...) bytes: the RoPE angle table (required with
+ *   RoPE), then 256 bytes of optional work-list counters, as for attn_prefill (same bits either way).
  * With q_start[b] = 0 and S = max_ctx this is exactly attn_prefill on the cached keys.
  * ------------------------------------------------------------------------------------------ */
 size_t attn_prefill_cached_workspace_bytes(int max_ctx, int Dh, float rope_theta);

@@ -160,8 +160,9 @@ def test_kv_append_argument_errors():
 def test_prefill_cached_workspace_query():
     from causal_head_attention_gqa_amd import lib
     _lib()
-    assert lib.prefill_cached_workspace_bytes(8192, 128, 0.0) == 0
-    assert lib.prefill_cached_workspace_bytes(8192, 128, 5e5) == 8192 * 64 * 8
+    # the angle table (required with RoPE), then 256 bytes of optional work-list counters
+    assert lib.prefill_cached_workspace_bytes(8192, 128, 0.0) == 256
+    assert lib.prefill_cached_workspace_bytes(8192, 128, 5e5) == 8192 * 64 * 8 + 256
 
 
 def test_prefill_mla_argument_errors():
@@ -185,9 +186,9 @@ def test_prefill_mla_argument_errors():
 def test_prefill_mla_workspace_query():
     from causal_head_attention_gqa_amd import lib
     _lib()
-    assert lib.prefill_mla_workspace_bytes(1, 4096, 128, 0.0) == 0
+    assert lib.prefill_mla_workspace_bytes(1, 4096, 128, 0.0) == 256  # the optional work-list counters
     # fp32 (cos, sin) table [S, 32] plus keys with the rotated k^R block
-    assert lib.prefill_mla_workspace_bytes(1, 4096, 128, 1e4) == 4096 * 32 * 8 + 4096 * 128 * 192 * 2
+    assert lib.prefill_mla_workspace_bytes(1, 4096, 128, 1e4) == 4096 * 32 * 8 + 4096 * 128 * 192 * 2 + 256
 
 
 class _FakeTensor:
