@@ -282,3 +282,25 @@ def test_llama3_sliding_window_full_size_sampled_rows():
     """Window 4096 + 4 sinks over the whole 8192-token sequence, the size the benchmark times."""
     got, want, rows = _llama3_full_size_rows(4096, 4)
     assert max_abs(got, want) <= BF16_TOL
+
+
+@pytest.mark.parametrize("window,sinks", [(0, 0), (300, 4)], ids=["causal", "window"])
+def test_prefill_cached_work_lists_give_the_static_order_bits(window, sinks):
+    """Chunked prefill against a cache: the optional work-list counters at the end of the workspace
+    only change which work-group takes a q-tile; the output equals, bit for bit, that of a call
+    whose workspace stops short of them (16 (sequence, head group) pairs: one list per XCD)."""
+    import causal_head_attention_gqa_amd as attn
+    torch = __import__("torch")
+    B, S, Nh, Nkv, D, T, theta = 2, 512, 32, 8, 128, 1536, 5e5
+    wid = 940 + window
+    kc = to_dev(synth.normal(wid, 1, (B, T, Nkv, D), "bf16"), "bf16")
+    vc = to_dev(synth.normal(wid, 2, (B, T, Nkv, D), "bf16"), "bf16")
+    q = to_dev(synth.normal(wid, 0, (B, S, Nh, D), "bf16"), "bf16")
+    start = torch.tensor([T - S, 400], dtype=torch.int32, device="cuda")
+    full = attn.prefill_cached_workspace_bytes(T, D, theta)
+    ws = torch.empty(full, dtype=torch.uint8, device="cuda")
+    kw = dict(rope_theta=theta, window=window, sinks=sinks)
+    listed = attn.prefill_cached(q, kc, vc, start, workspace=ws, **kw)
+    static = attn.prefill_cached(q, kc, vc, start, workspace=ws[:full - 256], **kw)
+    assert torch.isfinite(listed.float()).all()
+    assert torch.equal(listed, static)

@@ -94,3 +94,19 @@ def test_mla_prefill_full_size_sampled_rows():
     for h in heads:
         want = oracle.prefill_rows(qv, kv, vv, 0, int(h), rows, rope_theta=w.rope_theta)
         assert max_abs(out[0, rows, h], want) <= BF16_TOL, h
+
+
+def test_mla_prefill_work_lists_give_the_static_order_bits():
+    """The optional work-list counters at the end of the workspace only change which work-group takes
+    a q-tile: the output equals, bit for bit, that of a call whose workspace stops short of them
+    (64 (sequence, head) pairs: one list per XCD)."""
+    import causal_head_attention_gqa_amd as attn
+    torch = __import__("torch")
+    B, S, Nh, Nkv, rope = 2, 600, 32, 32, 1e4
+    q, k, v = (to_dev(t, "bf16") for t in _inputs(640, B, S, Nh, Nkv))
+    full = attn.prefill_mla_workspace_bytes(B, S, Nkv, rope)
+    ws = torch.empty(full, dtype=torch.uint8, device="cuda")
+    listed = attn.prefill_mla(q, k, v, rope_theta=rope, workspace=ws)
+    static = attn.prefill_mla(q, k, v, rope_theta=rope, workspace=ws[:full - 256])
+    assert torch.isfinite(listed.float()).all()
+    assert torch.equal(listed, static)
