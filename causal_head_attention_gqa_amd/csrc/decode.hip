@@ -41,20 +41,29 @@ __device__ __forceinline__ float rows_max4(float x) {
   return pair_max32(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
 }
 
-// Work item `item` of the split kernel, in the order the work-groups are dispatched: first every
-// sequence's full chunks (sequence-major), then the shorter last chunks of the sequences whose
-// context is not a multiple of the chunk, also sequence-major. Putting the short items last leaves
-// fewer compute units idle while the last items drain: -3.5 to -5 % decode time against the plain
-// sequence-major order of all chunks. Ordering the short chunks by length as well (longest or
-// shortest band first) measured slower than keeping them in sequence order. Returns false past the
-// last item. Called by every lane of a wave with the same `item`; the result is uniform over it.
+// Chunks of a context: n = ceil(ctx / chunk) of ceil(ctx / n) tokens each (the last one up to n - 1
+// tokens shorter): a context of 1025 tokens is two chunks of 513 and 512 tokens, not 1024 and 1.
+// The chunk count (and so the merge) is that of fixed chunks; all chunks hold chunk/2 .. chunk tokens.
+__device__ __forceinline__ void chunk_plan(int ctx, int chunk, int& n, int& len) {
+  n = (ctx + chunk - 1) / chunk;
+  len = n > 0 ? (ctx + n - 1) / n : 0;
+}
+
+// Work item `item` of the split kernel, in the order the work-groups are dispatched: sequence-major,
+// the chunks of a sequence together. With fixed chunks the random-length last chunks formed a round
+// of their own after the full ones (every slot finishing its last full chunk at the same time, then
+// one short chunk each, ending 0 .. 1 chunk apart); with balanced chunks the lengths are spread over
+// the whole grid: -1.7 % split-kernel time in a same-box A/B (a second ordering by length class
+// gained no more). Returns false past the last item. Called by every lane of a wave with the same
+// `item`; the result is uniform over it.
 __device__ __forceinline__ bool decode_item(const DecodeArgs& a, int item, int& b_out, int& s_out) {
   const int lane = threadIdx.x & 63;
-  int before = 0;  // full chunks of the sequences before this block of 64
+  int before = 0;  // chunks of the sequences before this block of 64
   for (int b0 = 0; b0 < a.B; b0 += 64) {
     const int b = b0 + lane;
     const int ctx = b < a.B ? min(max(a.ctx_lens[b], 0), a.max_ctx) : 0;
-    const int f = ctx / a.chunk;
+    int f, len;
+    chunk_plan(ctx, a.chunk, f, len);
     int incl = f;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -69,22 +78,6 @@ __device__ __forceinline__ bool decode_item(const DecodeArgs& a, int item, int& 
       return true;
     }
     before += total;
-  }
-  int j = item - before;  // index among the short last chunks
-  for (int b0 = 0; b0 < a.B; b0 += 64) {
-    const int b = b0 + lane;
-    const int ctx = b < a.B ? min(max(a.ctx_lens[b], 0), a.max_ctx) : 0;
-    const bool part = ctx % a.chunk != 0;
-    const unsigned long long m = __ballot(part);
-    const int cnt = __popcll(m);
-    if (j < cnt) {
-      const bool hit = part && (int)__popcll(m & ((1ull << lane) - 1)) == j;
-      const int l = __builtin_ctzll(__ballot(hit));
-      b_out = b0 + l;
-      s_out = __shfl(ctx, l) / a.chunk;
-      return true;
-    }
-    j -= cnt;
   }
   return false;
 }
@@ -129,9 +122,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   const int g = hgi / n_hg;
   const int h0 = g * G + (hgi % n_hg) * HG;
   const int ctx = min(max(a.ctx_lens[b], 0), a.max_ctx);
-  const int t0 = s * a.chunk;
+  int n_ch, len;
+  chunk_plan(ctx, a.chunk, n_ch, len);
+  const int t0 = s * len;
   if (t0 >= ctx) return;  // empty split: the reduction ignores it
-  const int t1 = min(ctx, t0 + a.chunk);
+  const int t1 = min(ctx, t0 + len);
   const int hc = lane & 15, rg = lane >> 4;
   const bool real = hc < HG;
 

@@ -1,11 +1,13 @@
-"""Host model of the GQA decode kernel's work-item order (csrc/decode.hip, decode_item).
+"""Host model of the GQA decode kernel's chunks and work-item order (csrc/decode.hip, chunk_plan and
+decode_item).
 
-The split kernel's work-groups are dispatched in the order: every sequence's full chunks
-(sequence-major), then the short last chunks of the sequences whose context is not a multiple of the
-chunk, also sequence-major. The model below replays the kernel's wave-level steps (a 64-lane
-inclusive scan per block of sequences, ballots, the j-th set bit) lane by lane on the CPU and checks
-that the items 0 .. B*nsplit-1 cover every non-empty (sequence, chunk) exactly once, in that order,
-and that the rest report "past the last item". No GPU is needed.
+A context of ctx tokens is n = ceil(ctx / chunk) chunks of ceil(ctx / n) tokens (the last one shorter
+by less than n), so every chunk of a context longer than one chunk holds chunk/2 .. chunk tokens. The
+split kernel's work-groups are dispatched sequence-major, the chunks of a sequence together. The model
+below replays the kernel's wave-level steps (a 64-lane inclusive scan per block of sequences, ballots)
+lane by lane on the CPU and checks that the items 0 .. B*nsplit-1 cover every (sequence, chunk)
+exactly once, in that order, that the chunks tile each context, and that the rest report "past the
+last item". No GPU is needed.
 """
 import numpy as np
 import pytest
@@ -22,6 +24,13 @@ def clamp_ctx(ctx_lens, max_ctx, b0):
     return ctx
 
 
+def chunk_plan(ctx, chunk):
+    """(count, length) of a context's chunks, as the kernel computes them."""
+    n = -(-ctx // chunk)
+    length = -(-ctx // n) if n > 0 else 0
+    return n, length
+
+
 def decode_item(ctx_lens, max_ctx, chunk, item):
     """Lane-level replay of the kernel's item -> (b, s) mapping; None past the last item."""
     B = len(ctx_lens)
@@ -29,7 +38,7 @@ def decode_item(ctx_lens, max_ctx, chunk, item):
     before = 0
     for b0 in range(0, B, LANES):
         ctx = clamp_ctx(ctx_lens, max_ctx, b0)
-        f = ctx // chunk
+        f = np.array([chunk_plan(int(c), chunk)[0] for c in ctx])
         incl = f.copy()
         d = 1
         while d < LANES:  # shfl_up scan: lanes below d keep their value
@@ -42,25 +51,12 @@ def decode_item(ctx_lens, max_ctx, chunk, item):
             l = int(np.argmax(mask))  # lowest set lane of the ballot
             return b0 + l, int(item - before - (incl[l] - f[l]))
         before += total
-    j = item - before
-    for b0 in range(0, B, LANES):
-        ctx = clamp_ctx(ctx_lens, max_ctx, b0)
-        part = (ctx % chunk) != 0
-        cnt = int(part.sum())
-        if j < cnt:
-            below = np.array([part[:i].sum() for i in range(LANES)])
-            hit = part & (below == j)
-            l = int(np.argmax(hit))
-            return b0 + l, int(ctx[l] // chunk)
-        j -= cnt
     return None
 
 
 def expected_order(ctx_lens, max_ctx, chunk):
     ctx = np.clip(np.asarray(ctx_lens), 0, max_ctx)
-    full = [(b, s) for b in range(len(ctx)) for s in range(int(ctx[b]) // chunk)]
-    short = [(b, int(ctx[b]) // chunk) for b in range(len(ctx)) if ctx[b] % chunk]
-    return full + short
+    return [(b, s) for b in range(len(ctx)) for s in range(chunk_plan(int(ctx[b]), chunk)[0])]
 
 
 CASES = [
@@ -75,7 +71,7 @@ CASES = [
 
 
 @pytest.mark.parametrize("B,chunk,max_ctx,recipe", CASES)
-def test_items_cover_every_chunk_once_longest_first(B, chunk, max_ctx, recipe):
+def test_items_cover_every_chunk_once_sequence_major(B, chunk, max_ctx, recipe):
     rng = np.random.default_rng(B * 7 + chunk)
     if recipe == "uniform":
         ctx = rng.integers(1, max_ctx + 1, B)
@@ -89,10 +85,20 @@ def test_items_cover_every_chunk_once_longest_first(B, chunk, max_ctx, recipe):
     want = expected_order(ctx, max_ctx, chunk)
     assert got[:len(want)] == want
     assert all(g is None for g in got[len(want):])
-    # every item maps inside the grid's (sequence, split) range and before the context end
+    # every item maps inside the grid's (sequence, split) range and before the context end; the
+    # chunks of a context tile it exactly, none empty, each of chunk/2 .. chunk tokens when the context
+    # spans more than one chunk
     ctxc = np.clip(ctx, 0, max_ctx)
+    covered = {}
     for b, s in want:
-        assert 0 <= b < B and 0 <= s < nsplit and s * chunk < ctxc[b]
+        n, length = chunk_plan(int(ctxc[b]), chunk)
+        t0, t1 = s * length, min(int(ctxc[b]), (s + 1) * length)
+        assert 0 <= b < B and 0 <= s < nsplit and t0 < t1 <= ctxc[b]
+        assert t1 - t0 <= chunk and (n == 1 or 2 * (t1 - t0) >= chunk)
+        covered.setdefault(b, []).append((t0, t1))
+    for b, spans in covered.items():
+        assert spans[0][0] == 0 and spans[-1][1] == ctxc[b]
+        assert all(spans[i][1] == spans[i + 1][0] for i in range(len(spans) - 1))
 
 
 @pytest.mark.parametrize("nhg", [8, 16, 1, 2, 4, 3])
