@@ -109,8 +109,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   const int n_hg = G / HG;  // head groups per KV head
   // block order: head group fastest, then the work item (sequence-major, balanced chunks). The KV
   // heads of one token sit side by side in a cache row, so consecutive work-groups (dispatched to
-  // different XCDs at the same time) read the neighbouring segments of the same rows together: +12 % bandwidth over a chunk-fastest order, which fetched each head's
-  // 256-byte segments of a row at different times. The head group is rotated by the sequence
+  // different XCDs at the same time) read the neighbouring segments of the same rows together:
+  // +12 % bandwidth over a chunk-fastest order, which fetched each head's 256-byte segments of a
+  // row at different times. The head group is rotated by the sequence
   // index, so that a work-group id's XCD (id % 8) reads different KV heads of different sequences:
   // with one KV head per XCD (each reading one fixed 256-byte slice of every row) some XCDs ran
   // ~15 % longer than others on the same work.
