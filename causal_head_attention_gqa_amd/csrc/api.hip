@@ -207,7 +207,7 @@ int attn_prefill(const void* q, const void* k, const void* v, void* out, int B, 
     hipError_t e;
     if (dtype == ATTN_BF16) {
       e = launch_rope_table_rotate_bf16(static_cast<const bf16_t*>(k), static_cast<bf16_t*>(krot), table, B, S, Nkv,
-                                        Dh, (double)rope_theta, st);
+                                        Dh, (double)rope_theta, st, a.queue, &a.queue_zeroed);
     } else {
       e = launch_rope_table(table, S, Dh, (double)rope_theta, st);
       if (e == hipSuccess)

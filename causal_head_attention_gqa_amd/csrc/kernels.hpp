@@ -23,8 +23,11 @@ __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return bf16_t{f32_
 // ---- RoPE (rope.hip) ----
 hipError_t launch_rope_table(float2* table, int S, int D, double theta, hipStream_t st);
 // The table and the bf16 rotation of K [B, S, N, D] (positions 0 .. S-1) in one launch.
+// zero: 128 words the one-launch form also zeroes (the prefill's work-list counters, which then
+// need no launch of their own), or nullptr; *zeroed tells whether it did.
 hipError_t launch_rope_table_rotate_bf16(const bf16_t* src, bf16_t* dst, float2* table, int B, int S, int N, int D,
-                                         double theta, hipStream_t st);
+                                         double theta, hipStream_t st, unsigned int* zero = nullptr,
+                                         bool* zeroed = nullptr);
 template <typename T>
 hipError_t launch_rope_rotate_table(const T* src, T* dst, const float2* table, long long rows, int S, int N,
                                     int D, hipStream_t st);
@@ -63,8 +66,9 @@ struct PrefillArgs {
   // bf16 path: kPrefillQueueBytes of device memory for the work lists' counters (zeroed at the
   // launch), or nullptr: each work-group's item follows from its id
   unsigned int* queue;
+  bool queue_zeroed;  // the counters were zeroed by an earlier launch on the stream (the RoPE pre-pass)
 };
-constexpr size_t kPrefillQueueBytes = 256;
+constexpr size_t kPrefillQueueBytes = 512;  // 8 counters, 64 bytes apart
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t st);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st);
 

@@ -793,7 +793,7 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t st) {
   unsigned int* lists = npairs % 8 == 0 ? a.queue : nullptr;
   const long long n_wg = lists != nullptr ? n_items + 8 * ((n_items / 8 + 7) / 8) : n_items;
   if (n_wg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  if (lists != nullptr) prefill_lists_reset_kernel<<<dim3(1), dim3(128), 0, st>>>(lists);
+  if (lists != nullptr && !a.queue_zeroed) prefill_lists_reset_kernel<<<dim3(1), dim3(128), 0, st>>>(lists);
   prefill_bf16_kernel<DQK, DV, HPW, kCache, kWin><<<dim3((unsigned)n_wg), dim3(kThreads), 0, st>>>(
       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
       static_cast<uint16_t*>(a.out), a.table, a.B, a.S, a.Nh, a.Nkv, a.scale_log2, a.causal, n_ptiles, a.kv_tok,

@@ -106,8 +106,10 @@ constexpr int kTableRotLds = 2040 + kTableRotMaxD;
 __global__ __launch_bounds__(256) void rope_table_rotate_bf16_kernel(const uint16_t* __restrict__ src,
                                                                      uint16_t* __restrict__ dst,
                                                                      float2* __restrict__ table, int B, int S,
-                                                                     int N, int D, double neg2_log2theta_over_d) {
+                                                                     int N, int D, double neg2_log2theta_over_d,
+                                                                     unsigned int* __restrict__ zero) {
   __shared__ float2 cs_lds[kTableRotLds];
+  if (zero != nullptr && blockIdx.x == 0 && threadIdx.x < 128) zero[threadIdx.x] = 0u;
   const int half = D / 2, groups = D / 16;
   const long long total = (long long)S * N * groups;
   const long long first = (long long)blockIdx.x * 256;
@@ -378,7 +380,8 @@ template hipError_t launch_rope_rotate_table<bf16_t>(const bf16_t*, bf16_t*, con
                                                      int, hipStream_t);
 
 hipError_t launch_rope_table_rotate_bf16(const bf16_t* src, bf16_t* dst, float2* table, int B, int S, int N, int D,
-                                         double theta, hipStream_t st) {
+                                         double theta, hipStream_t st, unsigned int* zero, bool* zeroed) {
+  if (zeroed != nullptr) *zeroed = false;
   if (D % 16 != 0 || D > kTableRotMaxD || D <= 0 || B <= 0 || S <= 0 || N <= 0) {  // the two-launch form
     hipError_t e = launch_rope_table(table, S, D, theta, st);
     if (e != hipSuccess) return e;
@@ -387,8 +390,10 @@ hipError_t launch_rope_table_rotate_bf16(const bf16_t* src, bf16_t* dst, float2*
   const long long n = (long long)S * N * (D / 16);
   const double k = -2.0 * log2(theta) / (double)D;
   rope_table_rotate_bf16_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st>>>(
-      reinterpret_cast<const uint16_t*>(src), reinterpret_cast<uint16_t*>(dst), table, B, S, N, D, k);
-  return hipGetLastError();
+      reinterpret_cast<const uint16_t*>(src), reinterpret_cast<uint16_t*>(dst), table, B, S, N, D, k, zero);
+  const hipError_t e = hipGetLastError();
+  if (e == hipSuccess && zeroed != nullptr) *zeroed = zero != nullptr;
+  return e;
 }
 template hipError_t launch_rope_apply<float>(float*, const int*, long long, int, int, int, double, int,
                                              hipStream_t);

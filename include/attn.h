@@ -67,7 +67,7 @@ const char* attn_status_str(int status);
  * B == 0 or S == 0 is a valid empty call (nothing launched).
  * workspace: device buffer of attn_prefill_workspace_bytes(...) bytes. With RoPE its leading part
  *   (the angle table and the rotated keys) is required: a smaller or NULL workspace is
- *   ATTN_ERR_WORKSPACE. For ATTN_BF16 the figure ends with 256 bytes of work-list counters, which
+ *   ATTN_ERR_WORKSPACE. For ATTN_BF16 the figure ends with 512 bytes of work-list counters, which
  *   are optional: with them, XCDs that run faster take q-tiles left in the slower XCDs' lists;
  *   without them (a workspace just short of the figure, or NULL without RoPE) every q-tile has a
  *   fixed work-group. The output is the same bits either way. The contents are scratch, set by
@@ -97,7 +97,7 @@ int attn_prefill(const void* q, const void* k, const void* v, void* out,
  * B == 0 or S == 0 is a valid empty call (nothing launched).
  * workspace: attn_prefill_mla_workspace_bytes(...) bytes. With RoPE its leading part, the angle
  *   table and the keys with their rotated k^R block (k itself is never modified), is required;
- *   the last 256 bytes are optional work-list counters, as for attn_prefill (same bits either way).
+ *   the last 512 bytes are optional work-list counters, as for attn_prefill (same bits either way).
  * ------------------------------------------------------------------------------------------ */
 size_t attn_prefill_mla_workspace_bytes(int B, int S, int Nkv, float rope_theta);
 
@@ -135,7 +135,7 @@ int attn_prefill_mla(const void* q, const void* k, const void* v, void* out, int
  *          scale <= 0 selects 1 / sqrt(Dh).
  * Supported: ATTN_BF16, Dh in {64, 128}, 1 <= S <= max_ctx, ld % 8 == 0, ld >= Dh.
  * workspace: attn_prefill_cached_workspace_bytes(...) bytes: the RoPE angle table (required with
- *   RoPE), then 256 bytes of optional work-list counters, as for attn_prefill (same bits either way).
+ *   RoPE), then 512 bytes of optional work-list counters, as for attn_prefill (same bits either way).
  * With q_start[b] = 0 and S = max_ctx this is exactly attn_prefill on the cached keys.
  * ------------------------------------------------------------------------------------------ */
 size_t attn_prefill_cached_workspace_bytes(int max_ctx, int Dh, float rope_theta);

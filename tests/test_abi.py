@@ -102,11 +102,11 @@ def test_rope_argument_errors():
 def test_workspace_queries():
     from causal_head_attention_gqa_amd import lib
     _lib()
-    # bf16: 256 bytes for the work lists' counters, optional; fp32 has none
-    assert lib.prefill_workspace_bytes(4, 8192, 8, 128, 0.0, 1) == 256
+    # bf16: 512 bytes for the work lists' counters (8, 64 bytes apart), optional; fp32 has none
+    assert lib.prefill_workspace_bytes(4, 8192, 8, 128, 0.0, 1) == 512
     assert lib.prefill_workspace_bytes(4, 8192, 8, 64, 0.0, 0) == 0
     # RoPE: fp32 (cos, sin) table [S, Dh/2] plus rotated keys (required), then the counters
-    assert lib.prefill_workspace_bytes(4, 8192, 8, 128, 5e5, 1) == 8192 * 64 * 8 + 4 * 8192 * 8 * 128 * 2 + 256
+    assert lib.prefill_workspace_bytes(4, 8192, 8, 128, 5e5, 1) == 8192 * 64 * 8 + 4 * 8192 * 8 * 128 * 2 + 512
     ws = lib.decode_workspace_bytes(64, 32, 8, 128, 128, 8192, 1)
     assert ws > 0 and ws % 256 == 0
     # MLA: split partials (bf16 rows + fp32 max/sum) for 8 chunks of 512 tokens at B = 32 ...
@@ -160,9 +160,9 @@ def test_kv_append_argument_errors():
 def test_prefill_cached_workspace_query():
     from causal_head_attention_gqa_amd import lib
     _lib()
-    # the angle table (required with RoPE), then 256 bytes of optional work-list counters
-    assert lib.prefill_cached_workspace_bytes(8192, 128, 0.0) == 256
-    assert lib.prefill_cached_workspace_bytes(8192, 128, 5e5) == 8192 * 64 * 8 + 256
+    # the angle table (required with RoPE), then 512 bytes of optional work-list counters
+    assert lib.prefill_cached_workspace_bytes(8192, 128, 0.0) == 512
+    assert lib.prefill_cached_workspace_bytes(8192, 128, 5e5) == 8192 * 64 * 8 + 512
 
 
 def test_prefill_mla_argument_errors():
@@ -186,9 +186,9 @@ def test_prefill_mla_argument_errors():
 def test_prefill_mla_workspace_query():
     from causal_head_attention_gqa_amd import lib
     _lib()
-    assert lib.prefill_mla_workspace_bytes(1, 4096, 128, 0.0) == 256  # the optional work-list counters
+    assert lib.prefill_mla_workspace_bytes(1, 4096, 128, 0.0) == 512  # the optional work-list counters
     # fp32 (cos, sin) table [S, 32] plus keys with the rotated k^R block
-    assert lib.prefill_mla_workspace_bytes(1, 4096, 128, 1e4) == 4096 * 32 * 8 + 4096 * 128 * 192 * 2 + 256
+    assert lib.prefill_mla_workspace_bytes(1, 4096, 128, 1e4) == 4096 * 32 * 8 + 4096 * 128 * 192 * 2 + 512
 
 
 class _FakeTensor:

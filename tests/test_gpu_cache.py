@@ -298,9 +298,11 @@ def test_prefill_cached_work_lists_give_the_static_order_bits(window, sinks):
     q = to_dev(synth.normal(wid, 0, (B, S, Nh, D), "bf16"), "bf16")
     start = torch.tensor([T - S, 400], dtype=torch.int32, device="cuda")
     full = attn.prefill_cached_workspace_bytes(T, D, theta)
-    ws = torch.empty(full, dtype=torch.uint8, device="cuda")
+    buf = torch.full((full + 4096,), 0xA5, dtype=torch.uint8, device="cuda")  # canary past the figure
     kw = dict(rope_theta=theta, window=window, sinks=sinks)
-    listed = attn.prefill_cached(q, kc, vc, start, workspace=ws, **kw)
-    static = attn.prefill_cached(q, kc, vc, start, workspace=ws[:full - 256], **kw)
+    listed = attn.prefill_cached(q, kc, vc, start, workspace=buf[:full], **kw)
+    torch.cuda.synchronize()
+    assert bool((buf[full:] == 0xA5).all())
+    static = attn.prefill_cached(q, kc, vc, start, workspace=buf[:full - 512], **kw)
     assert torch.isfinite(listed.float()).all()
     assert torch.equal(listed, static)

@@ -105,8 +105,10 @@ def test_mla_prefill_work_lists_give_the_static_order_bits():
     B, S, Nh, Nkv, rope = 2, 600, 32, 32, 1e4
     q, k, v = (to_dev(t, "bf16") for t in _inputs(640, B, S, Nh, Nkv))
     full = attn.prefill_mla_workspace_bytes(B, S, Nkv, rope)
-    ws = torch.empty(full, dtype=torch.uint8, device="cuda")
-    listed = attn.prefill_mla(q, k, v, rope_theta=rope, workspace=ws)
-    static = attn.prefill_mla(q, k, v, rope_theta=rope, workspace=ws[:full - 256])
+    buf = torch.full((full + 4096,), 0xA5, dtype=torch.uint8, device="cuda")  # canary past the figure
+    listed = attn.prefill_mla(q, k, v, rope_theta=rope, workspace=buf[:full])
+    torch.cuda.synchronize()
+    assert bool((buf[full:] == 0xA5).all())
+    static = attn.prefill_mla(q, k, v, rope_theta=rope, workspace=buf[:full - 512])
     assert torch.isfinite(listed.float()).all()
     assert torch.equal(listed, static)

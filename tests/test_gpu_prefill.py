@@ -250,7 +250,9 @@ def test_work_lists_give_the_static_order_bits(B, S, Nh, Nkv, rope):
     k = to_dev(synth.normal(wid, 1, (B, S, Nkv, 128), "bf16"), "bf16")
     v = to_dev(synth.normal(wid, 2, (B, S, Nkv, 128), "bf16"), "bf16")
     full = attn.prefill_workspace_bytes(B, S, Nkv, 128, rope, attn.ATTN_BF16)
-    ws = torch.zeros(full, dtype=torch.uint8, device="cuda")
+    # the workspace sits at the start of a larger buffer whose tail holds a canary: nothing past the
+    # figure may be written
+    buf = torch.full((full + 4096,), 0xA5, dtype=torch.uint8, device="cuda")
 
     def call(ws_ptr, ws_len):
         out = torch.full_like(q, float("nan"))
@@ -261,10 +263,12 @@ def test_work_lists_give_the_static_order_bits(B, S, Nh, Nkv, rope):
         torch.cuda.synchronize()
         return out
 
-    listed = call(ws.data_ptr(), full)
-    static = call(ws.data_ptr(), full - 256)
+    listed = call(buf.data_ptr(), full)
+    assert bool((buf[full:] == 0xA5).all())
+    static = call(buf.data_ptr(), full - 512)
     assert torch.isfinite(listed.float()).all()
     assert torch.equal(listed, static)
-    assert torch.equal(call(ws.data_ptr(), full), static)
+    assert torch.equal(call(buf.data_ptr(), full), static)
+    assert bool((buf[full:] == 0xA5).all())
     if rope == 0.0:
         assert torch.equal(call(None, 0), static)
