@@ -210,12 +210,18 @@ def test_llama3_prefill_every_head_sampled_rows():
     work-group order, heaviest q-tiles first), then EVERY (batch, query head) pair on at least 256
     rows against the oracle: the edge rows of the 32-row work-group tiles and 32-key blocks (0, 1,
     31, 32, 33, 63, 64, 127, 128, the middle, the last tiles) plus rows drawn per pair. The oracle
-    does ~1 GFLOP per pair (~20 s in all); the whole 4.4 TFLOP output would take hours on the host."""
+    does ~1 GFLOP per pair (~20 s in all); the whole 4.4 TFLOP output would take hours on the host.
+    Over the whole output: every element is written (a NaN fill is gone everywhere), and row 0 of
+    every head, a softmax over a single key, is that key's value row exactly."""
     import causal_head_attention_gqa_amd as attn
     torch = __import__("torch")
     w = synth.LLAMA3_PREFILL
     q, k, v = w.inputs()
-    out = attn.prefill(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), rope_theta=w.rope_theta)
+    qd, vd = to_dev(q, "bf16"), to_dev(v, "bf16")
+    out = attn.prefill(qd, to_dev(k, "bf16"), vd, rope_theta=w.rope_theta, out=torch.full_like(qd, float("nan")))
+    assert bool(torch.isfinite(out).all())
+    for h in range(w.Nh):
+        assert torch.equal(out[:, 0, h], vd[:, 0, h // (w.Nh // w.Nkv)])
     edges = np.array([0, 1, 31, 32, 33, 63, 64, 127, 128, 4095, 4096, 8127, 8128, 8159, 8160, 8190, 8191])
     rng = np.random.default_rng(7)
     worst, n_rows = 0.0, 0
