@@ -306,8 +306,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 // phase of the chunks (chunks ph, ph + SPL, ...); the loads of up to 8 chunks per phase are issued
 // together with that of the context length (non-temporal: each partial is read once), so a row of up
 // to 8 * SPL chunks costs one round trip to memory, and the phases are summed across lanes at the end.
-// The waves share nothing, so a work-group holds kMergeWaves of them: a quarter as many work-groups
-// as 4-wave ones fill the chip sooner (the 64-sequence decode merges run ~1.5 % faster end to end).
+// The waves share nothing, so a work-group holds kMergeWaves of them (as fast as 4-wave work-groups).
 constexpr int kMergeWaves = 16;
 __global__ __launch_bounds__(kMergeWaves * 64) void decode_reduce_kernel(DecodeArgs a) {
   const int wid = blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
